@@ -1,0 +1,127 @@
+"""CPU oracle for the generation-logprob reduction (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding)
+never does.  The arithmetic lives in ``oracle_logprobs.c``; this module only
+builds it with gcc and marshals numpy arrays through ctypes.
+
+Every function is pinned by tests that do not reuse its arithmetic; none is
+"parity unpinned" except the conventions listed in the C file's readings
+(bit patterns for unused or invalid entries), which the pages do not fix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle_logprobs.c")
+LIB = os.path.join(HERE, "liboracle_logprobs.so")
+
+DTYPE_FP32 = 0
+DTYPE_BF16 = 1
+MAX_IDS = 128
+ROW_WORDS = 258
+MAX_K = 20
+NAN_BITS = 0x7FC00000
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+             "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(src: str = SRC, out: str = LIB, extra: list[str] | None = None) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    cmd = ["gcc", *GCC_FLAGS, *(extra or []), src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class Oracle:
+    """ctypes handle on one build of the oracle shared library."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            build(out=path)
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        c = ctypes
+        self.lib.oracle_row_lse.restype = c.c_float
+        self.lib.oracle_row_lse.argtypes = [c.c_void_p, c.c_int, c.c_int32]
+        self.lib.oracle_row.restype = c.c_int
+        self.lib.oracle_row.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
+                                        c.c_int32, c.c_void_p, c.c_int32,
+                                        c.c_void_p, c.c_void_p]
+        self.lib.oracle_frame.restype = c.c_int64
+        self.lib.oracle_frame.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
+                                          c.c_int32, c.c_int32, c.c_void_p,
+                                          c.c_void_p, c.c_void_p, c.c_void_p,
+                                          c.c_void_p, c.c_int32, c.c_void_p,
+                                          c.c_void_p]
+
+    @staticmethod
+    def _dtype_of(a: np.ndarray) -> int:
+        if a.dtype == np.float32:
+            return DTYPE_FP32
+        if a.dtype == np.uint16:  # bf16 bit patterns
+            return DTYPE_BF16
+        raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {a.dtype}")
+
+    def row_lse(self, row: np.ndarray, V: int | None = None) -> float:
+        row = np.ascontiguousarray(row)
+        V = row.shape[-1] if V is None else V
+        return float(self.lib.oracle_row_lse(row.ctypes.data, self._dtype_of(row), V))
+
+    def row(self, row: np.ndarray, token: int, K: int, sel=None, V: int | None = None):
+        """One emitted position.  Returns (words[2 + 2W] as int32, L)."""
+        row = np.ascontiguousarray(row)
+        V = row.shape[-1] if V is None else V
+        words = np.zeros(ROW_WORDS, dtype=np.int32)
+        L = ctypes.c_float(0.0)
+        if sel is None or len(sel) == 0:
+            sel_arr, n = None, 0
+        else:
+            sel_arr = np.ascontiguousarray(sel, dtype=np.int32)
+            n = len(sel_arr)
+        rc = self.lib.oracle_row(row.ctypes.data, self._dtype_of(row), V, int(token), n,
+                                 None if sel_arr is None else sel_arr.ctypes.data, K,
+                                 words.ctypes.data, ctypes.byref(L))
+        if rc < 0:
+            raise ValueError("oracle_row rejected its arguments")
+        return words[:rc].copy(), float(L.value)
+
+    def frame(self, logits: np.ndarray, capacity: int, T: int, V: int, V_pad: int,
+              requested, id_counts, ids, emitted, tokens, K: int, out: np.ndarray):
+        """One frame.  `out` is [capacity, T, 258] int32 and is written in place
+        (only active positions).  Returns (active rows, lse[capacity*T])."""
+        logits = np.ascontiguousarray(logits)
+        assert logits.size >= capacity * T * V_pad
+        req = np.ascontiguousarray(requested, dtype=np.int32)
+        cnt = np.ascontiguousarray(id_counts, dtype=np.int32)
+        idv = np.ascontiguousarray(ids, dtype=np.int32)
+        emi = np.ascontiguousarray(emitted, dtype=np.int32)
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        assert req.size == capacity and cnt.size == capacity and emi.size == capacity
+        assert idv.size == capacity * MAX_IDS and tok.size == capacity * T
+        assert out.dtype == np.int32 and out.size == capacity * T * ROW_WORDS
+        assert out.flags.c_contiguous
+        lse = np.full(capacity * T, np.nan, dtype=np.float32)
+        n = self.lib.oracle_frame(logits.ctypes.data, self._dtype_of(logits), capacity, T,
+                                  V, V_pad, req.ctypes.data, cnt.ctypes.data,
+                                  idv.ctypes.data, emi.ctypes.data, tok.ctypes.data, K,
+                                  out.ctypes.data, lse.ctypes.data)
+        if n < 0:
+            raise ValueError("oracle_frame rejected its arguments")
+        return int(n), lse
+
+
+_DEFAULT: Oracle | None = None
+
+
+def get() -> Oracle:
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT

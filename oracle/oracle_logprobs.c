@@ -1,0 +1,220 @@
+/*
+ * CPU oracle for the generation-logprob reduction.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant with the
+ * GPU library; the two meet only on the seeded inputs.
+ *
+ * It is the plain definition, written out as directly as possible:
+ * single-threaded, IEEE arithmetic, no blocking, no fusion, a full sort per
+ * row.  Build with gcc without -ffast-math and with -ffp-contract=off.
+ *
+ * Sources (the Flare "generation logprobs" design page, hereafter GLP):
+ *   - GLP, definition paragraph: a returned token's logprob is its logit
+ *     minus the logsumexp of the whole vocabulary the sampler saw, formed in
+ *     (at least) FP32 and before any sampling transform.
+ *   - GLP, definition paragraph: K natural alternatives ordered by
+ *     decreasing logprob, equal values by increasing token ID; or up to 128
+ *     caller-selected IDs reported in caller order with the same
+ *     normalization; the chosen token is stored on its own.
+ *   - GLP, packed-position paragraph after the buffer table: word layout
+ *     [chosen id, chosen bits, id0, bits0, ...]; IDs past the vocabulary are
+ *     -1 when it has fewer than K entries.
+ *   - GLP, gating paragraphs: only emitted positions are reduced; a zero
+ *     request flag skips the row entirely (tiled-reduction paragraph and
+ *     zero-flag paragraph).
+ *   - GLP, tiled-reduction paragraph: the order is taken on the reported
+ *     FP32 values (so equalities created by the subtraction are ties),
+ *     signed zero is normalized, padded vocabulary lanes never take part,
+ *     and selected IDs subtract the same normalization from their raw logit.
+ *   - MTP design page, section "A speculative round is a state transaction":
+ *     a slot's verify rows are emitted as a prefix of length 1..k+1.
+ *
+ * Readings where the pages leave a step open:
+ *   R1  only lanes [0, V) are normalized or ranked; [V, V_pad) is padding.
+ *   R2  the sum is taken in double, the normalization L is rounded to FP32
+ *       once, and each reported value is one FP32 subtraction x - L.
+ *   R4  a reported -0.0 is stored as +0.0.
+ *   R5  unused pairs when V < K are (-1, 0x7FC00000).
+ *   R6  cells that the rules do not write are left untouched.
+ *   R7  a chosen or selected ID outside [0, V) is written as given with
+ *       value bits 0x7FC00000 and is never dereferenced.
+ *   R10 emitted counts are clamped to [0, T], ID counts to [0, 128]; a zero
+ *       request flag wins over a nonzero ID count.
+ *
+ * Parity pins: every function here is pinned by tests that do not reuse its
+ * arithmetic (closed forms, brute-force ranks, designed tie rows, a library
+ * logsumexp, poison invariants); see the test suite for the list.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_DTYPE_FP32 0
+#define ORACLE_DTYPE_BF16 1
+#define ORACLE_MAX_IDS 128
+#define ORACLE_ROW_WORDS 258
+#define ORACLE_MAX_K 20
+#define ORACLE_NAN_BITS 0x7FC00000u
+
+/* One vocabulary entry with its reported value, for sorting. */
+typedef struct {
+  float lp;
+  int32_t id;
+} oracle_entry;
+
+/* Element i of a row as a double.  bf16 widens exactly: its 16 bits are
+ * the top half of an FP32 word. */
+static double oracle_widen(const void* row, int dtype, int64_t i) {
+  if (dtype == ORACLE_DTYPE_BF16) {
+    uint16_t h = ((const uint16_t*)row)[i];
+    uint32_t w = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)row)[i];
+}
+
+static uint32_t oracle_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return u;
+}
+
+/* GLP definition paragraph: L = logsumexp over the unpadded vocabulary
+ * (reading R1), computed as M + log(sum exp(x - M)) in double and rounded
+ * to FP32 once (reading R2). */
+float oracle_row_lse(const void* row, int dtype, int32_t V) {
+  double M = -INFINITY;
+  for (int32_t i = 0; i < V; ++i) {
+    double x = oracle_widen(row, dtype, i);
+    if (x > M) M = x;
+  }
+  if (M == -INFINITY) return -INFINITY; /* all lanes -inf: out of contract */
+  double S = 0.0;
+  for (int32_t i = 0; i < V; ++i) S += exp(oracle_widen(row, dtype, i) - M);
+  return (float)(M + log(S));
+}
+
+/* The reported value of one lane: one FP32 subtraction, -0 stored as +0
+ * (GLP tiled-reduction paragraph; readings R2 and R4). */
+static float oracle_reported(const void* row, int dtype, int32_t i, float L) {
+  float x = (float)oracle_widen(row, dtype, i);
+  float lp = x - L;
+  if (lp == 0.0f) lp = 0.0f;
+  return lp;
+}
+
+/* Decreasing value, then increasing token ID (GLP definition paragraph). */
+static int oracle_cmp_entry(const void* a, const void* b) {
+  const oracle_entry* p = (const oracle_entry*)a;
+  const oracle_entry* q = (const oracle_entry*)b;
+  if (p->lp > q->lp) return -1;
+  if (p->lp < q->lp) return 1;
+  return (p->id < q->id) ? -1 : (p->id > q->id) ? 1 : 0;
+}
+
+/* A chosen or selected ID's pair (reading R7 for IDs outside [0, V)). */
+static void oracle_pair(const void* row, int dtype, int32_t V, int32_t id,
+                        float L, int32_t* w) {
+  w[0] = id;
+  if (id >= 0 && id < V)
+    w[1] = (int32_t)oracle_bits(oracle_reported(row, dtype, id, L));
+  else
+    w[1] = (int32_t)ORACLE_NAN_BITS;
+}
+
+/*
+ * One emitted position.  Writes words [0, 2 + 2W) of `words`, where W = n
+ * (selected mode, n > 0) or K (natural mode), and returns that word count,
+ * or -1 when the arguments are unusable.  `L_out` (may be NULL) gets the
+ * row's normalization.
+ */
+int oracle_row(const void* row, int dtype, int32_t V, int32_t token,
+               int32_t n_sel, const int32_t* sel, int32_t K, int32_t* words,
+               float* L_out) {
+  if (!row || !words || V < 1 || K < 0 || K > ORACLE_MAX_K) return -1;
+  if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16) return -1;
+  if (n_sel < 0) n_sel = 0;
+  if (n_sel > ORACLE_MAX_IDS) n_sel = ORACLE_MAX_IDS;
+  if (n_sel > 0 && !sel) return -1;
+
+  float L = oracle_row_lse(row, dtype, V);
+  if (L_out) *L_out = L;
+
+  oracle_pair(row, dtype, V, token, L, words);
+  if (n_sel > 0) {
+    for (int32_t j = 0; j < n_sel; ++j)
+      oracle_pair(row, dtype, V, sel[j], L, words + 2 + 2 * j);
+    return 2 + 2 * n_sel;
+  }
+  if (K == 0) return 2;
+
+  oracle_entry* all = (oracle_entry*)malloc((size_t)V * sizeof(oracle_entry));
+  if (!all) return -1;
+  for (int32_t i = 0; i < V; ++i) {
+    all[i].lp = oracle_reported(row, dtype, i, L);
+    all[i].id = i;
+  }
+  qsort(all, (size_t)V, sizeof(oracle_entry), oracle_cmp_entry);
+  for (int32_t j = 0; j < K; ++j) {
+    int32_t* w = words + 2 + 2 * j;
+    if (j < V) {
+      w[0] = all[j].id;
+      w[1] = (int32_t)oracle_bits(all[j].lp);
+    } else { /* GLP packed-position paragraph; reading R5 */
+      w[0] = -1;
+      w[1] = (int32_t)ORACLE_NAN_BITS;
+    }
+  }
+  free(all);
+  return 2 + 2 * K;
+}
+
+/*
+ * One frame [capacity, T, 258].  Row (s, t) of `logits` starts at element
+ * (s * T + t) * V_pad.  Only active positions are written (GLP gating and
+ * zero-flag paragraphs; MTP design page, round section):
+ *   active(s, t)  <=>  requested[s] != 0  and  t < clamp(emitted[s], 0, T).
+ * `lse_out` (may be NULL) is [capacity * T] and gets L for active rows only.
+ * Returns the number of active rows, or -1 on unusable arguments.
+ */
+int64_t oracle_frame(const void* logits, int dtype, int32_t capacity,
+                     int32_t T, int32_t V, int32_t V_pad,
+                     const int32_t* requested, const int32_t* id_counts,
+                     const int32_t* ids, const int32_t* emitted,
+                     const int32_t* tokens, int32_t K, int32_t* out,
+                     float* lse_out) {
+  if (!logits || !requested || !id_counts || !ids || !emitted || !tokens ||
+      !out)
+    return -1;
+  if (capacity < 1 || T < 1 || V < 1 || V_pad < V || K < 0 ||
+      K > ORACLE_MAX_K)
+    return -1;
+  size_t esize = (dtype == ORACLE_DTYPE_BF16) ? 2 : 4;
+  int64_t active = 0;
+  for (int32_t s = 0; s < capacity; ++s) {
+    if (requested[s] == 0) continue;
+    int32_t e = emitted[s];
+    if (e < 0) e = 0;
+    if (e > T) e = T;
+    int32_t n = id_counts[s];
+    if (n < 0) n = 0;
+    if (n > ORACLE_MAX_IDS) n = ORACLE_MAX_IDS;
+    for (int32_t t = 0; t < e; ++t) {
+      int64_t r = (int64_t)s * T + t;
+      const char* row = (const char*)logits + (size_t)r * (size_t)V_pad * esize;
+      float L;
+      int rc = oracle_row(row, dtype, V, tokens[r], n,
+                          ids + (size_t)s * ORACLE_MAX_IDS, K,
+                          out + (size_t)r * ORACLE_ROW_WORDS, &L);
+      if (rc < 0) return -1;
+      if (lse_out) lse_out[r] = L;
+      ++active;
+    }
+  }
+  return active;
+}

@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` handle and raises
+AssertionError when the oracle disagrees with something it must agree with.
+None of them re-derives a result with the oracle's own recipe: they use
+closed forms, brute-force ranks, a library logsumexp, designed tie rows and
+poison invariants.  The same functions run against deliberately broken
+builds of the oracle (test_oracle_mutants.py) to show that each plausible
+mistake is caught.
+
+Citations are to the Flare generation-logprobs design page (GLP) and the
+Flare MTP design page.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+
+import synth
+
+NAN_BITS = 0x7FC00000
+F32 = np.float32
+
+
+def f32(x) -> np.float32:
+    return np.float32(x)
+
+
+def bits(x) -> int:
+    return int(np.array([x], dtype=np.float32).view(np.int32)[0])
+
+
+def from_bits(b) -> np.float32:
+    return np.array([b], dtype=np.int32).view(np.float32)[0]
+
+
+def ulp32(x: float) -> float:
+    x = abs(float(x))
+    return float(np.spacing(np.float32(x)))
+
+
+def pairs(words):
+    """words -> (ids, values) of the alternative pairs."""
+    w = np.asarray(words, dtype=np.int32)
+    return w[2::2].copy(), w[3::2].copy().view(np.float32)
+
+
+# ---------------------------------------------------------------- closed forms
+def pin_uniform_row(o):
+    """A constant row x = c has L = c + ln V exactly, so every reported value
+    is fl(c - fl(c + ln V)) (GLP definition paragraph)."""
+    for V in (1, 7, 1000, 32000, 151936, 248320, 262144):
+        for c in (0.0, 1.5, -3.25, 1000.0, -1000.0, 88.0):
+            row = np.full(V, c, dtype=np.float32)
+            words, L = o.row(row, token=V // 2, K=20)
+            L_exact = f32(c + math.log(V))
+            assert abs(float(L) - float(L_exact)) <= ulp32(L_exact), (V, c, L, L_exact)
+            lp_tok = from_bits(words[1])
+            want = f32(f32(c) - f32(L))
+            assert lp_tok == want, (V, c, lp_tok, want)
+            assert abs(float(lp_tok) - (c - (c + math.log(V)))) <= 2 * ulp32(L_exact) + 1e-7
+    # The values printed for reference: -ln V rounded to FP32.
+    for V, v in ((32000, -10.3734913), (151936, -11.9312143), (248320, -12.4224739),
+                 (262144, -12.4766493)):
+        words, _ = o.row(np.zeros(V, dtype=np.float32), token=0, K=1)
+        assert abs(float(from_bits(words[1])) - v) < 2e-6, (V, from_bits(words[1]))
+
+
+def pin_uniform_row_bf16(o):
+    """Same closed form through the bf16 widening path."""
+    for V in (3, 4096, 248320):
+        for c in (0.0, 2.5, -7.75):
+            row = synth.bf16_bits(np.full(V, c, dtype=np.float32))
+            words, L = o.row(row, token=1 % V, K=20)
+            L_exact = f32(c + math.log(V))
+            assert abs(float(L) - float(L_exact)) <= ulp32(L_exact), (V, c, L)
+            assert from_bits(words[1]) == f32(f32(c) - f32(L))
+
+
+def pin_two_level_row(o):
+    """a lanes at A and V - a lanes at B: L = A + ln(a + (V - a) e^(B - A))."""
+    rng = np.random.default_rng(11)
+    for V, a, A, B in ((10, 3, 2.0, -1.0), (5000, 17, 6.5, 0.25), (248320, 1, 12.0, 0.0),
+                       (32000, 31999, 1.0, 3.0)):
+        row = np.full(V, B, dtype=np.float32)
+        hot = rng.choice(V, size=a, replace=False)
+        row[hot] = A
+        words, L = o.row(row, token=int(hot[0]), K=20)
+        L_exact = A + math.log(a + (V - a) * math.exp(B - A))
+        assert abs(float(L) - L_exact) <= ulp32(L_exact), (V, a, L, L_exact)
+        assert from_bits(words[1]) == f32(f32(A) - f32(L))
+
+
+def pin_probabilities_sum_to_one(o):
+    """exp of the reported values over the whole vocabulary sums to 1.  All
+    IDs are reported through selected-ID calls that cover [0, V)."""
+    rng = np.random.default_rng(12)
+    for V, scale in ((1, 1.0), (19, 3.0), (128, 4.0), (1000, 3.0), (5000, 8.0)):
+        row = (rng.standard_normal(V) * scale).astype(np.float32)
+        total = 0.0
+        for start in range(0, V, 128):
+            sel = np.arange(start, min(V, start + 128), dtype=np.int32)
+            words, _ = o.row(row, token=0, K=20, sel=sel)
+            ids, vals = pairs(words)
+            assert np.array_equal(ids, sel)
+            total += math.fsum(math.exp(float(v)) for v in vals)
+        assert abs(total - 1.0) < 1e-5, (V, total)
+    # Natural mode lists the whole vocabulary when V <= K.
+    for V in range(1, 21):
+        row = (rng.standard_normal(V) * 5).astype(np.float32)
+        words, _ = o.row(row, token=0, K=20)
+        ids, vals = pairs(words)
+        assert sorted(ids[:V].tolist()) == list(range(V))
+        assert abs(math.fsum(math.exp(float(v)) for v in vals[:V]) - 1.0) < 1e-5
+
+
+def pin_one_hot(o):
+    """One finite lane, the rest -inf: the hot lane's logprob is exactly +0
+    and every other lane is -inf, listed by increasing ID."""
+    for V, hot, v in ((64, 17, 3.5), (1000, 0, -2.0), (4096, 4095, 0.0), (257, 100, -0.0),
+                      (248320, 123456, 7.0)):
+        row = np.full(V, -np.inf, dtype=np.float32)
+        row[hot] = v
+        words, L = o.row(row, token=hot, K=20)
+        assert words[0] == hot and words[1] == 0, (V, hot, words[:2])
+        ids, vals = pairs(words)
+        assert ids[0] == hot and bits(vals[0]) == 0
+        rest = [i for i in range(V) if i != hot][:19]
+        assert ids[1:1 + len(rest)].tolist() == rest
+        assert np.all(np.isneginf(vals[1:1 + len(rest)]))
+
+
+def pin_library_logsumexp(o):
+    """L agrees with torch.logsumexp in float64 to within one FP32 ulp, and
+    each reported value is one FP32 subtraction away from that L."""
+    rng = np.random.default_rng(13)
+    cases = []
+    for V in (32000, 151936, 262144):
+        cases.append((rng.standard_normal(V) * 3).astype(np.float32))
+    g = rng.gumbel(size=248320)
+    g[rng.integers(248320)] += 10
+    cases.append(synth.bf16_bits(g.astype(np.float32)))
+    cases.append((rng.standard_normal(50000) * 30 + 500).astype(np.float32))
+    for row in cases:
+        xs = synth.bf16_to_f32(row) if row.dtype == np.uint16 else row
+        V = xs.size
+        ref = float(torch.logsumexp(torch.from_numpy(xs.astype(np.float64)), 0))
+        tok = int(rng.integers(V))
+        words, L = o.row(row, token=tok, K=20)
+        assert abs(float(L) - ref) <= ulp32(ref), (V, L, ref)
+        assert from_bits(words[1]) == f32(xs[tok] - f32(L))
+        assert abs(float(from_bits(words[1])) - (float(xs[tok]) - ref)) <= 2e-5
+
+
+# ------------------------------------------------------------------ ordering
+def _rank_order(vals: np.ndarray) -> list[int]:
+    """The order given by pos(i) = #{j: v_j > v_i} + #{j: v_j == v_i, j < i}."""
+    n = len(vals)
+    pos = [sum(1 for j in range(n) if vals[j] > vals[i]) +
+           sum(1 for j in range(i) if vals[j] == vals[i]) for i in range(n)]
+    order = [0] * n
+    for i, p in enumerate(pos):
+        order[p] = i
+    return order
+
+
+def _check_full_listing(o, row_f32: np.ndarray):
+    V = row_f32.size
+    words, L = o.row(row_f32, token=0, K=20)
+    ids, vals = pairs(words)
+    expect_vals = (row_f32 - f32(L)).astype(np.float32)
+    expect_vals[expect_vals == 0] = 0.0  # -0 is reported as +0
+    order = _rank_order(expect_vals)
+    assert ids[:V].tolist() == order, (row_f32, ids[:V], order)
+    for k, i in enumerate(order):
+        assert bits(vals[k]) == bits(expect_vals[i]), (row_f32, k, vals[k], expect_vals[i])
+    t = torch.sort(torch.from_numpy(expect_vals), descending=True, stable=True)
+    assert t.indices.tolist() == order
+    assert np.all(ids[V:] == -1) and np.all(words[3 + 2 * V::2] == NAN_BITS)
+
+
+def pin_brute_force_order(o):
+    """Exhaustive small rows over {-inf, -2, -1, -0, +0, 1, 2}: the listed
+    order is decreasing reported value, then increasing ID (GLP definition
+    paragraph), equal to a stable library sort."""
+    values = np.array([-np.inf, -2.0, -1.0, -0.0, 0.0, 1.0, 2.0], dtype=np.float32)
+    for V in range(1, 5):
+        for combo in itertools.product(range(len(values)), repeat=V):
+            row = values[list(combo)]
+            if np.all(np.isneginf(row)):
+                continue  # an all -inf row is outside the contract
+            _check_full_listing(o, row)
+    rng = np.random.default_rng(14)
+    for _ in range(1500):
+        V = int(rng.integers(5, 11))
+        row = values[rng.integers(0, len(values), size=V)]
+        if np.all(np.isneginf(row)):
+            continue
+        _check_full_listing(o, row)
+
+
+def pin_all_equal_row(o):
+    """An all-equal row lists IDs 0..K-1."""
+    for V, c in ((1000, 0.0), (248320, -3.0), (40, 1e-3)):
+        words, _ = o.row(np.full(V, c, dtype=np.float32), token=5, K=20)
+        assert pairs(words)[0].tolist() == list(range(20))
+
+
+def pin_grid_row_by_counting(o):
+    """Rows on a 1/8 grid: the top-K is the smallest IDs at the highest
+    level, then at the next level, and so on (found here by counting)."""
+    rng = np.random.default_rng(15)
+    for V in (4096, 30000):
+        k = rng.integers(0, 129, size=V)
+        row = (k / 8.0 - 8.0).astype(np.float32)
+        want = []
+        for level in sorted(set(k.tolist()), reverse=True):
+            want += np.nonzero(k == level)[0].tolist()
+            if len(want) >= 20:
+                break
+        words, _ = o.row(synth.bf16_bits(row), token=0, K=20)
+        assert pairs(words)[0].tolist() == want[:20]
+
+
+def pin_subtraction_tie(o):
+    """Designed row where two different logits round to the same reported
+    value: x0 = nextafter(1, 0), x1 = 1, x2 = 100, the rest -inf.  L is
+    exactly 100, both x0 - L and x1 - L round to -99, so the tie goes to the
+    smaller ID and the order starts [2, 0, 1] (GLP tiled-reduction paragraph:
+    ties created by the subtraction are ties)."""
+    V = 64
+    row = np.full(V, -np.inf, dtype=np.float32)
+    row[0] = np.nextafter(np.float32(1.0), np.float32(0.0))
+    row[1] = 1.0
+    row[2] = 100.0
+    words, L = o.row(row, token=1, K=20)
+    assert L == f32(100.0)
+    ids, vals = pairs(words)
+    assert ids[:3].tolist() == [2, 0, 1]
+    assert vals[1] == f32(-99.0) and vals[2] == f32(-99.0) and bits(vals[0]) == 0
+    assert ids[3:20].tolist() == list(range(3, 20))
+
+
+def pin_signed_zero(o):
+    """A reported -0 is stored as +0 (GLP tiled-reduction paragraph; the
+    stored bits are reading R4)."""
+    row = np.full(32, -np.inf, dtype=np.float32)
+    row[9] = -0.0
+    words, L = o.row(row, token=9, K=3)
+    assert words[0] == 9 and words[1] == 0
+    ids, vals = pairs(words)
+    assert ids[0] == 9 and bits(vals[0]) == 0
+    row16 = synth.bf16_bits(row)
+    assert row16[9] == 0x8000
+    words, _ = o.row(row16, token=9, K=3, sel=[9, 9])
+    assert words[1] == 0 and words[3] == 0 and words[5] == 0
+
+
+def pin_v_below_k(o):
+    """When V < K the unused alternative IDs are -1 (GLP packed-position
+    paragraph) with NaN bits (reading R5)."""
+    rng = np.random.default_rng(16)
+    for V in range(1, 20):
+        row = (rng.standard_normal(V) * 2).astype(np.float32)
+        words, _ = o.row(row, token=0, K=20)
+        assert len(words) == 42
+        ids, _ = pairs(words)
+        assert sorted(ids[:V].tolist()) == list(range(V))
+        assert np.all(ids[V:] == -1)
+        assert np.all(words[3 + 2 * V::2] == NAN_BITS)
+
+
+def pin_selected_ids(o):
+    """Selected IDs keep caller order, share the chosen token's value when
+    equal to it, and IDs outside [0, V) get NaN bits (GLP definition
+    paragraph; reading R7)."""
+    rng = np.random.default_rng(17)
+    V = 3000
+    row = (rng.standard_normal(V) * 3).astype(np.float32)
+    sel = rng.choice(V, size=128, replace=False).astype(np.int32)
+    tok = int(sel[77])
+    words, L = o.row(row, token=tok, K=20, sel=sel)
+    assert len(words) == 2 + 2 * 128
+    ids, vals = pairs(words)
+    assert np.array_equal(ids, sel)
+    assert bits(vals[77]) == words[1]
+    assert np.array_equal(vals, (row[sel] - f32(L)).astype(np.float32))
+    bad = np.array([-1, V, V + 5, 2**31 - 1, 5, 5], dtype=np.int32)
+    words, _ = o.row(row, token=V, K=20, sel=bad)
+    ids, vals = pairs(words)
+    assert np.array_equal(ids, bad)
+    assert words[1] == NAN_BITS
+    assert np.all(words[3:3 + 8:2] == NAN_BITS)
+    assert vals[4] == vals[5] == f32(row[5] - f32(L))
+    words, _ = o.row(row, token=0, K=20, sel=np.arange(200, dtype=np.int32))
+    assert len(words) == 2 + 2 * 128  # counts clamp to 128
+
+
+# ------------------------------------------------------------- frame gating
+def pin_frame_gating(o):
+    """Only active positions are written and nothing else changes (GLP gating
+    and zero-flag paragraphs; MTP round section); rows are s*T + t; padded
+    lanes never enter; word 0 is the chosen token."""
+    cap, T, V, V_pad = 6, 3, 50, 64
+    rows = cap * T
+    logits = np.full((rows, V_pad), np.inf, dtype=np.float32)  # +inf pads
+    rng = np.random.default_rng(18)
+    hot = [(r * 7 + 3) % V for r in range(rows)]
+    for r in range(rows):
+        logits[r, :V] = rng.standard_normal(V).astype(np.float32)
+        logits[r, hot[r]] = 20.0
+    requested = np.array([1, 0, 1, 1, 1, 1], dtype=np.int32)
+    emitted = np.array([2, 3, 0, 7, -1, 3], dtype=np.int32)
+    id_counts = np.array([-5, 4, 3, 0, 0, 300], dtype=np.int32)
+    ids = np.full(cap * 128, -2, dtype=np.int32)
+    ids[5 * 128:6 * 128] = np.arange(128) % V
+    ids[1 * 128:1 * 128 + 4] = [1, 2, 3, 4]
+    tokens = (np.arange(rows, dtype=np.int32) * 5) % V
+    out = np.full((cap, T, 258), -559038737, dtype=np.int32)
+    n, lse = o.frame(logits, cap, T, V, V_pad, requested, id_counts, ids, emitted, tokens,
+                     20, out)
+    active = {(0, 0), (0, 1), (3, 0), (3, 1), (3, 2), (5, 0), (5, 1), (5, 2)}
+    assert n == len(active)
+    for s in range(cap):
+        for t in range(T):
+            cell = out[s, t]
+            if (s, t) not in active:
+                assert np.all(cell == -559038737), (s, t)
+                continue
+            r = s * T + t
+            W = 128 if s == 5 else 20
+            assert np.all(cell[2 + 2 * W:] == -559038737), (s, t)
+            assert cell[0] == tokens[r]
+            assert np.isfinite(lse[r]) and float(lse[r]) >= 20.0
+            if s == 5:
+                assert np.array_equal(cell[2:2 + 256:2], np.arange(128) % V)
+            else:
+                assert cell[2] == hot[r], (s, t, cell[2], hot[r])
+                assert float(from_bits(cell[3])) > -1e-3
+
+
+ALL_PINS = [pin_uniform_row, pin_uniform_row_bf16, pin_two_level_row,
+            pin_probabilities_sum_to_one, pin_one_hot, pin_library_logsumexp,
+            pin_brute_force_order, pin_all_equal_row, pin_grid_row_by_counting,
+            pin_subtraction_tie, pin_signed_zero, pin_v_below_k, pin_selected_ids,
+            pin_frame_gating]

@@ -1,0 +1,65 @@
+"""Each plausible mistake planted in the oracle must fail at least one pin.
+
+The mutants are built from a patched copy of the oracle's C source in a
+temporary directory (the committed oracle is never modified) and loaded as
+separate shared libraries.  Every mutant keeps memory accesses in bounds.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = [
+    ("no_max_shift",  # logsumexp without subtracting the maximum
+     "S += exp(oracle_widen(row, dtype, i) - M);\n  return (float)(M + log(S));",
+     "S += exp(oracle_widen(row, dtype, i));\n  return (float)(log(S));"),
+    ("log2_instead_of_ln", "return (float)(M + log(S));", "return (float)(M + log2(S));"),
+    ("float_accumulation", "double S = 0.0;", "float S = 0.0f;"),
+    ("ties_by_larger_id", "return (p->id < q->id) ? -1 : (p->id > q->id) ? 1 : 0;",
+     "return (p->id > q->id) ? -1 : (p->id < q->id) ? 1 : 0;"),
+    ("ascending_values", "if (p->lp > q->lp) return -1;\n  if (p->lp < q->lp) return 1;",
+     "if (p->lp < q->lp) return -1;\n  if (p->lp > q->lp) return 1;"),
+    ("no_signed_zero_canon", "if (lp == 0.0f) lp = 0.0f;", ""),
+    ("wrong_sign", "float lp = x - L;", "float lp = L - x;"),
+    ("rank_raw_logits", "all[i].lp = oracle_reported(row, dtype, i, L);",
+     "all[i].lp = (float)oracle_widen(row, dtype, i);"),
+    ("normalize_with_max", "return (float)(M + log(S));", "return (float)M;"),
+    ("padded_lanes_included", "int rc = oracle_row(row, dtype, V, tokens[r], n,",
+     "int rc = oracle_row(row, dtype, V_pad, tokens[r], n,"),
+    ("ignore_request_flag", "if (requested[s] == 0) continue;", ""),
+    ("rows_transposed", "int64_t r = (int64_t)s * T + t;",
+     "int64_t r = (int64_t)t * capacity + s;"),
+    ("chosen_from_slot", "oracle_row(row, dtype, V, tokens[r], n,",
+     "oracle_row(row, dtype, V, tokens[s], n,"),
+    ("selected_reversed", "oracle_pair(row, dtype, V, sel[j], L, words + 2 + 2 * j);",
+     "oracle_pair(row, dtype, V, sel[n_sel - 1 - j], L, words + 2 + 2 * j);"),
+    ("pad_id_zero", "      w[0] = -1;\n", "      w[0] = 0;\n"),
+    ("one_alternative_short", "for (int32_t j = 0; j < K; ++j) {\n    int32_t* w",
+     "for (int32_t j = 0; j + 1 < K; ++j) {\n    int32_t* w"),
+    ("bf16_low_half", "uint32_t w = ((uint32_t)h) << 16;", "uint32_t w = ((uint32_t)h) << 15;"),
+    ("no_count_clamp_to_zero", "if (n < 0) n = 0;\n    if (n > ORACLE_MAX_IDS)",
+     "if (n < 0) n = 1;\n    if (n > ORACLE_MAX_IDS)"),
+    ("invalid_id_zero_bits", "else\n    w[1] = (int32_t)ORACLE_NAN_BITS;", "else\n    w[1] = 0;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mutated = src.replace(old, new)
+    path = os.path.join(tmp_path, "oracle_mutant.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = os.path.join(tmp_path, "liboracle_mutant.so")
+    oracle.build(src=path, out=lib, extra=["-Wno-unused-variable", "-Wno-unused-but-set-variable"])
+    o = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError, OverflowError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
