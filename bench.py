@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Throughput of the generation-logprob reduction on one MI355X.
+
+One step = one flare_logprobs_run over one frame of the speculative-verify
+workload: 128 slots x T=8 verify rows x V=248,320 bf16 logits, emitted counts
+uniform in 1..8 (rows past each slot's prefix hold NaN/+inf garbage and are
+never read), K=20 natural alternatives.  Inputs are seeded synthetic logits
+(Gumbel plus a +10 peak), resident in HBM before timing; `--copies` rotated
+copies of the logits keep the 256 MB Infinity Cache from serving repeats.
+
+Prints one JSON line: rows/s over the whole timed region, the roofline of the
+reduction launch (algorithmic bytes / mean launch time, from HIP events on the
+launch stream), and the CPU oracle timed on a bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C3")
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--check-rows", type=int, default=4,
+                    help="oracle rows compared with the GPU output before timing")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the reduction is sharded by rows with no "
+              "exchange, so N GPUs run N independent copies; multi-GPU runs are not "
+              "part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    import full_vocab_logprob_amd as flp
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    spec = synth.CONFIGS[args.config]
+    bf16 = spec.dtype == synth.BF16
+    print(f"[bench] generating {spec.name}: {spec.description}", file=sys.stderr, flush=True)
+    w = synth.make(spec)
+    rows = spec.capacity * spec.T
+    active = w.active_rows()
+    algo_bytes = w.algorithmic_bytes()
+
+    def upload(a):
+        t = torch.from_numpy(a.view(np.int16) if bf16 else a).to(dev)
+        return t.view(torch.bfloat16).reshape(-1) if bf16 else t.reshape(-1)
+
+    copies = [upload(w.logits)]
+    for _ in range(1, args.copies):
+        copies.append(copies[0].clone())
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa
+    tokens, emitted, requested = g(w.tokens), g(w.emitted), g(w.requested)
+    id_counts, ids = g(w.id_counts), g(w.ids)
+    plan = flp.Plan(spec.capacity, spec.T, spec.V, spec.V_pad,
+                    dtype=torch.bfloat16 if bf16 else torch.float32, K=spec.K, device=0)
+    ws = plan.workspace()
+    out = plan.new_out(int(synth.POISON))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        plan.run(copies[i % len(copies)], tokens, emitted, requested, id_counts, ids, out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Correctness gate before timing: a few rows against the oracle.
+    got = out.cpu().numpy()
+    act_rows = np.nonzero(w.active_mask().reshape(-1))[0]
+    checked = 0
+    if args.check_rows > 0:
+        import oracle
+        o = oracle.get()
+        for r in act_rows[:: max(1, len(act_rows) // args.check_rows)][: args.check_rows]:
+            sl, t = divmod(int(r), spec.T)
+            words, _ = o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, V=spec.V)
+            g_ = got[sl, t, :len(words)]
+            assert np.array_equal(g_[0::2], words[0::2]), f"bench check: ids differ on row {r}"
+            d = np.abs(g_[1::2].view(np.float32).astype(np.float64)
+                       - words[1::2].view(np.float32).astype(np.float64))
+            assert np.all((d <= 2e-5) | (g_[1::2] == words[1::2])), f"values differ on row {r}"
+            checked += 1
+
+    # Timed region: K steps between synchronizations; per-launch HIP events
+    # on the launch stream give the kernel's mean duration.
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(args.warmup + i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_launch_ms = sum(launch_ms) / K
+    med_launch_ms = launch_ms[K // 2]
+    ms_per_step = total_ms / K
+    rows_per_s = active * K / (total_ms / 1e3)
+    achieved_gbps = algo_bytes / (mean_launch_ms / 1e3) / 1e9
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        o = oracle.get()
+        n = 0
+        c0 = time.perf_counter()
+        while n < len(act_rows) and time.perf_counter() - c0 < args.cpu_seconds:
+            r = int(act_rows[n])
+            o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, V=spec.V)
+            n += 1
+        dt = time.perf_counter() - c0
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} active rows of {spec.name} (of {active}), "
+                         f"single-threaded oracle, {dt:.1f} s"}
+
+    res = {
+        "metric": "logprob rows/s and achieved HBM GB/s (% of peak) at V=248,320, T=8, 128 slots",
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "fp32",
+        "data": "synthetic (seeded Gumbel logits + 10 peak; garbage rows past each prefix)",
+        "config": {"workload": f"{spec.name}: {spec.capacity} slots x T={spec.T} x V={spec.V} "
+                               f"{'bf16' if bf16 else 'fp32'}, emitted 1..{spec.T}, K={spec.K}",
+                   "active_rows": active, "capacity": spec.capacity, "T": spec.T, "V": spec.V,
+                   "K": spec.K, "copies": len(copies), "oracle_rows_checked": checked},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved_gbps / PEAK_HBM_GBPS, "traffic": None},
+        "launch_ms": {"mean": mean_launch_ms, "median": med_launch_ms,
+                      "p10": launch_ms[K // 10], "p90": launch_ms[(9 * K) // 10]},
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "wall_s": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+"""MI355X generation-logprob reduction: Python binding of libflare_logprobs.
+
+This module only marshals arguments.  Every step of the reduction runs in the
+HIP kernels behind the C ABI declared in include/flare_logprobs.h; PyTorch
+supplies device memory and the current stream.  There is no fallback: if the
+shared library is missing the import of a binding function raises.
+
+    plan = Plan(capacity, T, V, V_pad, dtype=torch.bfloat16, K=20)
+    ws = plan.workspace()                                # zeroed once
+    plan.run(logits, tokens, emitted_counts, requested, id_counts, ids, out, ws)
+
+The functions ``flare_logprobs_plan``, ``flare_logprobs_run``,
+``flare_logprobs_workspace_reset``, ``flare_status_string`` and
+``flare_logprobs_abi_version`` mirror the C entry points one to one.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libflare_logprobs.so")
+
+ABI_VERSION = 1
+MAX_K = 20
+MAX_IDS = 128
+ROW_WORDS = 258
+NAN_BITS = 0x7FC00000
+DTYPE_FP32 = 0
+DTYPE_BF16 = 1
+
+STATUS = {0: "FLARE_OK", 1: "FLARE_ERR_INVALID_ARGUMENT", 2: "FLARE_ERR_UNSUPPORTED_DTYPE",
+          3: "FLARE_ERR_PLAN_MISMATCH", 4: "FLARE_ERR_DEVICE", 5: "FLARE_ERR_LAUNCH",
+          6: "FLARE_ERR_UNSUPPORTED_SIZE"}
+
+
+class PlanStruct(ctypes.Structure):
+    """Mirror of flare_logprobs_plan_t."""
+    _fields_ = [("abi_version", ctypes.c_uint32), ("capacity", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("V", ctypes.c_int32), ("V_pad", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("K", ctypes.c_int32), ("device", ctypes.c_int32),
+                ("seg_elems", ctypes.c_int32), ("nseg", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("vector_rows", ctypes.c_int32),
+                ("cu_count", ctypes.c_int32), ("merge_mode", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
+                ("lse_offset", ctypes.c_uint64), ("ticket_offset", ctypes.c_uint64),
+                ("reserved", ctypes.c_uint32 * 8)]
+
+
+class FlareError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({flare_status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        L.flare_logprobs_plan.restype = c.c_int
+        L.flare_logprobs_plan.argtypes = [c.POINTER(PlanStruct), c.c_int32, c.c_int32, c.c_int32,
+                                          c.c_int32, c.c_int32, c.c_int32, c.c_int32]
+        L.flare_logprobs_run.restype = c.c_int
+        L.flare_logprobs_run.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64,
+                                         c.c_int32, c.c_int32, c.c_void_p, c.c_void_p,
+                                         c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32,
+                                         c.c_void_p, c.c_void_p, c.c_void_p]
+        L.flare_logprobs_workspace_reset.restype = c.c_int
+        L.flare_logprobs_workspace_reset.argtypes = [c.POINTER(PlanStruct), c.c_void_p,
+                                                     c.c_void_p]
+        L.flare_status_string.restype = c.c_char_p
+        L.flare_status_string.argtypes = [c.c_int]
+        L.flare_logprobs_abi_version.restype = c.c_uint32
+        L.flare_logprobs_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def flare_status_string(status: int) -> str:
+    return lib().flare_status_string(int(status)).decode()
+
+
+def flare_logprobs_abi_version() -> int:
+    return int(lib().flare_logprobs_abi_version())
+
+
+def dtype_code(dtype) -> int:
+    if dtype in (torch.bfloat16, "bf16", DTYPE_BF16):
+        return DTYPE_BF16
+    if dtype in (torch.float32, "fp32", DTYPE_FP32):
+        return DTYPE_FP32
+    raise ValueError(f"unsupported logits dtype {dtype}")
+
+
+def flare_logprobs_plan(capacity: int, T: int, V: int, V_pad: int, dtype, K: int,
+                        device: int) -> PlanStruct:
+    plan = PlanStruct()
+    rc = lib().flare_logprobs_plan(ctypes.byref(plan), capacity, T, V, V_pad, dtype_code(dtype),
+                                   K, device)
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_plan")
+    return plan
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr() if isinstance(t, torch.Tensor) else int(t)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def flare_logprobs_run(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                       requested, id_counts, ids, emitted_counts, tokens, K: int, out,
+                       workspace, stream=None) -> None:
+    """Launch one reduction on `stream` (default: torch's current stream).
+    Tensor arguments are passed by device pointer; the C library checks the
+    scalars against the plan before anything is launched."""
+    rc = lib().flare_logprobs_run(ctypes.byref(plan), _ptr(logits), dtype_code(dtype), rows, V,
+                                  V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids),
+                                  _ptr(emitted_counts), _ptr(tokens), K, _ptr(out),
+                                  _ptr(workspace), _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_run")
+
+
+def flare_logprobs_workspace_reset(plan: PlanStruct, workspace, stream=None) -> None:
+    rc = lib().flare_logprobs_workspace_reset(ctypes.byref(plan), _ptr(workspace),
+                                              _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_workspace_reset")
+
+
+def _check(t: torch.Tensor, name: str, dtype, numel: int, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() != numel or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} with {numel} elements on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+class Plan:
+    """A validated geometry plus the shapes its tensors must have."""
+
+    def __init__(self, capacity: int, T: int, V: int, V_pad: int | None = None,
+                 dtype=torch.bfloat16, K: int = 20, device: int | None = None):
+        if device is None:
+            device = torch.cuda.current_device()
+        self.torch_dtype = torch.bfloat16 if dtype_code(dtype) == DTYPE_BF16 else torch.float32
+        self.V_pad = V if V_pad is None else V_pad
+        self.raw = flare_logprobs_plan(capacity, T, V, self.V_pad, dtype, K, device)
+        self.capacity, self.T, self.V, self.K, self.device_index = capacity, T, V, K, device
+
+    @property
+    def device(self) -> torch.device:
+        return torch.device("cuda", self.device_index)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.raw.workspace_bytes)
+
+    def workspace(self) -> torch.Tensor:
+        return torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+
+    def lse(self, workspace: torch.Tensor) -> torch.Tensor:
+        """Diagnostic view: the normalization L of every reduced row."""
+        n = self.capacity * self.T
+        off = int(self.raw.lse_offset)
+        return workspace[off:off + 4 * n].view(torch.float32)
+
+    def new_out(self, fill: int = 0) -> torch.Tensor:
+        return torch.full((self.capacity, self.T, ROW_WORDS), fill, dtype=torch.int32,
+                          device=self.device)
+
+    def run(self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
+            stream=None) -> torch.Tensor:
+        dev = self.device
+        rows = self.capacity * self.T
+        _check(logits, "logits", self.torch_dtype, rows * self.V_pad, dev)
+        _check(tokens, "tokens", torch.int32, rows, dev)
+        _check(emitted_counts, "emitted_counts", torch.int32, self.capacity, dev)
+        _check(requested, "requested", torch.int32, self.capacity, dev)
+        _check(id_counts, "id_counts", torch.int32, self.capacity, dev)
+        _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
+        _check(out, "out", torch.int32, rows * ROW_WORDS, dev)
+        _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
+        flare_logprobs_run(self.raw, logits, self.torch_dtype, rows, self.V, self.V_pad,
+                           requested, id_counts, ids, emitted_counts, tokens, self.K, out,
+                           workspace, stream)
+        return out

@@ -1,0 +1,144 @@
+// Host side of the C ABI: argument validation, planning, workspace layout and
+// launch.  Nothing here allocates device memory, synchronizes or compiles.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/flare_logprobs.h"
+#include "flp_internal.h"
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+int32_t pow2_ceil(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p <<= 1;
+  return (int32_t)p;
+}
+
+bool geometry_ok(int32_t capacity, int32_t T, int32_t V, int32_t V_pad, int32_t K) {
+  if (capacity < 1 || T < 1 || V < 1 || V_pad < V) return false;
+  if (K < 0 || K > FLARE_LOGPROBS_MAX_K) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t flare_logprobs_abi_version(void) { return FLARE_LOGPROBS_ABI_VERSION; }
+
+const char* flare_status_string(int status) {
+  switch (status) {
+    case FLARE_OK: return "ok";
+    case FLARE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FLARE_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case FLARE_ERR_PLAN_MISMATCH: return "arguments do not match the plan";
+    case FLARE_ERR_DEVICE: return "device query failed or device is not gfx950";
+    case FLARE_ERR_LAUNCH: return "kernel launch failed";
+    case FLARE_ERR_UNSUPPORTED_SIZE: return "vocabulary too large for the plan";
+    default: return "unknown status";
+  }
+}
+
+int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, int32_t V,
+                        int32_t V_pad, int32_t dtype, int32_t K, int32_t device) {
+  if (!plan) return FLARE_ERR_INVALID_ARGUMENT;
+  memset(plan, 0, sizeof *plan);
+  if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
+  if (!geometry_ok(capacity, T, V, V_pad, K)) return FLARE_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)capacity * T;
+  if (rows > (int64_t)1 << 30) return FLARE_ERR_INVALID_ARGUMENT;
+  const int seg = flp::seg_elems(dtype);
+  const int64_t nseg = ((int64_t)V + seg - 1) / seg;
+  if (nseg > flp::kMaxSegs) return FLARE_ERR_UNSUPPORTED_SIZE;
+  if (rows * nseg > 0x7FFFFFFFll) return FLARE_ERR_UNSUPPORTED_SIZE;
+
+  int32_t cus = 256;
+  if (device >= 0) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device >= count) return FLARE_ERR_DEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FLARE_ERR_DEVICE;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FLARE_ERR_DEVICE;
+    cus = prop.multiProcessorCount;
+  }
+
+  plan->abi_version = FLARE_LOGPROBS_ABI_VERSION;
+  plan->capacity = capacity;
+  plan->T = T;
+  plan->V = V;
+  plan->V_pad = V_pad;
+  plan->dtype = dtype;
+  plan->K = K;
+  plan->device = device;
+  plan->seg_elems = seg;
+  plan->nseg = (int32_t)nseg;
+  plan->block = flp::kBlock;
+  plan->vector_rows = (((int64_t)V_pad * flp::elem_bytes(dtype)) % 16 == 0) ? 1 : 0;
+  plan->cu_count = cus;
+  plan->merge_mode = 0;
+  uint64_t off = 0;
+  plan->record_offset = off;
+  off = align_up(off + (uint64_t)rows * nseg * sizeof(flp::SegRecord), kAlign);
+  plan->lse_offset = off;
+  off = align_up(off + (uint64_t)rows * sizeof(float), kAlign);
+  plan->ticket_offset = off;
+  off = align_up(off + (uint64_t)rows * sizeof(uint32_t), kAlign);
+  plan->workspace_bytes = off;
+  return FLARE_OK;
+}
+
+int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
+                       int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
+                       const int32_t* id_counts, const int32_t* ids,
+                       const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
+                       int32_t* out, void* workspace, void* hip_stream) {
+  if (!plan || !logits || !requested || !id_counts || !ids || !emitted_counts || !tokens ||
+      !out || !workspace)
+    return FLARE_ERR_INVALID_ARGUMENT;
+  if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
+  if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
+  if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad || K != plan->K)
+    return FLARE_ERR_PLAN_MISMATCH;
+  if (rows != (int64_t)plan->capacity * plan->T) return FLARE_ERR_PLAN_MISMATCH;
+  if (((uintptr_t)workspace & 15u) != 0) return FLARE_ERR_INVALID_ARGUMENT;
+
+  char* ws = (char*)workspace;
+  flp::Params p;
+  p.logits = logits;
+  p.requested = requested;
+  p.id_counts = id_counts;
+  p.ids = ids;
+  p.emitted = emitted_counts;
+  p.tokens = tokens;
+  p.out = out;
+  p.records = (flp::SegRecord*)(ws + plan->record_offset);
+  p.lse = (float*)(ws + plan->lse_offset);
+  p.tickets = (uint32_t*)(ws + plan->ticket_offset);
+  p.V_pad = V_pad;
+  p.capacity = plan->capacity;
+  p.T = plan->T;
+  p.V = V;
+  p.K = K;
+  p.nseg = plan->nseg;
+  int32_t held = plan->nseg * flp::kKeep + flp::kBlock;
+  p.merge_pool = pow2_ceil(held < 64 ? 64 : held);
+
+  const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
+  int e = flp::launch_reduce(p, dtype, vec, plan->merge_mode, hip_stream);
+  return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
+}
+
+int flare_logprobs_workspace_reset(const flare_logprobs_plan_t* plan, void* workspace,
+                                   void* hip_stream) {
+  if (!plan || !workspace) return FLARE_ERR_INVALID_ARGUMENT;
+  if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
+  const int64_t rows = (int64_t)plan->capacity * plan->T;
+  uint32_t* t = (uint32_t*)((char*)workspace + plan->ticket_offset);
+  return flp::launch_reset(t, rows, hip_stream) == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
+}
+
+}  // extern "C"

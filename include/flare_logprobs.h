@@ -1,0 +1,148 @@
+/*
+ * flare_logprobs.h -- C ABI of the MI355X (gfx950) generation-logprob
+ * reduction.
+ *
+ * The operation (Flare generation-logprobs design page, definition paragraph
+ * and tiled-reduction paragraph): for every emitted verify position of a
+ * requesting slot, report
+ *     lp(i) = fl32( x[i] - L ),   L = FP32 logsumexp of x over lanes [0, V),
+ * where x is the raw target-logit row, before any sampling transform.  The
+ * chosen token's pair is always written; then either the K natural
+ * alternatives (decreasing lp, then increasing token ID, -0 reported as +0,
+ * padded lanes [V, V_pad) never taking part) or the slot's selected IDs in
+ * caller order with the same L.
+ *
+ * Output layout (design page, buffer table and packed-position paragraph):
+ * one frame int32 [capacity, T, 258]; position (s, t) holds
+ *     [chosen_id, chosen_bits, id_0, bits_0, ..., id_127, bits_127]
+ * where bits are the FP32 value's bit pattern.  Only words [0, 2 + 2W) of
+ * active positions are written, W = K (natural) or the slot's ID count
+ * (selected).  When V < K the unused natural pairs are (-1, 0x7FC00000).
+ *
+ * Gating (design page, gating and zero-flag paragraphs; MTP design page,
+ * round section):  position (s, t) is active iff requested[s] != 0 and
+ * 0 <= t < min(max(emitted_counts[s], 0), T).  Inactive positions read no
+ * logits and write nothing.  Logit row (s, t) is row s*T + t.
+ *
+ * Defined behaviour for device data that cannot be checked without a sync:
+ * emitted counts are clamped to [0, T]; ID counts to [0, 128]; a zero flag
+ * wins over a nonzero count; a chosen or selected ID outside [0, V) is
+ * written as given with bits 0x7FC00000 and never dereferenced.  NaN or +inf
+ * in lanes [0, V) and rows whose every lane is -inf are outside the contract.
+ *
+ * Threading and memory: every device buffer is owned by the caller.  The
+ * library keeps no pointer after a call returns and never allocates, frees,
+ * synchronizes or compiles at run time, so flare_logprobs_run may be captured
+ * in a HIP graph.  Calls on one stream are ordered; concurrent calls need
+ * distinct workspaces.  The inputs are only read.
+ */
+#ifndef FLARE_LOGPROBS_H
+#define FLARE_LOGPROBS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLARE_LOGPROBS_ABI_VERSION 1u
+#define FLARE_LOGPROBS_MAX_K 20
+#define FLARE_LOGPROBS_MAX_IDS 128
+#define FLARE_LOGPROBS_ROW_WORDS 258 /* 2 + 2 * 128 */
+#define FLARE_LOGPROBS_NAN_BITS 0x7FC00000u
+
+enum flare_dtype {
+  FLARE_DTYPE_FP32 = 0, /* IEEE binary32 logits */
+  FLARE_DTYPE_BF16 = 1  /* bfloat16 logits, widened exactly to FP32 */
+};
+
+enum flare_status {
+  FLARE_OK = 0,
+  FLARE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad geometry or K */
+  FLARE_ERR_UNSUPPORTED_DTYPE = 2,
+  FLARE_ERR_PLAN_MISMATCH = 3,    /* run arguments differ from the plan */
+  FLARE_ERR_DEVICE = 4,           /* device query failed or not gfx950 */
+  FLARE_ERR_LAUNCH = 5,           /* a kernel launch reported an error */
+  FLARE_ERR_UNSUPPORTED_SIZE = 6  /* V beyond what the plan can tile */
+};
+
+/*
+ * A plan is a host value filled by flare_logprobs_plan.  It owns nothing and
+ * needs no destruction.  Fields after `device` are chosen by the library and
+ * are informational except workspace_bytes, which the caller must allocate.
+ */
+typedef struct flare_logprobs_plan {
+  uint32_t abi_version;
+  int32_t capacity;      /* padded physical slot capacity */
+  int32_t T;             /* verify rows per slot (k drafts + 1) */
+  int32_t V;             /* vocabulary lanes that count */
+  int32_t V_pad;         /* row stride in elements, V_pad >= V */
+  int32_t dtype;         /* enum flare_dtype */
+  int32_t K;             /* natural alternatives, 0..20 */
+  int32_t device;        /* HIP device ordinal, or -1 for a host-only plan */
+  int32_t seg_elems;     /* vocabulary lanes per segment (one workgroup) */
+  int32_t nseg;          /* segments per row */
+  int32_t block;         /* threads per workgroup */
+  int32_t vector_rows;   /* 1 if V_pad * element size is a multiple of 16 */
+  int32_t cu_count;      /* compute units of `device` (256 if host-only) */
+  int32_t merge_mode;    /* 0: separate merge launch, 1: fused last-arrival merge */
+  uint64_t workspace_bytes; /* bytes of device workspace the caller provides */
+  uint64_t record_offset;   /* per-(row, segment) records */
+  uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
+  uint64_t ticket_offset;   /* uint32[capacity * T]: arrival counters */
+  uint32_t reserved[8];
+} flare_logprobs_plan_t;
+
+/*
+ * Validate a geometry and size a workspace.  Runs on the host only; with
+ * device >= 0 it reads that device's attributes (CU count, architecture).
+ *   capacity >= 1, T >= 1, V >= 1, V_pad >= V, dtype a flare_dtype,
+ *   0 <= K <= 20.
+ * Returns FLARE_OK and fills *plan, or an error and leaves *plan zeroed.
+ */
+int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T,
+                        int32_t V, int32_t V_pad, int32_t dtype, int32_t K,
+                        int32_t device);
+
+/*
+ * Reduce one frame, asynchronously on `hip_stream` (a hipStream_t; NULL is
+ * the null stream) of the current device.
+ *   logits          device, [rows, V_pad] of `dtype`, row-major, read only
+ *   dtype, V, V_pad, K   must equal the plan's (FLARE_ERR_PLAN_MISMATCH)
+ *   rows            number of logit rows; must equal capacity * T
+ *   requested       device int32 [capacity]: nonzero = slot requests logprobs
+ *   id_counts       device int32 [capacity]: 0 = natural mode, n > 0 = n IDs
+ *   ids             device int32 [capacity, 128]: selected IDs, caller order
+ *   emitted_counts  device int32 [capacity]: committed prefix length per slot
+ *   tokens          device int32 [capacity, T]: chosen token of each position
+ *   out             device int32 [capacity, T, 258]: one output frame
+ *   workspace       device, plan->workspace_bytes, 16-byte aligned, zeroed
+ *                   once before first use (the library leaves it reusable)
+ * Host-checkable errors return before anything is launched.
+ */
+int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
+                       int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                       const int32_t* requested, const int32_t* id_counts,
+                       const int32_t* ids, const int32_t* emitted_counts,
+                       const int32_t* tokens, int32_t K, int32_t* out,
+                       void* workspace, void* hip_stream);
+
+/*
+ * Return a workspace to its initial state (all arrival counters zero) with
+ * a fill kernel on `hip_stream`; needed only after a run was abandoned
+ * mid-flight.  Safe to capture in a HIP graph.
+ */
+int flare_logprobs_workspace_reset(const flare_logprobs_plan_t* plan, void* workspace,
+                                   void* hip_stream);
+
+/* Human-readable name of a flare_status value (static storage). */
+const char* flare_status_string(int status);
+
+/* FLARE_LOGPROBS_ABI_VERSION of the loaded library. */
+uint32_t flare_logprobs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLARE_LOGPROBS_H */

@@ -1,0 +1,152 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with status codes before launching anything.  No call
+here reaches a kernel launch."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def flp():
+    import full_vocab_logprob_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return m
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(flare_\w+)\s*\(", text,
+                            flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert {"flare_logprobs_plan", "flare_logprobs_run", "flare_logprobs_workspace_reset",
+            "flare_status_string", "flare_logprobs_abi_version"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol(flp):
+    lib = ctypes.CDLL(flp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(flp):
+    assert flp.flare_logprobs_abi_version() == flp.ABI_VERSION
+    for code in range(7):
+        assert flp.flare_status_string(code) != "unknown status"
+    assert flp.flare_status_string(99) == "unknown status"
+
+
+def test_plan_struct_layout_matches_header(flp):
+    # 14 int32-sized fields, 4 uint64, 8 reserved uint32
+    assert ctypes.sizeof(flp.PlanStruct) == 14 * 4 + 4 * 8 + 8 * 4
+
+
+def host_plan(flp, capacity=128, T=8, V=248320, V_pad=248320, dtype=1, K=20):
+    plan = flp.PlanStruct()
+    rc = flp.lib().flare_logprobs_plan(ctypes.byref(plan), capacity, T, V, V_pad, dtype, K, -1)
+    return rc, plan
+
+
+def test_plan_host_only_geometry(flp):
+    rc, p = host_plan(flp)
+    assert rc == 0
+    assert p.nseg == 16 and p.seg_elems == 16384 and p.block == 256 and p.vector_rows == 1
+    assert p.cu_count == 256 and p.abi_version == 1
+    rows = 128 * 8
+    assert p.lse_offset >= rows * 16 * 272 and p.ticket_offset >= p.lse_offset + 4 * rows
+    assert p.workspace_bytes >= p.ticket_offset + 4 * rows
+    rc, p = host_plan(flp, capacity=1024, T=4, V=262144, V_pad=262144, dtype=0)
+    assert rc == 0 and p.nseg == 32 and p.seg_elems == 8192
+    rc, p = host_plan(flp, V=37, V_pad=41)
+    assert rc == 0 and p.vector_rows == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(capacity=0), 1), (dict(T=0), 1), (dict(V=0), 1), (dict(V_pad=100, V=200), 1),
+    (dict(K=-1), 1), (dict(K=21), 1), (dict(dtype=2), 2), (dict(dtype=-1), 2),
+    (dict(V=16384 * 64 + 1, V_pad=16384 * 64 + 1), 6),
+])
+def test_plan_rejects(flp, kw, status):
+    rc, p = host_plan(flp, **kw)
+    assert rc == status
+    assert p.abi_version == 0  # left zeroed
+
+
+def test_plan_null_pointer(flp):
+    assert flp.lib().flare_logprobs_plan(None, 1, 1, 1, 1, 0, 0, -1) == 1
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+def run_status(flp, plan, **over):
+    args = dict(logits=FAKE, dtype=plan.dtype, rows=plan.capacity * plan.T, V=plan.V,
+                V_pad=plan.V_pad, requested=FAKE, id_counts=FAKE, ids=FAKE, emitted=FAKE,
+                tokens=FAKE, K=plan.K, out=FAKE, workspace=FAKE, stream=None)
+    args.update(over)
+    return flp.lib().flare_logprobs_run(
+        ctypes.byref(plan), args["logits"], args["dtype"], args["rows"], args["V"],
+        args["V_pad"], args["requested"], args["id_counts"], args["ids"], args["emitted"],
+        args["tokens"], args["K"], args["out"], args["workspace"], args["stream"])
+
+
+@pytest.mark.parametrize("field", ["logits", "requested", "id_counts", "ids", "emitted",
+                                   "tokens", "out", "workspace"])
+def test_run_rejects_null_pointers(flp, field):
+    rc, plan = host_plan(flp)
+    assert rc == 0
+    assert run_status(flp, plan, **{field: None}) == 1
+
+
+@pytest.mark.parametrize("over", [dict(dtype=0), dict(V=1000), dict(V_pad=248321), dict(K=5),
+                                  dict(rows=1023)])
+def test_run_rejects_plan_mismatch(flp, over):
+    rc, plan = host_plan(flp)
+    assert run_status(flp, plan, **over) == 3
+
+
+def test_run_rejects_bad_dtype_and_stale_plan(flp):
+    rc, plan = host_plan(flp)
+    assert run_status(flp, plan, dtype=7) == 2
+    plan.abi_version = 99
+    assert run_status(flp, plan) == 3
+    assert flp.lib().flare_logprobs_run(None, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        0, FAKE, FAKE, None) == 1
+
+
+def test_run_rejects_misaligned_workspace(flp):
+    rc, plan = host_plan(flp)
+    assert run_status(flp, plan, workspace=FAKE + 4) == 1
+
+
+def test_reset_rejects_null(flp):
+    rc, plan = host_plan(flp)
+    assert flp.lib().flare_logprobs_workspace_reset(ctypes.byref(plan), None, None) == 1
+    assert flp.lib().flare_logprobs_workspace_reset(None, FAKE, None) == 1
+
+
+def test_binding_names_mirror_the_abi(flp):
+    for name in declared_functions():
+        assert callable(getattr(flp, name)), name
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "full_vocab_logprob_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("oracle_handle", ""), f

@@ -1,0 +1,300 @@
+"""Parity of the HIP path with the CPU oracle (needs an MI355X).
+
+Every test prints the case it runs before touching the GPU.  Inputs come from
+the seeded generator; expected values come from the oracle only.
+"""
+from __future__ import annotations
+
+import json
+import glob
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import full_vocab_logprob_amd as flp
+    flp.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    yield
+
+
+def full_compare(o, spec, **kw):
+    announce(f"full compare {spec.name} cap={spec.capacity} T={spec.T} V={spec.V} "
+             f"V_pad={spec.V_pad} dtype={spec.dtype} K={spec.K} {kw}")
+    w = synth.make(spec)
+    got, lse = H.run_gpu(w)
+    ref = H.oracle_frame(o, w)
+    H.compare_words(got, ref, spec.name)
+    H.check_properties(w, got, lse)
+    return w, got, ref, lse
+
+
+# ------------------------------------------------------------ named workloads
+def test_c1_decode_full(oracle_handle):
+    full_compare(oracle_handle, synth.CONFIGS["C1"])
+
+
+def test_c2_padded_half_requesting_full(oracle_handle):
+    full_compare(oracle_handle, synth.CONFIGS["C2"])
+
+
+@pytest.mark.parametrize("cap,T", [(8, 8), (3, 5)])
+def test_c3_verify_reduced(oracle_handle, cap, T):
+    full_compare(oracle_handle, synth.CONFIGS["C3"].with_(capacity=cap, T=T))
+
+
+def test_c4_ties_and_selected_reduced(oracle_handle):
+    w, got, ref, lse = full_compare(oracle_handle, synth.CONFIGS["C4"].with_(capacity=16))
+    assert (w.id_counts > 0).sum() == 6
+
+
+@pytest.mark.parametrize("variant", ["K20", "K0", "sel128"])
+def test_c5_large_batch_reduced(oracle_handle, variant):
+    spec = synth.CONFIGS["C5"].with_(capacity=4)
+    if variant == "K0":
+        spec = spec.with_(K=0)
+    elif variant == "sel128":
+        spec = spec.with_(selected="all")
+    full_compare(oracle_handle, spec)
+
+
+def sampled_full_size(o, spec, nsample=24):
+    announce(f"full size {spec.name} cap={spec.capacity} T={spec.T} V={spec.V} (sampled rows)")
+    w = synth.make(spec)
+    got, lse = H.run_gpu(w)
+    act = np.nonzero(w.active_mask().reshape(-1))[0]
+    rng = np.random.default_rng(spec.seed + 100)
+    pick = sorted(set(rng.choice(act, size=min(nsample, act.size), replace=False).tolist()
+                      + [int(act[0]), int(act[-1])]))
+    worst = 0.0
+    for r in pick:
+        sl, t = divmod(r, spec.T)
+        n = int(np.clip(w.id_counts[sl], 0, 128))
+        sel = w.ids[sl * 128: sl * 128 + n] if n > 0 else None
+        words, L = o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, sel=sel, V=spec.V)
+        H.compare_words(got[sl, t, :len(words)], words, f"{spec.name} row {r}")
+        assert abs(float(lse[r]) - L) <= H.TOL, (r, lse[r], L)
+        worst = max(worst, H.max_value_delta(got[sl, t, :len(words)], words))
+    H.check_properties(w, got, lse)
+    announce(f"{spec.name}: {len(pick)} sampled rows exact, max |d logprob| = {worst:.3g}")
+
+
+def test_c3_full_size_sampled(oracle_handle):
+    sampled_full_size(oracle_handle, synth.CONFIGS["C3"])
+
+
+def test_c4_full_size_sampled(oracle_handle):
+    sampled_full_size(oracle_handle, synth.CONFIGS["C4"])
+
+
+def test_c5_full_size_sampled(oracle_handle):
+    sampled_full_size(oracle_handle, synth.CONFIGS["C5"], nsample=12)
+
+
+# ----------------------------------------------------------------- edge cases
+EDGE = [
+    ("v1", dict(V=1, V_pad=1)),
+    ("v5_vpad8", dict(V=5, V_pad=8)),
+    ("v19", dict(V=19, V_pad=19)),
+    ("v37_unaligned", dict(V=37, V_pad=41)),
+    ("one_segment", dict(V=16384, V_pad=16384)),
+    ("segment_plus_one", dict(V=16385, V_pad=16392)),
+    ("ragged_chunk", dict(V=2 * 16384 + 3, V_pad=2 * 16384 + 8)),
+    ("unaligned_stride", dict(V=50001, V_pad=50003)),
+    ("k1", dict(V=30000, V_pad=30000, K=1)),
+    ("k0", dict(V=30000, V_pad=30000, K=0)),
+]
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(oracle_handle, dtype, name, kw):
+    spec = synth.CONFIGS["C3"].with_(capacity=3, T=4, dtype=dtype, recipe=synth.GUMBEL,
+                                     p1=10.0, seed=77, **kw)
+    full_compare(oracle_handle, spec)
+
+
+def _frame_from_rows(rows_f32: np.ndarray, dtype, T=1, K=20, V_pad=None):
+    """A workload whose active rows are the given rows (one slot per row)."""
+    nrow, V = rows_f32.shape
+    V_pad = V if V_pad is None else V_pad
+    spec = synth.Spec("designed", nrow, T, V, V_pad, dtype, synth.NORMAL, K=K, emitted="one",
+                      seed=9)
+    req, emi, tok, cnt, ids = synth.gating(spec)
+    buf = np.zeros((nrow * T, V_pad), np.float32)
+    buf[::T, :V] = rows_f32
+    logits = synth.bf16_bits(buf) if dtype == synth.BF16 else buf
+    return synth.Workload(spec, np.ascontiguousarray(logits), req, emi, tok, cnt, ids)
+
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP32], ids=["bf16", "fp32"])
+def test_ties_all_equal_and_one_hot_rows(oracle_handle, dtype):
+    """All-equal rows and one-hot rows take the tie fallback inside segments."""
+    V = 40000
+    rows = np.zeros((6, V), np.float32)
+    rows[1, :] = -3.0
+    rows[2, :] = -np.inf
+    rows[2, 31337] = 2.0
+    rows[3, :] = -np.inf
+    rows[3, 7] = -0.0
+    rows[4, :] = (np.arange(V) % 3).astype(np.float32)  # many ties at 2.0
+    rows[5, :] = -np.inf
+    rows[5, 39999] = 5.0
+    rows[5, 16384] = 5.0
+    announce(f"designed tie rows dtype={dtype}")
+    w = _frame_from_rows(rows, dtype)
+    got, lse = H.run_gpu(w)
+    ref = H.oracle_frame(oracle_handle, w)
+    H.compare_words(got, ref, "ties")
+    H.check_properties(w, got, lse)
+    # one finite lane: L is that lane's value and its logprob is exactly +0
+    assert got[2, 0, 2] == 31337 and got[2, 0, 3] == 0
+    assert got[3, 0, 2] == 7 and got[3, 0, 3] == 0
+
+
+@pytest.mark.parametrize("dtype", [synth.FP32, synth.BF16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("background", ["neginf", "noise"])
+def test_guard_trips_on_subtraction_ties(oracle_handle, dtype, background):
+    """Segment 0 holds 32 distinct logits that all round to the same reported
+    value after subtracting L.  Its best 32 raw keys keep the largest of them
+    and drop the smallest, which have the smallest IDs and so belong in the
+    top K.  The merge guard must catch this and rescan the segment.  With a
+    -inf background the segment takes the in-segment tie fallback; with a
+    noise background it takes the ordinary candidate path."""
+    V = 3 * 16384
+    rng = np.random.default_rng(5)
+    if background == "neginf":
+        row = np.full(V, -np.inf, np.float32)
+    else:
+        row = rng.uniform(-10.0, -5.0, size=V).astype(np.float32)
+        if dtype == synth.BF16:
+            row = synth.bf16_to_f32(synth.bf16_bits(row))
+    if dtype == synth.FP32:
+        base = np.float32(1.0)
+        for k in range(33):
+            row[k] = base
+            base = np.nextafter(base, np.float32(2.0))
+        row[50] = 100.0
+    else:
+        for k in range(33):
+            row[k] = np.float32((k + 1) * 2.0 ** -30)  # exact in bf16
+        row[50] = 10.0
+    announce(f"guard trip row dtype={dtype} background={background}")
+    w = _frame_from_rows(row[None, :], dtype)
+    got, lse = H.run_gpu(w)
+    ref = H.oracle_frame(oracle_handle, w)
+    assert ref[0, 0, 2:8:2].tolist() == [50, 0, 1]
+    H.compare_words(got, ref, "guard")
+
+
+def test_golden_fixtures_on_gpu(oracle_handle):
+    for path in sorted(glob.glob(os.path.join(HERE, "golden", "*.json"))):
+        fx = json.load(open(path))
+        announce(f"golden {fx['name']}")
+        if fx["dtype"] == "bf16":
+            vals = synth.bf16_to_f32(np.asarray(fx["row_bits"], np.uint16))
+            dt = synth.BF16
+        else:
+            vals = np.asarray(fx["row_bits"], np.uint32).view(np.float32)
+            dt = synth.FP32
+        w = _frame_from_rows(vals[None, :].astype(np.float32), dt, K=fx["K"])
+        w.tokens[0] = fx["token"]
+        if fx["sel"]:
+            w.id_counts[0] = len(fx["sel"])
+            w.ids[:len(fx["sel"])] = fx["sel"]
+        got, _ = H.run_gpu(w)
+        H.compare_words(got[0, 0, :len(fx["words"])], np.asarray(fx["words"], np.int32),
+                        fx["name"])
+
+
+def test_gating_clamps_and_invalid_ids(oracle_handle):
+    spec = synth.CONFIGS["C3"].with_(capacity=6, T=3, V=20000, V_pad=20000, seed=31)
+    w = synth.make(spec)
+    w.requested[:] = [1, 0, 1, 1, 1, 1]
+    w.emitted[:] = [2, 3, 0, 9, -4, 3]
+    w.id_counts[:] = [-5, 4, 3, 0, 0, 300]
+    w.ids[5 * 128:6 * 128] = np.arange(128) * 7
+    w.ids[5 * 128 + 3] = -1
+    w.ids[5 * 128 + 4] = 20000
+    w.ids[5 * 128 + 5] = 2**31 - 1
+    w.ids[1 * 128:1 * 128 + 4] = [1, 2, 3, 4]
+    w.tokens[3 * 3 + 1] = -7
+    w.tokens[3 * 3 + 2] = 20000
+    announce("gating clamps and invalid ids")
+    got, lse = H.run_gpu(w)
+    ref = H.oracle_frame(oracle_handle, w)
+    H.compare_words(got, ref, "gating")
+
+
+def test_unaligned_base_pointer(oracle_handle):
+    """A logits pointer 2 bytes past a 16-byte boundary takes the scalar path."""
+    spec = synth.CONFIGS["C3"].with_(capacity=2, T=2, V=33000, V_pad=33000, seed=41)
+    w = synth.make(spec)
+    d = H.to_device(w)
+    n = d["logits"].numel()
+    big = torch.empty(n + 8, dtype=torch.bfloat16, device="cuda")
+    big[1:1 + n].copy_(d["logits"])
+    view = big[1:1 + n]
+    assert view.data_ptr() % 16 == 2
+    announce("unaligned base pointer bf16")
+    got, lse = H.run_gpu(w, dev_inputs=d, logits=view)
+    ref = H.oracle_frame(oracle_handle, w)
+    H.compare_words(got, ref, "unaligned")
+
+
+# -------------------------------------------------- repeatability and graphs
+def test_repeatable_bit_identical():
+    spec = synth.CONFIGS["C3"].with_(capacity=16)
+    w = synth.make(spec)
+    d = H.to_device(w)
+    plan = H.make_plan(spec)
+    ws = plan.workspace()
+    announce("repeatability C3 cap=16")
+    a, la = H.run_gpu(w, d, plan, ws)
+    b, lb = H.run_gpu(w, d, plan, ws)
+    assert np.array_equal(a, b) and np.array_equal(la.view(np.int32), lb.view(np.int32))
+
+
+def test_hip_graph_replay_matches_eager():
+    spec = synth.CONFIGS["C4"].with_(capacity=8, seed=44)
+    w = synth.make(spec)
+    d = H.to_device(w)
+    plan = H.make_plan(spec)
+    ws = plan.workspace()
+    announce("hip graph capture and replay C4 cap=8")
+    eager, _ = H.run_gpu(w, d, plan, ws)
+    out = plan.new_out(H.POISON)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            plan.run(d["logits"], d["tokens"], d["emitted"], d["requested"], d["id_counts"],
+                     d["ids"], out, ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(H.POISON)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {i}"
+        del junk
