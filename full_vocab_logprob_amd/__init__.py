@@ -41,9 +41,10 @@ class PlanStruct(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint32), ("capacity", ctypes.c_int32),
                 ("T", ctypes.c_int32), ("V", ctypes.c_int32), ("V_pad", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("K", ctypes.c_int32), ("device", ctypes.c_int32),
-                ("seg_elems", ctypes.c_int32), ("nseg", ctypes.c_int32),
-                ("block", ctypes.c_int32), ("vector_rows", ctypes.c_int32),
-                ("cu_count", ctypes.c_int32), ("merge_mode", ctypes.c_int32),
+                ("unit_elems", ctypes.c_int32), ("units", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("vector_rows", ctypes.c_int32), ("cu_count", ctypes.c_int32),
+                ("fused", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
                 ("lse_offset", ctypes.c_uint64), ("ticket_offset", ctypes.c_uint64),
                 ("reserved", ctypes.c_uint32 * 8)]
@@ -159,12 +160,14 @@ class Plan:
     """A validated geometry plus the shapes its tensors must have."""
 
     def __init__(self, capacity: int, T: int, V: int, V_pad: int | None = None,
-                 dtype=torch.bfloat16, K: int = 20, device: int | None = None):
+                 dtype=torch.bfloat16, K: int = 20, device: int | None = None,
+                 fused: bool = False):
         if device is None:
             device = torch.cuda.current_device()
         self.torch_dtype = torch.bfloat16 if dtype_code(dtype) == DTYPE_BF16 else torch.float32
         self.V_pad = V if V_pad is None else V_pad
         self.raw = flare_logprobs_plan(capacity, T, V, self.V_pad, dtype, K, device)
+        self.raw.fused = 1 if fused else 0
         self.capacity, self.T, self.V, self.K, self.device_index = capacity, T, V, K, device
 
     @property

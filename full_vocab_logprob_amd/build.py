@@ -29,7 +29,8 @@ def build(verbose: bool = False) -> str:
     cmds = [
         [HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, "flp_kernels.hip"),
          "-o", kobj],
-        [HIPCC, *COMMON, "-c", os.path.join(CSRC, "flp_host.cpp"), "-o", hobj],
+        [HIPCC, *COMMON, f"--offload-arch={ARCH}", "-c", os.path.join(CSRC, "flp_host.cpp"),
+         "-o", hobj],
         [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, hobj, "-o", LIB + ".tmp"],
     ]
     for c in cmds:

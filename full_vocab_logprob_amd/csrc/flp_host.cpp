@@ -12,12 +12,6 @@ constexpr uint64_t kAlign = 256;
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
-int32_t pow2_ceil(int64_t v) {
-  int64_t p = 1;
-  while (p < v) p <<= 1;
-  return (int32_t)p;
-}
-
 bool geometry_ok(int32_t capacity, int32_t T, int32_t V, int32_t V_pad, int32_t K) {
   if (capacity < 1 || T < 1 || V < 1 || V_pad < V) return false;
   if (K < 0 || K > FLARE_LOGPROBS_MAX_K) return false;
@@ -49,14 +43,15 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   memset(plan, 0, sizeof *plan);
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
   if (!geometry_ok(capacity, T, V, V_pad, K)) return FLARE_ERR_INVALID_ARGUMENT;
+  if (capacity > flp::kMaxCapacity) return FLARE_ERR_INVALID_ARGUMENT;
   const int64_t rows = (int64_t)capacity * T;
   if (rows > (int64_t)1 << 30) return FLARE_ERR_INVALID_ARGUMENT;
-  const int seg = flp::seg_elems(dtype);
-  const int64_t nseg = ((int64_t)V + seg - 1) / seg;
-  if (nseg > flp::kMaxSegs) return FLARE_ERR_UNSUPPORTED_SIZE;
-  if (rows * nseg > 0x7FFFFFFFll) return FLARE_ERR_UNSUPPORTED_SIZE;
+  const int unit = flp::unit_elems(dtype);
+  const int64_t units = ((int64_t)V + unit - 1) / unit;
+  if (units > flp::kMaxUnits) return FLARE_ERR_UNSUPPORTED_SIZE;
+  const bool vec = ((int64_t)V_pad * flp::elem_bytes(dtype)) % 16 == 0;
 
-  int32_t cus = 256;
+  int32_t cus = 256, per_cu = 4;
   if (device >= 0) {
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || device >= count) return FLARE_ERR_DEVICE;
@@ -64,6 +59,12 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
     if (hipGetDeviceProperties(&prop, device) != hipSuccess) return FLARE_ERR_DEVICE;
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return FLARE_ERR_DEVICE;
     cus = prop.multiProcessorCount;
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return FLARE_ERR_DEVICE;
+    if (prev != device && hipSetDevice(device) != hipSuccess) return FLARE_ERR_DEVICE;
+    per_cu = flp::reduce_occupancy(dtype, vec, capacity);
+    if (prev != device && hipSetDevice(prev) != hipSuccess) return FLARE_ERR_DEVICE;
+    if (per_cu < 1) return FLARE_ERR_DEVICE;
   }
 
   plan->abi_version = FLARE_LOGPROBS_ABI_VERSION;
@@ -74,15 +75,16 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   plan->dtype = dtype;
   plan->K = K;
   plan->device = device;
-  plan->seg_elems = seg;
-  plan->nseg = (int32_t)nseg;
+  plan->unit_elems = unit;
+  plan->units = (int32_t)units;
   plan->block = flp::kBlock;
-  plan->vector_rows = (((int64_t)V_pad * flp::elem_bytes(dtype)) % 16 == 0) ? 1 : 0;
+  plan->grid = cus * per_cu;
+  plan->vector_rows = vec ? 1 : 0;
   plan->cu_count = cus;
-  plan->merge_mode = 0;
+  plan->fused = 0;
   uint64_t off = 0;
   plan->record_offset = off;
-  off = align_up(off + (uint64_t)rows * nseg * sizeof(flp::SegRecord), kAlign);
+  off = align_up(off + (uint64_t)rows * units * sizeof(flp::PartRecord), kAlign);
   plan->lse_offset = off;
   off = align_up(off + (uint64_t)rows * sizeof(float), kAlign);
   plan->ticket_offset = off;
@@ -104,6 +106,9 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, in
   if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad || K != plan->K)
     return FLARE_ERR_PLAN_MISMATCH;
   if (rows != (int64_t)plan->capacity * plan->T) return FLARE_ERR_PLAN_MISMATCH;
+  if (plan->grid < 1 || plan->units < 1 || plan->units > flp::kMaxUnits ||
+      (plan->fused != 0 && plan->fused != 1))
+    return FLARE_ERR_PLAN_MISMATCH;
   if (((uintptr_t)workspace & 15u) != 0) return FLARE_ERR_INVALID_ARGUMENT;
 
   char* ws = (char*)workspace;
@@ -115,7 +120,7 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, in
   p.emitted = emitted_counts;
   p.tokens = tokens;
   p.out = out;
-  p.records = (flp::SegRecord*)(ws + plan->record_offset);
+  p.records = (flp::PartRecord*)(ws + plan->record_offset);
   p.lse = (float*)(ws + plan->lse_offset);
   p.tickets = (uint32_t*)(ws + plan->ticket_offset);
   p.V_pad = V_pad;
@@ -123,12 +128,12 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, in
   p.T = plan->T;
   p.V = V;
   p.K = K;
-  p.nseg = plan->nseg;
-  int32_t held = plan->nseg * flp::kKeep + flp::kBlock;
-  p.merge_pool = pow2_ceil(held < 64 ? 64 : held);
+  p.units = plan->units;
+  p.grid = plan->grid;
+  p.fused = plan->fused;
 
   const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
-  int e = flp::launch_reduce(p, dtype, vec, plan->merge_mode, hip_stream);
+  const int e = flp::launch_reduce(p, dtype, vec, hip_stream);
   return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
 }
 

@@ -5,27 +5,31 @@
 
 namespace flp {
 
-constexpr int kBlock = 256;      // threads per workgroup (4 wave64s)
+constexpr int kBlock = 256;        // threads per workgroup (4 wave64s)
 constexpr int kWaves = kBlock / 64;
-constexpr int kChunks = 8;       // 16-byte chunks held per thread
-constexpr int kKeep = 32;        // raw keys a segment retains
-constexpr int kMaxSegs = 64;     // segments per row the merge pool supports
+constexpr int kChunks = 8;         // 16-byte chunks each thread holds per unit
+constexpr int kKeep = 32;          // raw keys a part keeps
+constexpr int kMaxUnits = 64;      // units per row (one merge lane per unit)
+constexpr int kMaxCapacity = 8192; // slots whose active-row prefix fits in LDS
 
-// Vocabulary lanes per 16-byte chunk and per segment (= one workgroup).
+// Vocabulary lanes per 16-byte chunk, and per unit: the lanes one workgroup
+// holds in registers at a time (16,384 bf16 or 8,192 FP32 lanes, 32 KiB).
 constexpr int elems_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }
-constexpr int seg_elems(int dtype) { return kBlock * kChunks * elems_per_chunk(dtype); }
+constexpr int unit_elems(int dtype) { return kBlock * kChunks * elems_per_chunk(dtype); }
 constexpr int elem_bytes(int dtype) { return dtype == 1 ? 2 : 4; }
 
-// One segment's contribution to a row: its max and exp-sum relative to that
-// max, and its best raw keys (value, then smaller ID), sorted descending.
-struct SegRecord {
+// One part's contribution to a row: a part is the run of consecutive units
+// of one row that one workgroup reduced.  m is the part's max, s the sum of
+// exp(x - m) over its lanes, keys its best raw keys (value, then smaller ID)
+// sorted descending.  Stored at records[row * units + first unit of part].
+struct PartRecord {
   float m;
   float s;
-  int32_t n;      // keys held (kKeep unless the segment has fewer lanes)
-  int32_t flags;  // kRecComplete: every lane of the segment is held
+  int32_t n;      // keys held (kKeep unless the part has fewer lanes)
+  int32_t flags;  // kRecComplete: every lane of the part is held
   uint64_t keys[kKeep];
 };
-static_assert(sizeof(SegRecord) == 272, "record layout");
+static_assert(sizeof(PartRecord) == 272, "record layout");
 constexpr int32_t kRecComplete = 1;
 
 struct Params {
@@ -36,7 +40,7 @@ struct Params {
   const int32_t* emitted;
   const int32_t* tokens;
   int32_t* out;
-  SegRecord* records;
+  PartRecord* records;
   float* lse;
   uint32_t* tickets;
   int64_t V_pad;
@@ -44,13 +48,16 @@ struct Params {
   int32_t T;
   int32_t V;
   int32_t K;
-  int32_t nseg;
-  int32_t merge_pool;  // keys in the merge workgroup's LDS pool (power of 2)
+  int32_t units;   // units per row
+  int32_t grid;    // workgroups of the persistent launch
+  int32_t fused;   // 1: the last part of a row merges it in the same launch
 };
 
 // Launchers implemented in flp_kernels.hip; return a hipError_t as int.
-int launch_reduce(const Params& p, int dtype, bool vector_rows, int merge_mode,
-                  void* stream);
+int launch_reduce(const Params& p, int dtype, bool vector_rows, void* stream);
 int launch_reset(uint32_t* tickets, int64_t n, void* stream);
+// Resident workgroups per CU of the reduction kernel (0 on error).
+int reduce_occupancy(int dtype, bool vector_rows, int capacity);
+size_t reduce_lds_bytes(int capacity);
 
 }  // namespace flp

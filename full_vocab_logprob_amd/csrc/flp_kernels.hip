@@ -3,29 +3,35 @@
 // What is computed (Flare generation-logprobs design page, definition and
 // tiled-reduction paragraphs): for each emitted position, L = FP32 logsumexp
 // of the raw logits over lanes [0, V); the chosen token's fl32(x - L); then
-// either the K best lanes by (fl32(x - L) desc, ID asc) with -0 read as +0,
-// or the caller's selected IDs in order.
+// either the K best lanes by (fl32(x - L) desc, ID asc), -0 read as +0, or
+// the caller's selected IDs in caller order.
 //
-// How (a single read of every logit; no MFMA, nothing here is a contraction):
-//   segment pass, one workgroup per (active row, segment of 16K bf16 / 8K FP32
-//   lanes): each thread loads 8 x 16-byte chunks with coalesced dwordx4 loads
-//   and keeps them in VGPRs; per wave: max, then sum of exp2 against that
-//   max; across the 4 waves an exact segment (m, s).  Natural-mode rows also
-//   pick the segment's 32 best *raw* keys (value, then smaller ID) while the
-//   data is still in registers: the 32nd-largest lane maximum is found by an
-//   LDS radix select, only 16-byte chunks whose maximum reaches it are
-//   staged to LDS, their qualifying lanes become 64-bit keys, and a bitonic
-//   sort keeps the best 32.
-//   merge, one workgroup per active row: combine the segment (m, s) in
-//   segment order into L, re-key the retained candidates by the reported
-//   value fl32(x - L), sort, and check an exactness guard per segment; a
-//   segment that fails it is rescanned with final keys.  Then the chosen
-//   and selected-ID gathers and the packed write.
+// How.  Every logit is read from HBM once; nothing here is a contraction, so
+// there is no MFMA.  One persistent launch of `grid` workgroups.  The work is
+// the concatenation, over active rows, of each row's units (16,384 bf16 or
+// 8,192 FP32 lanes, 32 KiB); workgroup g owns the contiguous unit range
+// [g N / grid, (g + 1) N / grid), so every workgroup streams the same number
+// of bytes and a range may cross rows.  The units of one row inside one range
+// form a part.
+//   Per unit, each thread holds 8 x 16-byte chunks (coalesced dwordx4 loads)
+//   in VGPRs.  Each wave keeps a running (max, sum of exp2) for the part.
+//   Natural-mode rows also feed an LDS candidate pool: a unit's threshold is
+//   the wave's 32nd-largest lane maximum (ballot radix select) until the
+//   pool's first compaction, then the part's running 32nd-best key; only
+//   16-byte chunks whose maximum passes it are staged to LDS and expanded
+//   into 64-bit raw keys (value, then smaller ID).  Compaction sorts 64-key
+//   lists in registers and rank-merges them (no block-wide sort).
+//   At the end of a part the workgroup writes a part record (m, s, best 32
+//   raw keys), publishes it with an agent-scope release fence and adds the
+//   part's unit count to the row's ticket; the workgroup that completes the
+//   ticket merges the row: L from the parts in part order, the chosen and
+//   selected gathers, and the natural top K re-keyed by the reported value
+//   fl32(x - L), with an exactness guard that rescans a part when the raw
+//   order it kept could differ from the final order.
 //
 // The pages' own scheme ranks normalized values in a second pass over the
 // vocabulary; ranking raw values and re-keying only the survivors is what
-// lets this path read the logits once.  The guard makes the two agree
-// exactly (see merge_kernel).
+// lets this path read the logits once.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,22 +44,21 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kNanBits = 0x7FC00000u;
-constexpr int kStageCap = 64;   // hot chunks staged per wave
-constexpr int kPoolCap = 512;   // candidate keys per segment
 constexpr int kRowWords = 258;
 
 // ------------------------------------------------------------------ keys
 // Order-preserving map of an FP32 value (with -0 read as +0) to uint32.
 __device__ __forceinline__ uint32_t ukey32(float x) {
   x = (x == 0.0f) ? 0.0f : x;
-  uint32_t b = __float_as_uint(x);
+  const uint32_t b = __float_as_uint(x);
   return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float unkey32(uint32_t u) {
-  uint32_t b = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  const uint32_t b = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
   return __uint_as_float(b);
 }
-// 64-bit key: larger value first, then smaller token ID.
+// 64-bit key: larger value first, then smaller token ID.  Never 0 for a
+// real lane (the key of -inf is 0x007FFFFF in the high word).
 __device__ __forceinline__ uint64_t make_key(float x, uint32_t id) {
   return ((uint64_t)ukey32(x) << 32) | (uint64_t)(~id);
 }
@@ -72,50 +77,49 @@ template <int DT> struct Elem;
 template <> struct Elem<1> {  // bf16
   static constexpr int kPer = 8;
   static constexpr int kBytes = 2;
-  static constexpr int kDigits = 2;  // a bf16 value's key has 16 bits
   static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
   __device__ static __forceinline__ float get(const uint4& r, int j) {
-    uint32_t w = (j >> 1) == 0 ? r.x : (j >> 1) == 1 ? r.y : (j >> 1) == 2 ? r.z : r.w;
+    const uint32_t w = (j >> 1) == 0 ? r.x : (j >> 1) == 1 ? r.y : (j >> 1) == 2 ? r.z : r.w;
     return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
   }
   __device__ static __forceinline__ uint32_t load_bits(const char* row, int64_t i) {
     return (uint32_t)(*(const uint16_t*)(row + 2 * i));
   }
-  // Previous representable input value, for the merge guard.
+  // Largest input value below x (skipping -0, equal to +0 after canon0).
   __device__ static __forceinline__ float pred(float x) {
-    uint32_t u = ukey32(x) >> 16;  // 16-bit key of a bf16 value
-    uint32_t v = u - 1;
-    if (v == 0x7FFFu) v = 0x7FFEu;  // skip -0: it equals +0 after canon0
-    uint32_t h = (v & 0x8000u) ? (v & 0x7FFFu) : (~v & 0xFFFFu);
-    return __uint_as_float(h << 16);
-  }
-  __device__ static __forceinline__ float key_floor(uint32_t k16) {
-    uint32_t h = (k16 & 0x8000u) ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu);
+    uint32_t v = (ukey32(x) >> 16) - 1;
+    if (v == 0x7FFFu) v = 0x7FFEu;
+    const uint32_t h = (v & 0x8000u) ? (v & 0x7FFFu) : (~v & 0xFFFFu);
     return __uint_as_float(h << 16);
   }
 };
 template <> struct Elem<0> {  // fp32
   static constexpr int kPer = 4;
   static constexpr int kBytes = 4;
-  static constexpr int kDigits = 4;
   static constexpr uint32_t kNegInfWord = 0xFF800000u;
   __device__ static __forceinline__ float get(const uint4& r, int j) {
-    uint32_t w = j == 0 ? r.x : j == 1 ? r.y : j == 2 ? r.z : r.w;
+    const uint32_t w = j == 0 ? r.x : j == 1 ? r.y : j == 2 ? r.z : r.w;
     return __uint_as_float(w);
   }
   __device__ static __forceinline__ uint32_t load_bits(const char* row, int64_t i) {
     return *(const uint32_t*)(row + 4 * i);
   }
   __device__ static __forceinline__ float pred(float x) {
-    uint32_t u = ukey32(x);
-    uint32_t v = u - 1;
-    if (v == 0x7FFFFFFFu) v = 0x7FFFFFFEu;  // skip -0
+    uint32_t v = ukey32(x) - 1;
+    if (v == 0x7FFFFFFFu) v = 0x7FFFFFFEu;
     return unkey32(v);
   }
-  __device__ static __forceinline__ float key_floor(uint32_t k32) { return unkey32(k32); }
 };
 
-// Chunk holding lanes [first, first + kPer) of a row; lanes >= V read as -inf.
+// Smallest FP32 value whose order key has the 16-bit prefix k16 (for the
+// prefix of a bf16 value, that value itself).
+__device__ __forceinline__ float key_floor16(uint32_t k16) {
+  uint32_t u = k16 << 16;
+  if (!(u & 0x80000000u)) u |= 0xFFFFu;
+  return unkey32(u);
+}
+
+// Chunk holding lanes [first, first + kPer) of a row; lanes >= V read -inf.
 template <int DT, bool VEC>
 __device__ __forceinline__ uint4 load_chunk(const char* row, int64_t first, int V) {
   using E = Elem<DT>;
@@ -125,7 +129,7 @@ __device__ __forceinline__ uint4 load_chunk(const char* row, int64_t first, int 
   if (VEC) {
     r = *(const uint4*)(row + first * E::kBytes);
     if (first + E::kPer > V) {
-      int nv = (int)(V - first);
+      const int nv = (int)(V - first);
       uint32_t* w = &r.x;
 #pragma unroll
       for (int j = 0; j < E::kPer; ++j) {
@@ -143,9 +147,9 @@ __device__ __forceinline__ uint4 load_chunk(const char* row, int64_t first, int 
     uint32_t* w = &r.x;
 #pragma unroll
     for (int j = 0; j < E::kPer; ++j) {
-      int64_t i = first + j;
+      const int64_t i = first + j;
       if (i < V) {
-        uint32_t b = E::load_bits(row, i);
+        const uint32_t b = E::load_bits(row, i);
         if (DT == 1) {
           uint32_t& word = w[j >> 1];
           word = (j & 1) ? ((word & 0x0000FFFFu) | (b << 16)) : ((word & 0xFFFF0000u) | b);
@@ -160,537 +164,791 @@ __device__ __forceinline__ uint4 load_chunk(const char* row, int64_t first, int 
 
 template <int DT>
 __device__ __forceinline__ float load_elem(const char* row, int64_t i) {
-  uint32_t b = Elem<DT>::load_bits(row, i);
+  const uint32_t b = Elem<DT>::load_bits(row, i);
   return __uint_as_float(DT == 1 ? (b << 16) : b);
 }
 
-// ------------------------------------------------------- wave / block helpers
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+// ------------------------------------------------------ fast cross-lane ops
+// All exchanges are VALU lane permutes (DPP and the gfx950 permlane swaps),
+// never LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
+// Value held by lane ^ X.
+template <int X>
+__device__ __forceinline__ uint32_t xlane(uint32_t v, int lane) {
+  if constexpr (X == 1) {
+    return dpp32<0xB1>(v);  // quad_perm [1,0,3,2]
+  } else if constexpr (X == 2) {
+    return dpp32<0x4E>(v);  // quad_perm [2,3,0,1]
+  } else if constexpr (X == 4) {
+    return dpp32<0x1B>(dpp32<0x141>(v));  // row_half_mirror, then quad_perm [3,2,1,0]
+  } else if constexpr (X == 8) {
+    return dpp32<0x128>(v);  // row_ror:8
+  } else if constexpr (X == 15) {
+    return dpp32<0x140>(v);  // row_mirror
+  } else if constexpr (X == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    static_assert(X == 32, "lane distance");
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? p[0] : p[1];
   }
+}
+template <int X>
+__device__ __forceinline__ uint64_t xlane64(uint64_t v, int lane) {
+  const uint32_t lo = xlane<X>((uint32_t)v, lane);
+  const uint32_t hi = xlane<X>((uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int X>
+__device__ __forceinline__ float xlanef(float v, int lane) {
+  return __uint_as_float(xlane<X>(__float_as_uint(v), lane));
+}
+// Value held by lane 63 - lane.
+__device__ __forceinline__ uint64_t reverse64(uint64_t v, int lane) {
+  return xlane64<32>(xlane64<16>(xlane64<15>(v, lane), lane), lane);
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Butterfly reductions: every lane ends with the same value, and the
+// order of the additions is fixed, so the sum is deterministic.
+__device__ __forceinline__ float wave_max(float v, int lane) {
+  v = fmaxf(v, xlanef<32>(v, lane));
+  v = fmaxf(v, xlanef<16>(v, lane));
+  v = fmaxf(v, xlanef<8>(v, lane));
+  v = fmaxf(v, xlanef<4>(v, lane));
+  v = fmaxf(v, xlanef<2>(v, lane));
+  v = fmaxf(v, xlanef<1>(v, lane));
   return v;
 }
+__device__ __forceinline__ float wave_sum(float v, int lane) {
+  v += xlanef<32>(v, lane);
+  v += xlanef<16>(v, lane);
+  v += xlanef<8>(v, lane);
+  v += xlanef<4>(v, lane);
+  v += xlanef<2>(v, lane);
+  v += xlanef<1>(v, lane);
+  return v;
+}
+
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Bitonic sort of pool[0, n) descending (n a power of two, all threads).
-__device__ __forceinline__ void block_sort_desc(uint64_t* pool, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += kBlock) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          uint64_t a = pool[i], b = pool[ixj];
-          bool first_half = (i & k) == 0;
-          if (first_half ? (a < b) : (a > b)) {
-            pool[i] = b;
-            pool[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+// Order LDS accesses of one wave (no other wave is involved).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ int pow2_at_least(int n, int lo) {
-  int p = lo;
-  while (p < n) p <<= 1;
-  return p;
+// One compare-exchange step of a bitonic network: the lane keeps the larger
+// key when `keep_max`.
+template <int STRIDE>
+__device__ __forceinline__ uint64_t cx(uint64_t k, int lane, bool keep_max) {
+  const uint64_t o = xlane64<STRIDE>(k, lane);
+  return keep_max ? (k > o ? k : o) : (k < o ? k : o);
+}
+// Sort one key per lane, descending by lane index.
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t k, int lane) {
+#define FLP_STEP(SIZE, STRIDE) \
+  k = cx<STRIDE>(k, lane, ((lane & (SIZE)) == 0) == ((lane & (STRIDE)) == 0));
+  FLP_STEP(2, 1)
+  FLP_STEP(4, 2) FLP_STEP(4, 1)
+  FLP_STEP(8, 4) FLP_STEP(8, 2) FLP_STEP(8, 1)
+  FLP_STEP(16, 8) FLP_STEP(16, 4) FLP_STEP(16, 2) FLP_STEP(16, 1)
+  FLP_STEP(32, 16) FLP_STEP(32, 8) FLP_STEP(32, 4) FLP_STEP(32, 2) FLP_STEP(32, 1)
+  FLP_STEP(64, 32) FLP_STEP(64, 16) FLP_STEP(64, 8) FLP_STEP(64, 4) FLP_STEP(64, 2)
+  FLP_STEP(64, 1)
+#undef FLP_STEP
+  return k;
+}
+// Sort a bitonic sequence (one key per lane) descending.
+__device__ __forceinline__ uint64_t bitonic_merge_desc(uint64_t k, int lane) {
+  k = cx<32>(k, lane, (lane & 32) == 0);
+  k = cx<16>(k, lane, (lane & 16) == 0);
+  k = cx<8>(k, lane, (lane & 8) == 0);
+  k = cx<4>(k, lane, (lane & 4) == 0);
+  k = cx<2>(k, lane, (lane & 2) == 0);
+  k = cx<1>(k, lane, (lane & 1) == 0);
+  return k;
+}
+// Lanes 0..31 of the result hold the best 32 of {top[0..32), list[0..64)}
+// sorted descending, given `top` sorted in lanes 0..31 and `list` sorted.
+__device__ __forceinline__ uint64_t merge_top32(uint64_t top, uint64_t list, int lane) {
+  const uint64_t rev = reverse64(list, lane);
+  return bitonic_merge_desc(lane < 32 ? top : rev, lane);
 }
 
-// The k-th largest of the voters' D-digit keys (one key per thread), by an
-// LDS radix select over 8-bit digits.  Requires at least k voters.
-template <int D>
-__device__ uint32_t block_kth_largest(uint32_t key, bool voter, int k, uint32_t* hist,
-                                      int* bcast) {
-  const int tid = threadIdx.x, lane = tid & 63;
+// The q-th largest 16-bit key among the wave's voting lanes (ballot radix
+// select; requires at least q voters).
+__device__ __forceinline__ uint32_t wave_kth_largest16(uint32_t key, bool voter, int q) {
   uint32_t prefix = 0;
-  int need = k;
 #pragma unroll
-  for (int d = D - 1; d >= 0; --d) {
-    hist[tid] = 0;
-    __syncthreads();
-    bool match = voter && (d == D - 1 || (key >> (8 * (d + 1))) == prefix);
-    if (match) atomicAdd(&hist[(key >> (8 * d)) & 255u], 1u);
-    __syncthreads();
-    if (tid < 64) {
-      int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-          h3 = hist[4 * lane + 3];
-      int own = h0 + h1 + h2 + h3;
-      int suf = own;  // inclusive suffix sum over lanes
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += t;
-      }
-      int above = suf - own;  // count in bins of higher lanes
-      int c3 = above + h3, c2 = c3 + h2, c1 = c2 + h1, c0 = c1 + h0;
-      int b = -1, gt = 0;
-      if (c3 >= need) { b = 4 * lane + 3; gt = above; }
-      else if (c2 >= need) { b = 4 * lane + 2; gt = c3; }
-      else if (c1 >= need) { b = 4 * lane + 1; gt = c2; }
-      else if (c0 >= need) { b = 4 * lane; gt = c1; }
-      // cnt_ge is non-increasing in the bin, so the highest qualifying bin
-      // lies in the highest lane that found one.
-      uint64_t found = __ballot(b >= 0);
-      int top = 63 - __builtin_clzll(found);
-      if (lane == top) {
-        bcast[0] = b;
-        bcast[1] = gt;
-      }
-    }
-    __syncthreads();
-    prefix = (prefix << 8) | (uint32_t)bcast[0];
-    need -= bcast[1];
-    __syncthreads();
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t trial = prefix | (1u << b);
+    const uint64_t m = __ballot(voter && key >= trial);
+    if (__popcll(m) >= q) prefix = trial;
   }
   return prefix;
 }
 
-// ============================================================ segment pass
-struct SegShared {
-  uint32_t hist[256];
-  int bcast[4];
+// ------------------------------------------------------- per-wave key pool
+// Each wave keeps, for the part it is reducing, a pool of candidate raw keys
+// that always contains the best 32 keys of the wave's lanes seen so far.
+// Compaction keeps exactly those 32 and makes their 32nd the admission bar.
+constexpr int kWavePool = 128;
+
+struct WavePool {
+  uint64_t* keys;  // this wave's kWavePool slots in LDS
+  int count;
+  bool have_bar;
+  uint64_t bar;    // 32nd-best key after the last compaction
+};
+
+__device__ __forceinline__ void pool_compact(WavePool& wp, int lane) {
+  wave_sync();
+  uint64_t a = lane < wp.count ? wp.keys[lane] : 0ull;
+  a = sort64_desc(a, lane);
+  if (wp.count > 64) {
+    uint64_t b = 64 + lane < wp.count ? wp.keys[64 + lane] : 0ull;
+    b = sort64_desc(b, lane);
+    a = merge_top32(a, b, lane);
+  }
+  wave_sync();
+  if (lane < kKeep) wp.keys[lane] = a;
+  wave_sync();
+  if (wp.count >= kKeep) {
+    wp.have_bar = true;
+    wp.bar = readlane64(a, kKeep - 1);
+    wp.count = kKeep;
+  }
+}
+
+// Append one key per lane (0 = none).
+__device__ __forceinline__ void pool_append(WavePool& wp, uint64_t k, int lane) {
+  uint64_t m = __ballot(k != 0ull);
+  if (m == 0ull) return;
+  int n = __popcll(m);
+  if (wp.count + n > kWavePool) {
+    pool_compact(wp, lane);
+    if (wp.have_bar && k <= wp.bar) k = 0ull;
+    m = __ballot(k != 0ull);
+    if (m == 0ull) return;
+    n = __popcll(m);
+  }
+  if (k != 0ull) wp.keys[wp.count + lanes_below(m)] = k;
+  wp.count += n;
+}
+
+// ------------------------------------------------------------ shared state
+struct Smem {
+  uint64_t pool[kWaves][kWavePool];  // per-wave pools; a 256-key batch in merges
+  int32_t stage_off[kWaves][kChunks * 64];  // first lane of each hot chunk
   float wm[kWaves];
   float ws[kWaves];
-  int wcount[kWaves];
-  int pool_count;
-  int overflow;
-  uint4 stage[kWaves][kStageCap];
-  int32_t stage_off[kWaves][kStageCap];
-  uint64_t pool[kPoolCap];
+  uint32_t ticket_old;
+  float L;
+  int n_parts;
+  int unsafe_any;
+  int16_t part_u0[kMaxUnits + 1];
+  int scan[kWaves];
 };
 
-__device__ __forceinline__ bool row_active(const Params& p, int row, int* n_sel) {
-  int s = row / p.T;
-  int t = row - s * p.T;
-  if (p.requested[s] == 0) return false;
-  int e = p.emitted[s];
-  e = e < 0 ? 0 : (e > p.T ? p.T : e);
-  if (t >= e) return false;
-  int n = p.id_counts[s];
-  *n_sel = n < 0 ? 0 : (n > 128 ? 128 : n);
-  return true;
-}
-
-// Keep the best kKeep keys of pool[0, count): sort, zero the rest.
-__device__ void pool_compact(uint64_t* pool, int count, int cap) {
-  for (int i = count + threadIdx.x; i < cap; i += kBlock) pool[i] = 0;
+// Sort each wave's 64 keys of batch[0, 256), then fold them into wave 0's
+// running best-32 `top` (lanes 0..31).  All threads; two barriers.
+__device__ __forceinline__ void fold_batch(uint64_t* batch, uint64_t& top, int lane, int w) {
   __syncthreads();
-  block_sort_desc(pool, pow2_at_least(count, 64));
+  uint64_t v = sort64_desc(batch[w * 64 + lane], lane);
+  batch[w * 64 + lane] = v;
+  __syncthreads();
+  if (w == 0) {
+    top = merge_top32(top, v, lane);
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) top = merge_top32(top, batch[q * 64 + lane], lane);
+  }
+  __syncthreads();
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) void segment_kernel(Params p) {
-  using E = Elem<DT>;
-  constexpr int kPer = E::kPer;
-  constexpr int kWaveElems = 64 * kChunks * kPer;
-  constexpr int kSegElems = kWaves * kWaveElems;
-  __shared__ SegShared sh;
+// ------------------------------------------------------------- row mapping
+__device__ __forceinline__ int slot_rows(const Params& p, int s) {
+  if (p.requested[s] == 0) return 0;
+  const int e = p.emitted[s];
+  return e < 0 ? 0 : (e > p.T ? p.T : e);
+}
 
-  const int row = blockIdx.x / p.nseg;
-  const int seg = blockIdx.x - row * p.nseg;
-  int n_sel = 0;
-  if (!row_active(p, row, &n_sel)) return;
-  const bool need_cand = (p.K > 0) && (n_sel == 0);
-
+// prefix[s] = active rows of slots before s; prefix[capacity] = total.
+__device__ int build_prefix(const Params& p, int* prefix, Smem& sh) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int V = p.V;
-  const int64_t seg_base = (int64_t)seg * kSegElems;
-  const int64_t wave_base = seg_base + (int64_t)w * kWaveElems;
-  const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * E::kBytes;
-
-  uint4 raw[kChunks];
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c)
-    raw[c] = load_chunk<DT, VEC>(rowp, wave_base + (int64_t)(c * 64 + lane) * kPer, V);
-
-  // ---- statistics: wave max, then sum of exp2 relative to it
-  float cm[kChunks];
-  float lm = kNegInf;
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    float m = E::get(raw[c], 0);
-#pragma unroll
-    for (int j = 1; j < kPer; ++j) m = fmaxf(m, E::get(raw[c], j));
-    cm[c] = m;
-    lm = fmaxf(lm, m);
+  const int cap = p.capacity;
+  const int per = (cap + kBlock - 1) / kBlock;
+  const int s0 = tid * per;
+  const int s1 = s0 + per < cap ? s0 + per : cap;
+  int local = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int c = slot_rows(p, s);
+    prefix[s] = c;
+    local += c;
   }
-  const float mw = wave_max(lm);
-  float sum = 0.0f;
-  if (mw != kNegInf) {
-    // exp2((x - m) * log2 e): the maximum's own term is exactly 1, so a row
-    // with one finite lane gets L equal to that lane and a logprob of +0.
+  // exclusive scan of `local` over the block (values can exceed 15 here)
+  int incl = local;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c)
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        sum += __builtin_amdgcn_exp2f((E::get(raw[c], j) - mw) * kLog2e);
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
   }
-  sum = wave_sum(sum);
-  if (lane == 0) {
-    sh.wm[w] = mw;
-    sh.ws[w] = sum;
-  }
-  if (tid == 0) {
-    sh.pool_count = 0;
-    sh.overflow = 0;
-  }
+  if (lane == 63) sh.scan[w] = incl;
   __syncthreads();
-  SegRecord* rec = p.records + (int64_t)row * p.nseg + seg;
-  if (tid == 0) {
-    float M = sh.wm[0];
-    for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[i]);
-    float S = 0.0f;
-    if (M != kNegInf) {
-      for (int i = 0; i < kWaves; ++i)
-        if (sh.wm[i] != kNegInf)
-          S += sh.ws[i] * __builtin_amdgcn_exp2f((sh.wm[i] - M) * kLog2e);
-    }
-    rec->m = M;
-    rec->s = S;
-    if (!need_cand) {
-      rec->n = 0;
-      rec->flags = 0;
-    }
-  }
-  if (!need_cand) return;
-
-  // ---- candidates: threshold = 32nd-largest lane maximum over valid lanes
-  const int64_t nvalid64 = (int64_t)V - seg_base;
-  const int nvalid = nvalid64 > kSegElems ? kSegElems : (int)nvalid64;
-  int valid_lanes = 0;
+  int run = incl - local, total = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    int rem = nvalid - i * kWaveElems;
-    int vl = rem <= 0 ? 0 : (rem + kPer - 1) / kPer;
-    valid_lanes += vl > 64 ? 64 : vl;
+    run += i < w ? sh.scan[i] : 0;
+    total += sh.scan[i];
   }
-  const bool lane_valid = (wave_base + (int64_t)lane * kPer) < V;
-  const bool take_all = valid_lanes < kKeep;
-  float tau = kNegInf;
-  if (!take_all) {
-    uint32_t k = ukey32(lm) >> (32 - 8 * E::kDigits);
-    uint32_t kth = block_kth_largest<E::kDigits>(k, lane_valid, kKeep, sh.hist, sh.bcast);
-    tau = E::key_floor(kth);
+  for (int s = s0; s < s1; ++s) {
+    const int c = prefix[s];
+    prefix[s] = run;
+    run += c;
   }
-
-  // ---- stage hot chunks (max reaches tau) into LDS in (chunk, lane) order
-  int nh = 0;
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int64_t first = wave_base + (int64_t)(c * 64 + lane) * kPer;
-    const bool hot = first < V && cm[c] >= tau;
-    const uint64_t m = __ballot(hot);
-    const int slot = nh + lanes_below(m);
-    if (hot && slot < kStageCap) {
-      sh.stage[w][slot] = raw[c];
-      sh.stage_off[w][slot] = (int32_t)(first - seg_base);
-    }
-    nh += __popcll(m);
-  }
-  if (nh > kStageCap && lane == 0) sh.overflow = 1;
+  if (tid == 0) prefix[cap] = total;
   __syncthreads();
-  const bool overflow_stage = sh.overflow != 0;
-
-  if (!overflow_stage) {
-    // Lane i expands staged chunk i into keys of qualifying lanes.
-    uint64_t keys[kPer];
-    int cnt = 0;
-    if (lane < nh) {
-      const uint4 r = sh.stage[w][lane];
-      const int64_t off = seg_base + sh.stage_off[w][lane];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const float x = E::get(r, j);
-        const int64_t id = off + j;
-        keys[j] = 0;
-        if (id < V && x >= tau) keys[j] = make_key(x, (uint32_t)id);
-        cnt += keys[j] != 0;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) keys[j] = 0;
-    }
-    const int incl = wave_incl_scan(cnt, lane);
-    if (lane == 63) sh.wcount[w] = incl;
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      base += (i < w) ? sh.wcount[i] : 0;
-      total += sh.wcount[i];
-    }
-    if (total <= kPoolCap) {
-      int pos = base + incl - cnt;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (keys[j] != 0) sh.pool[pos++] = keys[j];
-      __syncthreads();
-      pool_compact(sh.pool, total, kPoolCap);
-      if (tid == 0) sh.pool_count = total;
-      __syncthreads();
-    } else {
-      __syncthreads();
-      if (tid == 0) sh.overflow = 1;
-      __syncthreads();
-    }
-  }
-
-  if (sh.overflow != 0) {
-    // Exact fallback for tie-heavy segments: stream every qualifying lane
-    // through the pool, compacting to the best kKeep whenever it fills; the
-    // admission threshold rises to the kKeep-th key after each compaction.
-    __syncthreads();
-    if (tid == 0) sh.pool_count = 0;
-    __syncthreads();
-    uint64_t thr = take_all ? 0ull : ((uint64_t)ukey32(tau) << 32);
-    // The lanes are read again (from cache) so that no register array is
-    // indexed dynamically here.
-#pragma unroll 1
-    for (int c = 0; c < kChunks; ++c) {
-      const int64_t first = wave_base + (int64_t)(c * 64 + lane) * kPer;
-#pragma unroll 1
-      for (int j = 0; j < kPer; ++j) {
-        const int64_t id = first + j;
-        if (id < V) {
-          const uint64_t key = make_key(load_elem<DT>(rowp, id), (uint32_t)id);
-          if (key >= thr) {
-            int at = atomicAdd(&sh.pool_count, 1);
-            sh.pool[at] = key;
-          }
-        }
-        __syncthreads();
-        const int count = sh.pool_count;
-        if (count > kPoolCap - kBlock) {
-          pool_compact(sh.pool, count, kPoolCap);
-          thr = sh.pool[kKeep - 1];
-          __syncthreads();
-          if (tid == 0) sh.pool_count = kKeep;
-          __syncthreads();
-        }
-      }
-    }
-    const int count = sh.pool_count;
-    pool_compact(sh.pool, count, kPoolCap);
-    __syncthreads();
-  }
-
-  const int held = sh.pool_count < kKeep ? sh.pool_count : kKeep;
-  if (tid < kKeep) rec->keys[tid] = tid < held ? sh.pool[tid] : 0ull;
-  if (tid == 0) {
-    rec->n = held;
-    rec->flags = (nvalid <= kKeep) ? kRecComplete : 0;
-  }
+  return total;
 }
 
-// ================================================================== merge
-// Per row: L from the segment records; chosen and selected gathers; natural
-// top-K from the retained raw candidates re-keyed by the reported value.
+// Slot of active row a: the largest s with prefix[s] <= a.
+__device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
+  int lo = 0, hi = cap;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= a) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Is global unit x the first unit of some workgroup's range?
+__device__ __forceinline__ bool range_start(int64_t x, int64_t N, int64_t G) {
+  const int64_t g = (x * G + N - 1) / N;
+  return g <= G && (g * N) / G == x;
+}
+
+// ==================================================================== merge
+// Merge row `row` (active row a, slot s): L from its parts in part order,
+// the chosen and selected gathers, and the natural top K.
 //
-// Exactness guard.  Segment j holds its best 32 raw keys; let c be the 32nd,
+// Exactness guard.  A part keeps its best 32 raw keys; let c be the 32nd,
 // with value x_c.  With F the final key (reported value, then smaller ID),
-// F_K the K-th best final key among all held candidates and v_K its value,
-// every lane e that segment j dropped has either x_e == x_c and a larger ID
+// F_K the K-th best final key among all kept candidates and v_K its value,
+// every lane e that the part dropped has either x_e == x_c and a larger ID
 // (so F(e) < F(c)) or x_e <= pred(x_c) (so its value is at most
 // r(pred(x_c)), r(x) = fl32(x - L) being monotone).  Hence if F(c) <= F_K
-// and r(pred(x_c)) < v_K no dropped lane can enter the top K.  A segment
-// failing either test is rescanned lane by lane with final keys; F_K over a
+// and r(pred(x_c)) < v_K no dropped lane can enter the top K.  A part that
+// fails either test is rescanned lane by lane with final keys; F_K over a
 // subset never exceeds the true K-th key, so the test stays sound.
-struct MergeShared {
-  float red[kBlock];
-  int count;
-  int unsafe_any;
-  uint8_t unsafe[kMaxSegs];
-};
-
-__device__ float block_max_all(float v, float* red) {
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, red[i]);
-  __syncthreads();
-  return r;
-}
-
-// Deterministic block sum: a fixed tree over thread slots.
-__device__ float block_sum_fixed(float v, float* red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = kBlock / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  float r = red[0];
-  __syncthreads();
-  return r;
-}
-
 template <int DT>
-__device__ void merge_row(const Params& p, int row, int n_sel, MergeShared& sh,
-                          uint64_t* pool) {
+__device__ void merge_row(const Params& p, Smem& sh, int64_t N, int row, int a, int s,
+                          int n_sel, bool natural) {
   using E = Elem<DT>;
-  constexpr int kSegElems = kBlock * kChunks * E::kPer;
-  const int tid = threadIdx.x;
-  const int V = p.V;
-  const int nseg = p.nseg;
-  const SegRecord* rec = p.records + (int64_t)row * nseg;
+  constexpr int kUnitElems = kBlock * kChunks * E::kPer;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int V = p.V, U = p.units;
+  const PartRecord* rec = p.records + (int64_t)row * U;
   const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * E::kBytes;
   int32_t* out = p.out + (int64_t)row * kRowWords;
+  const int tok = p.tokens[row];
+  const int sel_id = tid < n_sel ? p.ids[(int64_t)s * 128 + tid] : 0;
 
-  // ---- normalization, combined in segment order
-  float M = kNegInf;
-  for (int j = tid; j < nseg; j += kBlock) M = fmaxf(M, rec[j].m);
-  M = block_max_all(M, sh.red);
-  float part = 0.0f;
-  if (M != kNegInf)
-    for (int j = tid; j < nseg; j += kBlock) {
-      float mj = rec[j].m;
-      if (mj != kNegInf) part += rec[j].s * __builtin_amdgcn_exp2f((mj - M) * kLog2e);
+  // ---- the row's parts (one lane per unit) and L (one lane per part)
+  if (w == 0) {
+    const bool start = lane < U && (lane == 0 || range_start((int64_t)a * U + lane, N, p.grid));
+    const uint64_t m = __ballot(start);
+    const int np = __popcll(m);
+    if (start) sh.part_u0[lanes_below(m)] = (int16_t)lane;
+    if (lane == 0) {
+      sh.n_parts = np;
+      sh.part_u0[np] = (int16_t)U;
+      sh.unsafe_any = 0;
     }
-  const float S = block_sum_fixed(part, sh.red);
-  const float L = M + logf(S);
-  if (tid == 0) p.lse[row] = L;
+    wave_sync();
+    float pm = kNegInf, ps = 0.0f;
+    if (lane < np) {
+      const PartRecord& r = rec[sh.part_u0[lane]];
+      pm = r.m;
+      ps = r.s;
+    }
+    const float M = wave_max(pm, lane);
+    float term = 0.0f;
+    if (lane < np && pm != kNegInf) term = ps * __builtin_amdgcn_exp2f((pm - M) * kLog2e);
+    const float S = wave_sum(term, lane);
+    const float L = M + logf(S);
+    if (lane == 0) {
+      sh.L = L;
+      p.lse[row] = L;
+    }
+  }
+  __syncthreads();
+  const float L = sh.L;
+  const int np = sh.n_parts;
 
-  // ---- chosen token
+  // ---- chosen token and selected IDs
   if (tid == 0) {
-    const int tok = p.tokens[row];
     uint32_t bits = kNanBits;
     if (tok >= 0 && tok < V) bits = __float_as_uint(reported(load_elem<DT>(rowp, tok), L));
     out[0] = tok;
     out[1] = (int32_t)bits;
   }
-
-  // ---- selected IDs, caller order
-  if (n_sel > 0) {
-    const int s = row / p.T;
-    for (int j = tid; j < n_sel; j += kBlock) {
-      const int id = p.ids[(int64_t)s * 128 + j];
-      uint32_t bits = kNanBits;
-      if (id >= 0 && id < V) bits = __float_as_uint(reported(load_elem<DT>(rowp, id), L));
-      out[2 + 2 * j] = id;
-      out[3 + 2 * j] = (int32_t)bits;
-    }
-    return;
+  if (tid < n_sel) {
+    uint32_t bits = kNanBits;
+    if (sel_id >= 0 && sel_id < V) bits = __float_as_uint(reported(load_elem<DT>(rowp, sel_id), L));
+    *(int2*)(out + 2 + 2 * tid) = make_int2(sel_id, (int32_t)bits);
   }
-  const int K = p.K;
-  if (K == 0) return;
-
-  // ---- natural top-K from the held candidates
-  const int cap = p.merge_pool;
-  const int held_slots = nseg * kKeep;
-  for (int i = tid; i < cap; i += kBlock) {
-    uint64_t f = 0;
-    if (i < held_slots) {
-      const int j = i / kKeep, k = i - j * kKeep;
-      if (k < rec[j].n) f = final_key(rec[j].keys[k], L);
+  if (natural) {
+    const int K = p.K;
+    const int Keff = K < V ? K : V;
+    uint64_t* batch = &sh.pool[0][0];
+    uint64_t top = 0ull;  // wave 0: best 32 final keys so far, lanes 0..31
+    // ---- kept candidates, 8 parts (256 keys) per batch, re-keyed by F
+    for (int pb = 0; pb < np; pb += kBlock / kKeep) {
+      const int part = pb + (tid >> 5), k = tid & 31;
+      uint64_t f = 0ull;
+      if (part < np) {
+        const uint64_t raw = rec[sh.part_u0[part]].keys[k];
+        if (raw != 0ull) f = final_key(raw, L);
+      }
+      batch[tid] = f;
+      fold_batch(batch, top, lane, w);
     }
-    pool[i] = f;
-  }
-  if (tid == 0) sh.unsafe_any = 0;
-  __syncthreads();
-  block_sort_desc(pool, pow2_at_least(held_slots, 64));
-  const int Keff = K < V ? K : V;
-  const uint64_t FK = pool[Keff - 1];
-  const uint32_t vK = (uint32_t)(FK >> 32);
-  for (int j = tid; j < nseg; j += kBlock) {
-    bool bad = false;
-    if (!(rec[j].flags & kRecComplete)) {
-      const uint64_t c = rec[j].keys[kKeep - 1];
-      const float xc = key_value(c);
-      bool ok = final_key(c, L) <= FK;
-      if (ok && xc != kNegInf) ok = ukey32(reported(E::pred(xc), L)) < vK;
-      bad = !ok;
-    }
-    sh.unsafe[j] = bad ? 1 : 0;
-    if (bad) atomicOr(&sh.unsafe_any, 1);
-  }
-  __syncthreads();
-
-  if (sh.unsafe_any) {
-    // Rebuild: held candidates of safe segments, then every lane of each
-    // unsafe segment whose final key reaches the bound FK.
-    if (tid == 0) sh.count = 0;
-    __syncthreads();
-    for (int i = tid; i < held_slots; i += kBlock) {
-      const int j = i / kKeep, k = i - j * kKeep;
-      if (!sh.unsafe[j] && k < rec[j].n) {
-        const int at = atomicAdd(&sh.count, 1);
-        pool[at] = final_key(rec[j].keys[k], L);
+    // ---- guard, one lane per part (wave 0 holds the K-th key)
+    if (w == 0) {
+      const uint64_t FK = readlane64(top, Keff - 1);
+      const uint32_t vK = (uint32_t)(FK >> 32);
+      bool bad = false;
+      if (lane < np) {
+        const PartRecord& r = rec[sh.part_u0[lane]];
+        if (!(r.flags & kRecComplete)) {
+          const uint64_t c = r.keys[kKeep - 1];
+          const float xc = key_value(c);
+          bool ok = final_key(c, L) <= FK;
+          if (ok && xc != kNegInf) ok = ukey32(reported(E::pred(xc), L)) < vK;
+          bad = !ok;
+        }
+      }
+      const uint64_t m = __ballot(bad);
+      if (lane == 0) {
+        sh.unsafe_any = m != 0ull;
+        batch[256] = m;  // unsafe parts (slot past the batch)
+        batch[257] = FK;
       }
     }
     __syncthreads();
-    uint64_t thr = FK;
-    for (int j = 0; j < nseg; ++j) {
-      if (!sh.unsafe[j]) continue;
-      const int64_t lo = (int64_t)j * kSegElems;
-      const int64_t hi = lo + kSegElems < V ? lo + kSegElems : V;
-      for (int64_t b = lo; b < hi; b += kBlock) {
-        const int64_t i = b + tid;
-        if (i < hi) {
-          const uint64_t f = make_key(reported(load_elem<DT>(rowp, i), L), (uint32_t)i);
-          if (f >= thr) {
-            const int at = atomicAdd(&sh.count, 1);
-            pool[at] = f;
+    if (sh.unsafe_any) {
+      // Rebuild from the safe parts' candidates plus every lane of each
+      // unsafe part whose final key reaches FK.
+      const uint64_t unsafe = batch[256];
+      const uint64_t FK = batch[257];
+      top = 0ull;
+      for (int pb = 0; pb < np; pb += kBlock / kKeep) {
+        const int part = pb + (tid >> 5), k = tid & 31;
+        uint64_t f = 0ull;
+        if (part < np && !((unsafe >> part) & 1ull)) {
+          const uint64_t raw = rec[sh.part_u0[part]].keys[k];
+          if (raw != 0ull) f = final_key(raw, L);
+        }
+        batch[tid] = f;
+        fold_batch(batch, top, lane, w);
+      }
+      for (int part = 0; part < np; ++part) {
+        if (!((unsafe >> part) & 1ull)) continue;
+        const int64_t lo = (int64_t)sh.part_u0[part] * kUnitElems;
+        int64_t hi = (int64_t)sh.part_u0[part + 1] * kUnitElems;
+        hi = hi < V ? hi : V;
+        for (int64_t b = lo; b < hi; b += kBlock) {
+          const int64_t i = b + tid;
+          uint64_t f = 0ull;
+          if (i < hi) {
+            f = make_key(reported(load_elem<DT>(rowp, i), L), (uint32_t)i);
+            if (f < FK) f = 0ull;
+          }
+          batch[tid] = f;
+          fold_batch(batch, top, lane, w);
+        }
+      }
+    }
+    if (w == 0 && lane < K) {
+      int32_t id = -1;
+      uint32_t bits = kNanBits;
+      if (lane < Keff) {
+        id = (int32_t)key_id(top);
+        bits = __float_as_uint(unkey32((uint32_t)(top >> 32)));
+      }
+      *(int2*)(out + 2 + 2 * lane) = make_int2(id, (int32_t)bits);
+    }
+  }
+  __syncthreads();
+}
+
+// ================================================================== reduce
+// Where a unit sits: active row a, unit u of that row, slot s, logit row.
+struct UnitPos {
+  int a, u, s, row;
+  const char* rowp;
+};
+
+template <int DT>
+__device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, int64_t x) {
+  UnitPos q;
+  q.a = (int)(x / p.units);
+  q.u = (int)(x - (int64_t)q.a * p.units);
+  q.s = slot_of(prefix, p.capacity, q.a);
+  q.row = q.s * p.T + (q.a - prefix[q.s]);
+  q.rowp = (const char*)p.logits + (int64_t)q.row * p.V_pad * Elem<DT>::kBytes;
+  return q;
+}
+
+// Chunk c of this lane in the wave's slice starting at wave_base.
+template <int DT, bool VEC>
+__device__ __forceinline__ uint4 load_lane_chunk(const char* rowp, int64_t wave_base, int c,
+                                                 int lane, int V, bool interior) {
+  using E = Elem<DT>;
+  const int64_t first = wave_base + (int64_t)(c * 64 + lane) * E::kPer;
+  if (VEC && interior) return *(const uint4*)(rowp + first * E::kBytes);
+  return load_chunk<DT, VEC>(rowp, first, V);
+}
+
+// Append the keys a lane holds (0 = none) to its wave's pool in one step;
+// returns false if they do not fit even after a compaction.
+template <int N>
+__device__ __forceinline__ bool pool_append_all(WavePool& wp, uint64_t (&keys)[N], int lane) {
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) cnt += keys[j] != 0ull;
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint64_t m = __ballot((cnt >> b) & 1);
+    pre += lanes_below(m) << b;
+    tot += __popcll(m) << b;
+  }
+  if (tot == 0) return true;
+  if (wp.count + tot > kWavePool) {
+    pool_compact(wp, lane);
+    cnt = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      if (wp.have_bar && keys[j] <= wp.bar) keys[j] = 0ull;
+      cnt += keys[j] != 0ull;
+    }
+    pre = 0;
+    tot = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint64_t m = __ballot((cnt >> b) & 1);
+      pre += lanes_below(m) << b;
+      tot += __popcll(m) << b;
+    }
+    if (wp.count + tot > kWavePool) return false;
+  }
+  int pos = wp.count + pre;
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    if (keys[j] != 0ull) wp.keys[pos++] = keys[j];
+  wp.count += tot;
+  return true;
+}
+
+// One unit's statistics pass over a wave's registers: exp2 against the
+// running max (or the unit's first chunk max), lane and chunk maxima on the
+// side.  With ROLL each chunk's registers are refilled with the same chunk of
+// the next unit as soon as they have been used, so a unit's loads are always
+// in flight behind the current unit's arithmetic.
+struct PassOut {
+  float acc, lm, mref, nb;
+};
+
+template <int DT, bool VEC, bool ROLL>
+__device__ __forceinline__ PassOut unit_pass(uint4 (&raw)[kChunks], float (&cm)[kChunks],
+                                             float m_l, const char* next_rowp, int64_t next_base,
+                                             bool next_interior, int V, int lane) {
+  using E = Elem<DT>;
+  constexpr int kPer = E::kPer;
+  PassOut o;
+  float c0 = E::get(raw[0], 0);
+#pragma unroll
+  for (int j = 1; j < kPer; ++j) c0 = fmaxf(c0, E::get(raw[0], j));
+  o.mref = fmaxf(m_l, c0);
+  o.nb = -o.mref * kLog2e;
+  o.acc = 0.0f;
+  o.lm = kNegInf;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    // Empty asm statements only add data dependencies: chunk c is not
+    // unpacked before chunk c - 1 is summed, and its registers are refilled
+    // only after it is summed.  Without them the compiler hoists every
+    // unpack (or every refill) and keeps two units live at once.
+    if (c > 0)
+      asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w)
+                   : "v"(o.acc), "v"(o.lm));
+    float mc = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float xv = E::get(raw[c], j);
+      mc = fmaxf(mc, xv);
+      o.acc += __builtin_amdgcn_exp2f(__builtin_fmaf(xv, kLog2e, o.nb));
+    }
+    cm[c] = mc;
+    o.lm = fmaxf(o.lm, mc);
+    if (ROLL) {
+      int64_t nbase = next_base;
+      asm volatile("" : "+v"(nbase) : "v"(o.acc), "v"(o.lm));
+      raw[c] = load_lane_chunk<DT, VEC>(next_rowp, nbase, c, lane, V, next_interior);
+    }
+  }
+  return o;
+}
+
+// Four workgroups (16 waves) per CU: 128 VGPRs per lane.
+template <int DT, bool VEC, bool FUSED>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void reduce_kernel(
+    Params p) {
+  using E = Elem<DT>;
+  constexpr int kPer = E::kPer;
+  constexpr int kWaveElems = 64 * kChunks * kPer;
+  constexpr int kUnitElems = kWaves * kWaveElems;
+  __shared__ Smem sh;
+  extern __shared__ int prefix[];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int V = p.V, U = p.units;
+  const int total = build_prefix(p, prefix, sh);
+  const int64_t N = (int64_t)total * U;
+  const int64_t G = p.grid;
+  const int64_t x0 = (int64_t)blockIdx.x * N / G;
+  const int64_t x1 = ((int64_t)blockIdx.x + 1) * N / G;
+  if (x0 >= x1) return;
+
+  UnitPos cur = locate<DT>(p, prefix, x0);
+  int part_u0 = cur.u;
+  uint4 raw[kChunks];
+  {
+    const int64_t wb = (int64_t)cur.u * kUnitElems + (int64_t)w * kWaveElems;
+    const bool interior = wb + kWaveElems <= V;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)
+      raw[c] = load_lane_chunk<DT, VEC>(cur.rowp, wb, c, lane, V, interior);
+  }
+
+  // Per lane: running max m_l and the sum, relative to m_l, of exp over the
+  // lane's values except one occurrence of m_l (whose term is exactly 1 and
+  // is added back when the lanes are combined).
+  float m_l = kNegInf, s_l = 0.0f;
+  WavePool wp{&sh.pool[w][0], 0, false, 0ull};
+  int n_sel = p.id_counts[cur.s];
+  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
+  bool natural = p.K > 0 && n_sel == 0;
+
+  for (int64_t x = x0; x < x1; ++x) {
+    const bool has_next = x + 1 < x1;
+    UnitPos nxt = cur;
+    if (has_next) {
+      if (cur.u + 1 < U) {
+        nxt.u = cur.u + 1;
+      } else {
+        nxt = locate<DT>(p, prefix, x + 1);
+      }
+    }
+    const bool part_ends = !has_next || nxt.a != cur.a;
+    const int64_t wave_base = (int64_t)cur.u * kUnitElems + (int64_t)w * kWaveElems;
+    const int64_t next_base = (int64_t)nxt.u * kUnitElems + (int64_t)w * kWaveElems;
+    const bool next_interior = next_base + kWaveElems <= V;
+
+    float cm[kChunks];
+    const PassOut po =
+        has_next ? unit_pass<DT, VEC, true>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V, lane)
+                 : unit_pass<DT, VEC, false>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V, lane);
+    const float lm = po.lm;
+
+    // ---- fold the unit into the lane's running (max, sum)
+    {
+      float mr = po.mref, nbr = po.nb, acc = po.acc;
+      if (lm != kNegInf && !(acc < __builtin_huge_valf())) {
+        // The reference was -inf or far below this unit's maximum: redo the
+        // sum against the maximum, reading the lanes again.
+        mr = lm;
+        nbr = -lm * kLog2e;
+        acc = 0.0f;
+        for (int c = 0; c < kChunks; ++c) {
+          const uint4 r2 =
+              load_chunk<DT, VEC>(cur.rowp, wave_base + (int64_t)(c * 64 + lane) * kPer, V);
+#pragma unroll
+          for (int j = 0; j < kPer; ++j)
+            acc += __builtin_amdgcn_exp2f(__builtin_fmaf(E::get(r2, j), kLog2e, nbr));
+        }
+      }
+      const bool any = lm != kNegInf;
+      const bool up = lm > m_l;
+      const float e_lm = __builtin_amdgcn_exp2f(__builtin_fmaf(lm, kLog2e, nbr));
+      const float carry =
+          m_l != kNegInf ? (1.0f + s_l) * __builtin_amdgcn_exp2f((m_l - mr) * kLog2e) : 0.0f;
+      const float s_up = ((acc - e_lm) + carry) * __builtin_amdgcn_exp2f((mr - lm) * kLog2e);
+      const float s_keep = s_l + acc;  // lm <= m_l implies mr == m_l
+      s_l = any ? (up ? s_up : s_keep) : s_l;
+      m_l = any && up ? lm : m_l;
+    }
+
+    // ---- candidates for this wave's pool
+    if (natural) {
+      // Threshold: after the pool's first compaction, its 32nd-best key (a
+      // later lane equal to that key's value has a larger ID and cannot
+      // beat it, so values must be strictly larger); before it, the wave's
+      // 32nd-largest lane maximum (lane maxima are distinct lanes), or -inf
+      // when fewer than 32 lanes hold any of the vocabulary.
+      const bool strict = wp.have_bar;
+      float tau = kNegInf;
+      if (strict) {
+        tau = key_value(wp.bar);
+      } else {
+        const int64_t rem = (int64_t)V - wave_base;
+        const int vl = rem <= 0 ? 0 : (rem >= 64 * kPer ? 64 : (int)((rem + kPer - 1) / kPer));
+        if (vl >= kKeep) tau = key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, kKeep));
+      }
+      // Stage the offsets of hot chunks (maximum passes tau), then expand
+      // them 64 at a time, one reloaded chunk per lane.
+      if (__ballot(strict ? lm > tau : lm >= tau) != 0ull) {
+        int nh = 0;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          const int64_t first = wave_base + (int64_t)(c * 64 + lane) * kPer;
+          const bool hot = first < V && (strict ? cm[c] > tau : cm[c] >= tau);
+          const uint64_t m = __ballot(hot);
+          if (hot) sh.stage_off[w][nh + lanes_below(m)] = (int32_t)first;
+          nh += __popcll(m);
+        }
+        wave_sync();
+        for (int b = 0; b < nh; b += 64) {
+          const bool mine = b + lane < nh;
+          const int64_t first = mine ? (int64_t)sh.stage_off[w][b + lane] : 0;
+          const uint4 r = mine ? load_chunk<DT, VEC>(cur.rowp, first, V) : make_uint4(0u, 0u, 0u, 0u);
+          uint64_t keys[kPer];
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            const float xv = E::get(r, j);
+            const int64_t id = first + j;
+            const uint64_t k = make_key(xv, (uint32_t)id);
+            const bool pass = mine && id < V && (wp.have_bar ? k > wp.bar : xv >= tau);
+            keys[j] = pass ? k : 0ull;
+          }
+          if (!pool_append_all(wp, keys, lane)) {
+            // More qualifying lanes than a pool holds even after compaction
+            // (ties at the threshold): one key per lane per step.
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+              uint64_t k = keys[j];
+              if (wp.have_bar && k <= wp.bar) k = 0ull;
+              pool_append(wp, k, lane);
+            }
           }
         }
-        __syncthreads();
-        const int count = sh.count;
-        if (count > cap - kBlock) {
-          for (int q = count + tid; q < cap; q += kBlock) pool[q] = 0;
-          __syncthreads();
-          block_sort_desc(pool, cap);
-          thr = pool[Keff - 1];
-          __syncthreads();
-          if (tid == 0) sh.count = Keff;
-          __syncthreads();
+        wave_sync();
+      }
+      if (!wp.have_bar && wp.count >= kKeep) pool_compact(wp, lane);
+    }
+
+    if (part_ends) {
+      // ---- part record: combine lanes, then waves
+      {
+        const float M = wave_max(m_l, lane);
+        float term = 0.0f;
+        if (m_l != kNegInf) term = (1.0f + s_l) * __builtin_amdgcn_exp2f((m_l - M) * kLog2e);
+        const float S = wave_sum(term, lane);
+        if (lane == 0) {
+          sh.wm[w] = M;
+          sh.ws[w] = S;
         }
       }
+      if (natural) {
+        if (wp.count > 0) pool_compact(wp, lane);
+        if (lane < kKeep && lane >= wp.count) wp.keys[lane] = 0ull;
+      }
+      __syncthreads();
+      const int u1 = cur.u + 1;
+      PartRecord* rec = p.records + (int64_t)cur.row * U + part_u0;
+      if (w == 0) {
+        uint64_t top = 0ull;
+        int held = 0;
+        if (natural) {
+          top = lane < kKeep ? sh.pool[0][lane] : 0ull;
+#pragma unroll
+          for (int q = 1; q < kWaves; ++q)
+            top = merge_top32(top, lane < kKeep ? sh.pool[q][lane] : 0ull, lane);
+          held = __popcll(__ballot(lane < kKeep && top != 0ull));
+        }
+        if (lane < kKeep) rec->keys[lane] = top;
+        if (lane == 0) {
+          float M = sh.wm[0];
+          for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[i]);
+          float S = 0.0f;
+          if (M != kNegInf)
+            for (int i = 0; i < kWaves; ++i)
+              if (sh.wm[i] != kNegInf)
+                S += sh.ws[i] * __builtin_amdgcn_exp2f((sh.wm[i] - M) * kLog2e);
+          const int64_t lo = (int64_t)part_u0 * kUnitElems;
+          const int64_t hi = (int64_t)u1 * kUnitElems < V ? (int64_t)u1 * kUnitElems : V;
+          rec->m = M;
+          rec->s = S;
+          rec->n = held;
+          rec->flags = (hi - lo <= kKeep) ? kRecComplete : 0;
+        }
+        if (FUSED) {
+          // Publish the record, then count this part's units on the ticket.
+          __threadfence();
+          if (lane == 0)
+            sh.ticket_old = atomicAdd(&p.tickets[cur.row], (uint32_t)(u1 - part_u0));
+        }
+      }
+      __syncthreads();
+      if (FUSED && sh.ticket_old + (uint32_t)(u1 - part_u0) == (uint32_t)U) {
+        __threadfence();  // acquire the other parts' records
+        merge_row<DT>(p, sh, N, cur.row, cur.a, cur.s, n_sel, natural);
+        if (tid == 0) p.tickets[cur.row] = 0u;
+      }
+      // ---- next part
+      if (has_next) {
+        m_l = kNegInf;
+        s_l = 0.0f;
+        wp.count = 0;
+        wp.have_bar = false;
+        wp.bar = 0ull;
+        part_u0 = nxt.u;
+        n_sel = p.id_counts[nxt.s];
+        n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
+        natural = p.K > 0 && n_sel == 0;
+      }
     }
-    const int count = sh.count;
-    for (int q = count + tid; q < cap; q += kBlock) pool[q] = 0;
-    __syncthreads();
-    block_sort_desc(pool, cap);
-  }
-
-  for (int j = tid; j < K; j += kBlock) {
-    int32_t id = -1;
-    uint32_t bits = kNanBits;
-    if (j < Keff) {
-      const uint64_t f = pool[j];
-      id = (int32_t)key_id(f);
-      bits = __float_as_uint(unkey32((uint32_t)(f >> 32)));
-    }
-    out[2 + 2 * j] = id;
-    out[3 + 2 * j] = (int32_t)bits;
+    cur = nxt;
   }
 }
 
+// Separate merge launch (when the plan does not fuse): one workgroup per
+// physical row.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void merge_kernel(Params p) {
-  __shared__ MergeShared sh;
-  extern __shared__ uint64_t pool[];
+  __shared__ Smem sh;
+  extern __shared__ int prefix[];
+  const int total = build_prefix(p, prefix, sh);
   const int row = blockIdx.x;
-  int n_sel = 0;
-  if (!row_active(p, row, &n_sel)) return;
-  merge_row<DT>(p, row, n_sel, sh, pool);
+  const int s = row / p.T, t = row - s * p.T;
+  if (t >= slot_rows(p, s)) return;
+  int n_sel = p.id_counts[s];
+  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
+  merge_row<DT>(p, sh, (int64_t)total * p.units, row, prefix[s] + t, s, n_sel,
+                p.K > 0 && n_sel == 0);
 }
 
 __global__ void reset_kernel(uint32_t* t, int64_t n) {
@@ -701,21 +959,45 @@ __global__ void reset_kernel(uint32_t* t, int64_t n) {
 
 template <int DT, bool VEC>
 hipError_t launch_typed(const Params& p, hipStream_t st) {
-  const int64_t rows = (int64_t)p.capacity * p.T;
-  hipLaunchKernelGGL((segment_kernel<DT, VEC>), dim3((uint32_t)(rows * p.nseg)), dim3(kBlock),
-                     0, st, p);
+  const size_t lds = reduce_lds_bytes(p.capacity);
+  if (p.fused) {
+    hipLaunchKernelGGL((reduce_kernel<DT, VEC, true>), dim3((uint32_t)p.grid), dim3(kBlock), lds,
+                       st, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((reduce_kernel<DT, VEC, false>), dim3((uint32_t)p.grid), dim3(kBlock), lds,
+                     st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)rows), dim3(kBlock),
-                     (size_t)p.merge_pool * sizeof(uint64_t), st, p);
+  const int64_t rows = (int64_t)p.capacity * p.T;
+  hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)rows), dim3(kBlock), lds, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int launch_reduce(const Params& p, int dtype, bool vector_rows, int merge_mode,
-                  void* stream) {
-  (void)merge_mode;
+size_t reduce_lds_bytes(int capacity) { return (size_t)(capacity + 1) * sizeof(int); }
+
+int reduce_occupancy(int dtype, bool vector_rows, int capacity) {
+  // Sized for the default (separate merge) kernel; the fused variant is
+  // launched with the same grid.
+  int n = 0;
+  const size_t lds = reduce_lds_bytes(capacity);
+  hipError_t e;
+  if (dtype == 1)
+    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                          &n, reduce_kernel<1, true, false>, kBlock, lds)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                          &n, reduce_kernel<1, false, false>, kBlock, lds);
+  else
+    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                          &n, reduce_kernel<0, true, false>, kBlock, lds)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                          &n, reduce_kernel<0, false, false>, kBlock, lds);
+  return e == hipSuccess ? n : 0;
+}
+
+int launch_reduce(const Params& p, int dtype, bool vector_rows, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dtype == 1)

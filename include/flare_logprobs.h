@@ -69,7 +69,8 @@ enum flare_status {
 /*
  * A plan is a host value filled by flare_logprobs_plan.  It owns nothing and
  * needs no destruction.  Fields after `device` are chosen by the library and
- * are informational except workspace_bytes, which the caller must allocate.
+ * are informational, except workspace_bytes, which the caller must allocate,
+ * and `fused`, which the caller may set to 0 or 1 before flare_logprobs_run.
  */
 typedef struct flare_logprobs_plan {
   uint32_t abi_version;
@@ -80,14 +81,18 @@ typedef struct flare_logprobs_plan {
   int32_t dtype;         /* enum flare_dtype */
   int32_t K;             /* natural alternatives, 0..20 */
   int32_t device;        /* HIP device ordinal, or -1 for a host-only plan */
-  int32_t seg_elems;     /* vocabulary lanes per segment (one workgroup) */
-  int32_t nseg;          /* segments per row */
+  int32_t unit_elems;    /* vocabulary lanes one workgroup holds at a time */
+  int32_t units;         /* units per row, ceil(V / unit_elems), at most 64 */
   int32_t block;         /* threads per workgroup */
+  int32_t grid;          /* workgroups of the persistent launch */
   int32_t vector_rows;   /* 1 if V_pad * element size is a multiple of 16 */
   int32_t cu_count;      /* compute units of `device` (256 if host-only) */
-  int32_t merge_mode;    /* 0: separate merge launch, 1: fused last-arrival merge */
+  int32_t fused;         /* 0: a second launch merges every row (default);
+                            1: the workgroup that finishes a row merges it
+                            in the same launch, behind agent-scope fences */
+  int32_t reserved0;
   uint64_t workspace_bytes; /* bytes of device workspace the caller provides */
-  uint64_t record_offset;   /* per-(row, segment) records */
+  uint64_t record_offset;   /* per-(row, unit) part records */
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
   uint64_t ticket_offset;   /* uint32[capacity * T]: arrival counters */
   uint32_t reserved[8];
@@ -95,9 +100,11 @@ typedef struct flare_logprobs_plan {
 
 /*
  * Validate a geometry and size a workspace.  Runs on the host only; with
- * device >= 0 it reads that device's attributes (CU count, architecture).
- *   capacity >= 1, T >= 1, V >= 1, V_pad >= V, dtype a flare_dtype,
- *   0 <= K <= 20.
+ * device >= 0 it reads that device's attributes (CU count, architecture,
+ * resident workgroups per CU) to size the persistent launch.
+ *   1 <= capacity <= 8192, T >= 1, V >= 1, V_pad >= V, dtype a flare_dtype,
+ *   0 <= K <= 20; V at most 64 units (1,048,576 bf16 or 524,288 FP32 lanes),
+ *   else FLARE_ERR_UNSUPPORTED_SIZE.
  * Returns FLARE_OK and fills *plan, or an error and leaves *plan zeroed.
  */
 int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T,

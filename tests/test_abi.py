@@ -50,8 +50,8 @@ def test_abi_version_and_status_strings(flp):
 
 
 def test_plan_struct_layout_matches_header(flp):
-    # 14 int32-sized fields, 4 uint64, 8 reserved uint32
-    assert ctypes.sizeof(flp.PlanStruct) == 14 * 4 + 4 * 8 + 8 * 4
+    # 16 int32-sized fields, 4 uint64, 8 reserved uint32
+    assert ctypes.sizeof(flp.PlanStruct) == 16 * 4 + 4 * 8 + 8 * 4
 
 
 def host_plan(flp, capacity=128, T=8, V=248320, V_pad=248320, dtype=1, K=20):
@@ -63,13 +63,13 @@ def host_plan(flp, capacity=128, T=8, V=248320, V_pad=248320, dtype=1, K=20):
 def test_plan_host_only_geometry(flp):
     rc, p = host_plan(flp)
     assert rc == 0
-    assert p.nseg == 16 and p.seg_elems == 16384 and p.block == 256 and p.vector_rows == 1
-    assert p.cu_count == 256 and p.abi_version == 1
+    assert p.units == 16 and p.unit_elems == 16384 and p.block == 256 and p.vector_rows == 1
+    assert p.cu_count == 256 and p.abi_version == 1 and p.grid == 1024 and p.fused == 0
     rows = 128 * 8
     assert p.lse_offset >= rows * 16 * 272 and p.ticket_offset >= p.lse_offset + 4 * rows
     assert p.workspace_bytes >= p.ticket_offset + 4 * rows
     rc, p = host_plan(flp, capacity=1024, T=4, V=262144, V_pad=262144, dtype=0)
-    assert rc == 0 and p.nseg == 32 and p.seg_elems == 8192
+    assert rc == 0 and p.units == 32 and p.unit_elems == 8192
     rc, p = host_plan(flp, V=37, V_pad=41)
     assert rc == 0 and p.vector_rows == 0
 
@@ -77,7 +77,7 @@ def test_plan_host_only_geometry(flp):
 @pytest.mark.parametrize("kw,status", [
     (dict(capacity=0), 1), (dict(T=0), 1), (dict(V=0), 1), (dict(V_pad=100, V=200), 1),
     (dict(K=-1), 1), (dict(K=21), 1), (dict(dtype=2), 2), (dict(dtype=-1), 2),
-    (dict(V=16384 * 64 + 1, V_pad=16384 * 64 + 1), 6),
+    (dict(V=16384 * 64 + 1, V_pad=16384 * 64 + 1), 6), (dict(capacity=8193, T=1), 1),
 ])
 def test_plan_rejects(flp, kw, status):
     rc, p = host_plan(flp, **kw)
@@ -125,6 +125,15 @@ def test_run_rejects_bad_dtype_and_stale_plan(flp):
     assert run_status(flp, plan) == 3
     assert flp.lib().flare_logprobs_run(None, FAKE, 1, 1, 1, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
                                         0, FAKE, FAKE, None) == 1
+
+
+def test_run_rejects_corrupt_plan(flp):
+    rc, plan = host_plan(flp)
+    plan.fused = 2
+    assert run_status(flp, plan) == 3
+    rc, plan = host_plan(flp)
+    plan.grid = 0
+    assert run_status(flp, plan) == 3
 
 
 def test_run_rejects_misaligned_workspace(flp):

@@ -260,6 +260,22 @@ def test_unaligned_base_pointer(oracle_handle):
     H.compare_words(got, ref, "unaligned")
 
 
+@pytest.mark.parametrize("name", ["C3", "C4", "C5"])
+def test_fused_merge_mode(oracle_handle, name):
+    """The in-launch merge (plan.fused = 1) gives the same frame as the
+    oracle and as the separate merge launch."""
+    spec = synth.CONFIGS[name].with_(capacity={"C3": 6, "C4": 10, "C5": 3}[name])
+    announce(f"fused merge mode {name} cap={spec.capacity}")
+    w = synth.make(spec)
+    d = H.to_device(w)
+    got_f, lse_f = H.run_gpu(w, d, plan=H.make_plan(spec, fused=True))
+    got_s, lse_s = H.run_gpu(w, d, plan=H.make_plan(spec, fused=False))
+    ref = H.oracle_frame(oracle_handle, w)
+    H.compare_words(got_f, ref, f"{name} fused")
+    assert np.array_equal(got_f, got_s)
+    assert np.array_equal(lse_f.view(np.int32), lse_s.view(np.int32))
+
+
 # -------------------------------------------------- repeatability and graphs
 def test_repeatable_bit_identical():
     spec = synth.CONFIGS["C3"].with_(capacity=16)
