@@ -37,6 +37,9 @@ def parse():
                     help="budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--check-rows", type=int, default=4,
                     help="oracle rows compared with the GPU output before timing")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run a plain elementwise FP32 copy of this many MiB "
+                         "three times (scales HBM byte counters; 0 disables it)")
     return ap.parse_args()
 
 
@@ -146,6 +149,16 @@ def main():
         cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
                "sample": f"first {n} active rows of {spec.name} (of {active}), "
                          f"single-threaded oracle, {dt:.1f} s"}
+
+    if args.copy_mib > 0:
+        # A kernel of known traffic (reads and writes copy_mib MiB each) so that
+        # profiler byte counters can be converted into bytes.
+        src = torch.ones(args.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     res = {
         "metric": "logprob rows/s and achieved HBM GB/s (% of peak) at V=248,320, T=8, 128 slots",

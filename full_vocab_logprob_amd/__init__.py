@@ -6,12 +6,12 @@ supplies device memory and the current stream.  There is no fallback: if the
 shared library is missing the import of a binding function raises.
 
     plan = Plan(capacity, T, V, V_pad, dtype=torch.bfloat16, K=20)
-    ws = plan.workspace()                                # zeroed once
+    ws = plan.workspace()
     plan.run(logits, tokens, emitted_counts, requested, id_counts, ids, out, ws)
 
 The functions ``flare_logprobs_plan``, ``flare_logprobs_run``,
-``flare_logprobs_workspace_reset``, ``flare_status_string`` and
-``flare_logprobs_abi_version`` mirror the C entry points one to one.
+``flare_status_string`` and ``flare_logprobs_abi_version`` mirror the C entry
+points one to one.
 """
 from __future__ import annotations
 
@@ -44,9 +44,9 @@ class PlanStruct(ctypes.Structure):
                 ("unit_elems", ctypes.c_int32), ("units", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("vector_rows", ctypes.c_int32), ("cu_count", ctypes.c_int32),
-                ("fused", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("ranges", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
-                ("lse_offset", ctypes.c_uint64), ("ticket_offset", ctypes.c_uint64),
+                ("lse_offset", ctypes.c_uint64), ("reserved1", ctypes.c_uint64),
                 ("reserved", ctypes.c_uint32 * 8)]
 
 
@@ -76,9 +76,6 @@ def lib() -> ctypes.CDLL:
                                          c.c_int32, c.c_int32, c.c_void_p, c.c_void_p,
                                          c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32,
                                          c.c_void_p, c.c_void_p, c.c_void_p]
-        L.flare_logprobs_workspace_reset.restype = c.c_int
-        L.flare_logprobs_workspace_reset.argtypes = [c.POINTER(PlanStruct), c.c_void_p,
-                                                     c.c_void_p]
         L.flare_status_string.restype = c.c_char_p
         L.flare_status_string.argtypes = [c.c_int]
         L.flare_logprobs_abi_version.restype = c.c_uint32
@@ -141,13 +138,6 @@ def flare_logprobs_run(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad
         raise FlareError(rc, "flare_logprobs_run")
 
 
-def flare_logprobs_workspace_reset(plan: PlanStruct, workspace, stream=None) -> None:
-    rc = lib().flare_logprobs_workspace_reset(ctypes.byref(plan), _ptr(workspace),
-                                              _stream(stream))
-    if rc != 0:
-        raise FlareError(rc, "flare_logprobs_workspace_reset")
-
-
 def _check(t: torch.Tensor, name: str, dtype, numel: int, device) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -160,14 +150,12 @@ class Plan:
     """A validated geometry plus the shapes its tensors must have."""
 
     def __init__(self, capacity: int, T: int, V: int, V_pad: int | None = None,
-                 dtype=torch.bfloat16, K: int = 20, device: int | None = None,
-                 fused: bool = False):
+                 dtype=torch.bfloat16, K: int = 20, device: int | None = None):
         if device is None:
             device = torch.cuda.current_device()
         self.torch_dtype = torch.bfloat16 if dtype_code(dtype) == DTYPE_BF16 else torch.float32
         self.V_pad = V if V_pad is None else V_pad
         self.raw = flare_logprobs_plan(capacity, T, V, self.V_pad, dtype, K, device)
-        self.raw.fused = 1 if fused else 0
         self.capacity, self.T, self.V, self.K, self.device_index = capacity, T, V, K, device
 
     @property
@@ -179,7 +167,7 @@ class Plan:
         return int(self.raw.workspace_bytes)
 
     def workspace(self) -> torch.Tensor:
-        return torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
 
     def lse(self, workspace: torch.Tensor) -> torch.Tensor:
         """Diagnostic view: the normalization L of every reduced row."""

@@ -49,6 +49,7 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   const int unit = flp::unit_elems(dtype);
   const int64_t units = ((int64_t)V + unit - 1) / unit;
   if (units > flp::kMaxUnits) return FLARE_ERR_UNSUPPORTED_SIZE;
+  if (rows * units > (int64_t)0x7FFFFFFF) return FLARE_ERR_UNSUPPORTED_SIZE;
   const bool vec = ((int64_t)V_pad * flp::elem_bytes(dtype)) % 16 == 0;
 
   int32_t cus = 256, per_cu = 4;
@@ -81,14 +82,12 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   plan->grid = cus * per_cu;
   plan->vector_rows = vec ? 1 : 0;
   plan->cu_count = cus;
-  plan->fused = 0;
+  plan->ranges = plan->grid;
   uint64_t off = 0;
   plan->record_offset = off;
   off = align_up(off + (uint64_t)rows * units * sizeof(flp::PartRecord), kAlign);
   plan->lse_offset = off;
   off = align_up(off + (uint64_t)rows * sizeof(float), kAlign);
-  plan->ticket_offset = off;
-  off = align_up(off + (uint64_t)rows * sizeof(uint32_t), kAlign);
   plan->workspace_bytes = off;
   return FLARE_OK;
 }
@@ -107,7 +106,7 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, in
     return FLARE_ERR_PLAN_MISMATCH;
   if (rows != (int64_t)plan->capacity * plan->T) return FLARE_ERR_PLAN_MISMATCH;
   if (plan->grid < 1 || plan->units < 1 || plan->units > flp::kMaxUnits ||
-      (plan->fused != 0 && plan->fused != 1))
+      plan->ranges != plan->grid || plan->block != flp::kBlock)
     return FLARE_ERR_PLAN_MISMATCH;
   if (((uintptr_t)workspace & 15u) != 0) return FLARE_ERR_INVALID_ARGUMENT;
 
@@ -122,28 +121,17 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, in
   p.out = out;
   p.records = (flp::PartRecord*)(ws + plan->record_offset);
   p.lse = (float*)(ws + plan->lse_offset);
-  p.tickets = (uint32_t*)(ws + plan->ticket_offset);
   p.V_pad = V_pad;
   p.capacity = plan->capacity;
   p.T = plan->T;
   p.V = V;
   p.K = K;
   p.units = plan->units;
-  p.grid = plan->grid;
-  p.fused = plan->fused;
+  p.workers = plan->ranges;
 
   const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
   const int e = flp::launch_reduce(p, dtype, vec, hip_stream);
   return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
-}
-
-int flare_logprobs_workspace_reset(const flare_logprobs_plan_t* plan, void* workspace,
-                                   void* hip_stream) {
-  if (!plan || !workspace) return FLARE_ERR_INVALID_ARGUMENT;
-  if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
-  const int64_t rows = (int64_t)plan->capacity * plan->T;
-  uint32_t* t = (uint32_t*)((char*)workspace + plan->ticket_offset);
-  return flp::launch_reset(t, rows, hip_stream) == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -5,17 +5,18 @@
 
 namespace flp {
 
-constexpr int kBlock = 256;        // threads per workgroup (4 wave64s)
-constexpr int kWaves = kBlock / 64;
-constexpr int kChunks = 8;         // 16-byte chunks each thread holds per unit
-constexpr int kKeep = 32;          // raw keys a part keeps
-constexpr int kMaxUnits = 64;      // units per row (one merge lane per unit)
-constexpr int kMaxCapacity = 8192; // slots whose active-row prefix fits in LDS
+constexpr int kChunks = 8;          // 16-byte chunks each thread holds per unit
+constexpr int kUnitThreads = 256;   // threads (4 wave64s) sharing one unit
+constexpr int kBlock = kUnitThreads; // reduction workgroup
+constexpr int kMergeBlock = 256;    // merge workgroup
+constexpr int kKeep = 32;           // raw keys a part keeps
+constexpr int kMaxUnits = 64;       // units per row (one merge lane per unit)
+constexpr int kMaxCapacity = 8192;  // slots whose active-row prefix fits in LDS
 
 // Vocabulary lanes per 16-byte chunk, and per unit: the lanes one workgroup
 // holds in registers at a time (16,384 bf16 or 8,192 FP32 lanes, 32 KiB).
 constexpr int elems_per_chunk(int dtype) { return dtype == 1 ? 8 : 4; }
-constexpr int unit_elems(int dtype) { return kBlock * kChunks * elems_per_chunk(dtype); }
+constexpr int unit_elems(int dtype) { return kUnitThreads * kChunks * elems_per_chunk(dtype); }
 constexpr int elem_bytes(int dtype) { return dtype == 1 ? 2 : 4; }
 
 // One part's contribution to a row: a part is the run of consecutive units
@@ -42,22 +43,19 @@ struct Params {
   int32_t* out;
   PartRecord* records;
   float* lse;
-  uint32_t* tickets;
   int64_t V_pad;
   int32_t capacity;
   int32_t T;
   int32_t V;
   int32_t K;
-  int32_t units;   // units per row
-  int32_t grid;    // workgroups of the persistent launch
-  int32_t fused;   // 1: the last part of a row merges it in the same launch
+  int32_t units;    // units per row
+  int32_t workers;  // workgroups of the persistent launch (one unit range each)
 };
 
-// Launchers implemented in flp_kernels.hip; return a hipError_t as int.
+// Launcher implemented in flp_kernels.hip; returns a hipError_t as int.
 int launch_reduce(const Params& p, int dtype, bool vector_rows, void* stream);
-int launch_reset(uint32_t* tickets, int64_t n, void* stream);
-// Resident workgroups per CU of the reduction kernel (0 on error).
+// Resident reduction workgroups per CU (0 on error).
 int reduce_occupancy(int dtype, bool vector_rows, int capacity);
-size_t reduce_lds_bytes(int capacity);
+size_t prefix_lds_bytes(int capacity);
 
 }  // namespace flp

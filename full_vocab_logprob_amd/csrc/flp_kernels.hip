@@ -7,27 +7,33 @@
 // the caller's selected IDs in caller order.
 //
 // How.  Every logit is read from HBM once; nothing here is a contraction, so
-// there is no MFMA.  One persistent launch of `grid` workgroups.  The work is
-// the concatenation, over active rows, of each row's units (16,384 bf16 or
-// 8,192 FP32 lanes, 32 KiB); workgroup g owns the contiguous unit range
-// [g N / grid, (g + 1) N / grid), so every workgroup streams the same number
-// of bytes and a range may cross rows.  The units of one row inside one range
-// form a part.
+// there is no MFMA.  Two launches.
+//
+// reduce_kernel: a persistent launch of `grid` 256-thread workgroups (four
+// per CU).  The work is the concatenation, over active rows, of each row's
+// units (16,384 bf16 or 8,192 FP32 lanes, 32 KiB); workgroup g owns the
+// contiguous unit range [g N / grid, (g + 1) N / grid), so every workgroup
+// streams the same number of bytes and a range may cross rows.  The units of
+// one row inside one range form a part.
 //   Per unit, each thread holds 8 x 16-byte chunks (coalesced dwordx4 loads)
-//   in VGPRs.  Each wave keeps a running (max, sum of exp2) for the part.
-//   Natural-mode rows also feed an LDS candidate pool: a unit's threshold is
-//   the wave's 32nd-largest lane maximum (ballot radix select) until the
-//   pool's first compaction, then the part's running 32nd-best key; only
-//   16-byte chunks whose maximum passes it are staged to LDS and expanded
-//   into 64-bit raw keys (value, then smaller ID).  Compaction sorts 64-key
-//   lists in registers and rank-merges them (no block-wide sort).
-//   At the end of a part the workgroup writes a part record (m, s, best 32
-//   raw keys), publishes it with an agent-scope release fence and adds the
-//   part's unit count to the row's ticket; the workgroup that completes the
-//   ticket merges the row: L from the parts in part order, the chosen and
-//   selected gathers, and the natural top K re-keyed by the reported value
-//   fl32(x - L), with an exactness guard that rescans a part when the raw
-//   order it kept could differ from the final order.
+//   in VGPRs and refills each chunk with the next unit as soon as it is
+//   summed.  Each wave keeps a running (max, sum of exp2) for the part.
+//   Natural-mode rows also feed a per-wave LDS pool of 64-bit raw keys
+//   (value, then smaller ID) that always holds the wave's best 32: chunks
+//   whose maximum passes the admission bar are copied to an LDS stash as they
+//   stream by and expanded one lane per element afterwards.  A part's first
+//   unit sets the bar at the smallest of the waves' k-th largest lane maxima
+//   (32 lanes in all reach it; ballot radix select); later the bar is the
+//   largest of that value bar, the wave's own 32nd-best key and the smallest
+//   of the four waves' published 8th-best keys.  Compaction sorts 64-key
+//   lists in registers.  At the end of a part wave 0 merges the four waves'
+//   sorted best 32 into the part record (m, s, best 32 raw keys).
+//
+// merge_kernel: one workgroup per row merges the row's part records: L from
+// the parts in part order, the chosen and selected gathers, and the natural
+// top K re-keyed by the reported value fl32(x - L), with an exactness guard
+// that rescans a part when the raw order it kept could differ from the final
+// order.
 //
 // The pages' own scheme ranks normalized values in a second pass over the
 // vocabulary; ranking raw values and re-keying only the survivors is what
@@ -312,6 +318,7 @@ struct WavePool {
   int count;
   bool have_bar;
   uint64_t bar;    // 32nd-best key after the last compaction
+  uint64_t b8;     // 8th-best key after the last compaction (0: fewer than 8)
 };
 
 __device__ __forceinline__ void pool_compact(WavePool& wp, int lane) {
@@ -326,6 +333,7 @@ __device__ __forceinline__ void pool_compact(WavePool& wp, int lane) {
   wave_sync();
   if (lane < kKeep) wp.keys[lane] = a;
   wave_sync();
+  wp.b8 = wp.count >= 8 ? readlane64(a, 7) : 0ull;
   if (wp.count >= kKeep) {
     wp.have_bar = true;
     wp.bar = readlane64(a, kKeep - 1);
@@ -349,47 +357,21 @@ __device__ __forceinline__ void pool_append(WavePool& wp, uint64_t k, int lane) 
   wp.count += n;
 }
 
-// ------------------------------------------------------------ shared state
-struct Smem {
-  uint64_t pool[kWaves][kWavePool];  // per-wave pools; a 256-key batch in merges
-  int32_t stage_off[kWaves][kChunks * 64];  // first lane of each hot chunk
-  float wm[kWaves];
-  float ws[kWaves];
-  uint32_t ticket_old;
-  float L;
-  int n_parts;
-  int unsafe_any;
-  int16_t part_u0[kMaxUnits + 1];
-  int scan[kWaves];
-};
-
-// Sort each wave's 64 keys of batch[0, 256), then fold them into wave 0's
-// running best-32 `top` (lanes 0..31).  All threads; two barriers.
-__device__ __forceinline__ void fold_batch(uint64_t* batch, uint64_t& top, int lane, int w) {
-  __syncthreads();
-  uint64_t v = sort64_desc(batch[w * 64 + lane], lane);
-  batch[w * 64 + lane] = v;
-  __syncthreads();
-  if (w == 0) {
-    top = merge_top32(top, v, lane);
-#pragma unroll
-    for (int q = 1; q < kWaves; ++q) top = merge_top32(top, batch[q * 64 + lane], lane);
-  }
-  __syncthreads();
-}
-
-// ------------------------------------------------------------- row mapping
+// ------------------------------------------------------------ row mapping
 __device__ __forceinline__ int slot_rows(const Params& p, int s) {
   if (p.requested[s] == 0) return 0;
   const int e = p.emitted[s];
   return e < 0 ? 0 : (e > p.T ? p.T : e);
 }
 
-// prefix[s] = active rows of slots before s; prefix[capacity] = total.
-__device__ int build_prefix(const Params& p, int* prefix, Smem& sh) {
+// prefix[s] = active rows of slots before s; prefix[capacity] = total.  All
+// NW waves of the workgroup take part; `scan` is NW ints of LDS.
+template <int NW>
+__device__ int build_prefix(const Params& p, int* prefix, int* scan) {
+  constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int cap = p.capacity;
-  const int per = (cap + kBlock - 1) / kBlock;
+  const int per = (cap + NT - 1) / NT;
   const int s0 = tid * per;
   const int s1 = s0 + per < cap ? s0 + per : cap;
   int local = 0;
@@ -398,20 +380,20 @@ __device__ int build_prefix(const Params& p, int* prefix, Smem& sh) {
     prefix[s] = c;
     local += c;
   }
-  // exclusive scan of `local` over the block (values can exceed 15 here)
+  // exclusive scan of `local` over the block
   int incl = local;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int t = __shfl_up(incl, o, 64);
     if (lane >= o) incl += t;
   }
-  if (lane == 63) sh.scan[w] = incl;
+  if (lane == 63) scan[w] = incl;
   __syncthreads();
   int run = incl - local, total = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    run += i < w ? sh.scan[i] : 0;
-    total += sh.scan[i];
+  for (int i = 0; i < NW; ++i) {
+    run += i < w ? scan[i] : 0;
+    total += scan[i];
   }
   for (int s = s0; s < s1; ++s) {
     const int c = prefix[s];
@@ -433,13 +415,39 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
   return lo;
 }
 
-// Is global unit x the first unit of some workgroup's range?
-__device__ __forceinline__ bool range_start(int64_t x, int64_t N, int64_t G) {
-  const int64_t g = (x * G + N - 1) / N;
-  return g <= G && (g * N) / G == x;
+// Is global unit x the first unit of some workgroup's range (W ranges)?
+__device__ __forceinline__ bool range_start(int64_t x, int64_t N, int64_t W) {
+  const int64_t k = (x * W + N - 1) / N;
+  return k <= W && (k * N) / W == x;
 }
 
 // ==================================================================== merge
+constexpr int kMergeWaves = kMergeBlock / 64;
+
+struct MergeSmem {
+  uint64_t batch[kMergeBlock + 2];  // 256 keys, then the unsafe-part mask and F_K
+  float L;
+  int n_parts;
+  int unsafe_any;
+  int16_t part_u0[kMaxUnits + 1];
+  int scan[kMergeWaves];
+};
+
+// Sort each wave's 64 keys of batch[0, 256), then fold them into wave 0's
+// running best-32 `top` (lanes 0..31).  All threads; three barriers.
+__device__ __forceinline__ void fold_batch(uint64_t* batch, uint64_t& top, int lane, int w) {
+  __syncthreads();
+  uint64_t v = sort64_desc(batch[w * 64 + lane], lane);
+  batch[w * 64 + lane] = v;
+  __syncthreads();
+  if (w == 0) {
+    top = merge_top32(top, v, lane);
+#pragma unroll
+    for (int q = 1; q < kMergeWaves; ++q) top = merge_top32(top, batch[q * 64 + lane], lane);
+  }
+  __syncthreads();
+}
+
 // Merge row `row` (active row a, slot s): L from its parts in part order,
 // the chosen and selected gathers, and the natural top K.
 //
@@ -453,10 +461,10 @@ __device__ __forceinline__ bool range_start(int64_t x, int64_t N, int64_t G) {
 // fails either test is rescanned lane by lane with final keys; F_K over a
 // subset never exceeds the true K-th key, so the test stays sound.
 template <int DT>
-__device__ void merge_row(const Params& p, Smem& sh, int64_t N, int row, int a, int s,
+__device__ void merge_row(const Params& p, MergeSmem& sh, int64_t N, int row, int a, int s,
                           int n_sel, bool natural) {
   using E = Elem<DT>;
-  constexpr int kUnitElems = kBlock * kChunks * E::kPer;
+  constexpr int kUnitElems = kUnitThreads * kChunks * E::kPer;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int V = p.V, U = p.units;
   const PartRecord* rec = p.records + (int64_t)row * U;
@@ -467,7 +475,7 @@ __device__ void merge_row(const Params& p, Smem& sh, int64_t N, int row, int a, 
 
   // ---- the row's parts (one lane per unit) and L (one lane per part)
   if (w == 0) {
-    const bool start = lane < U && (lane == 0 || range_start((int64_t)a * U + lane, N, p.grid));
+    const bool start = lane < U && (lane == 0 || range_start((int64_t)a * U + lane, N, p.workers));
     const uint64_t m = __ballot(start);
     const int np = __popcll(m);
     if (start) sh.part_u0[lanes_below(m)] = (int16_t)lane;
@@ -512,10 +520,10 @@ __device__ void merge_row(const Params& p, Smem& sh, int64_t N, int row, int a, 
   if (natural) {
     const int K = p.K;
     const int Keff = K < V ? K : V;
-    uint64_t* batch = &sh.pool[0][0];
+    uint64_t* batch = sh.batch;
     uint64_t top = 0ull;  // wave 0: best 32 final keys so far, lanes 0..31
     // ---- kept candidates, 8 parts (256 keys) per batch, re-keyed by F
-    for (int pb = 0; pb < np; pb += kBlock / kKeep) {
+    for (int pb = 0; pb < np; pb += kMergeBlock / kKeep) {
       const int part = pb + (tid >> 5), k = tid & 31;
       uint64_t f = 0ull;
       if (part < np) {
@@ -543,18 +551,18 @@ __device__ void merge_row(const Params& p, Smem& sh, int64_t N, int row, int a, 
       const uint64_t m = __ballot(bad);
       if (lane == 0) {
         sh.unsafe_any = m != 0ull;
-        batch[256] = m;  // unsafe parts (slot past the batch)
-        batch[257] = FK;
+        batch[kMergeBlock] = m;
+        batch[kMergeBlock + 1] = FK;
       }
     }
     __syncthreads();
     if (sh.unsafe_any) {
       // Rebuild from the safe parts' candidates plus every lane of each
       // unsafe part whose final key reaches FK.
-      const uint64_t unsafe = batch[256];
-      const uint64_t FK = batch[257];
+      const uint64_t unsafe = batch[kMergeBlock];
+      const uint64_t FK = batch[kMergeBlock + 1];
       top = 0ull;
-      for (int pb = 0; pb < np; pb += kBlock / kKeep) {
+      for (int pb = 0; pb < np; pb += kMergeBlock / kKeep) {
         const int part = pb + (tid >> 5), k = tid & 31;
         uint64_t f = 0ull;
         if (part < np && !((unsafe >> part) & 1ull)) {
@@ -569,7 +577,7 @@ __device__ void merge_row(const Params& p, Smem& sh, int64_t N, int row, int a, 
         const int64_t lo = (int64_t)sh.part_u0[part] * kUnitElems;
         int64_t hi = (int64_t)sh.part_u0[part + 1] * kUnitElems;
         hi = hi < V ? hi : V;
-        for (int64_t b = lo; b < hi; b += kBlock) {
+        for (int64_t b = lo; b < hi; b += kMergeBlock) {
           const int64_t i = b + tid;
           uint64_t f = 0ull;
           if (i < hi) {
@@ -591,10 +599,39 @@ __device__ void merge_row(const Params& p, Smem& sh, int64_t N, int row, int a, 
       *(int2*)(out + 2 + 2 * lane) = make_int2(id, (int32_t)bits);
     }
   }
-  __syncthreads();
+}
+
+// One workgroup per physical row; rows outside the committed prefix exit.
+template <int DT>
+__global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
+  __shared__ MergeSmem sh;
+  extern __shared__ int prefix[];
+  const int total = build_prefix<kMergeWaves>(p, prefix, sh.scan);
+  const int row = blockIdx.x;
+  const int s = row / p.T, t = row - s * p.T;
+  if (t >= slot_rows(p, s)) return;
+  int n_sel = p.id_counts[s];
+  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
+  merge_row<DT>(p, sh, (int64_t)total * p.units, row, prefix[s] + t, s, n_sel,
+                p.K > 0 && n_sel == 0);
 }
 
 // ================================================================== reduce
+constexpr int kWaves = kBlock / 64;  // 4 waves share each unit
+constexpr int kStash = 64;           // hot chunks a wave can stash per unit
+constexpr int kCompactAt = 56;       // pool size that triggers a compaction
+
+struct ReduceSmem {
+  uint64_t pool[kWaves][kWavePool];  // per-wave candidate pools
+  uint4 stash[kWaves][kStash];       // hot chunks of the unit being reduced
+  int16_t stash_off[kWaves][kStash]; // their chunk index c * 64 + lane
+  uint64_t qbar[kWaves];             // each wave's 8th-best key of its part (0: none)
+  float tw[kWaves];                  // first-unit thresholds of the waves
+  float wm[kWaves];                  // a part's per-wave max and scaled sum
+  float ws[kWaves];
+  int scan[kWaves];
+};
+
 // Where a unit sits: active row a, unit u of that row, slot s, logit row.
 struct UnitPos {
   int a, u, s, row;
@@ -602,80 +639,75 @@ struct UnitPos {
 };
 
 template <int DT>
-__device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, int64_t x) {
+__device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, int x) {
   UnitPos q;
-  q.a = (int)(x / p.units);
-  q.u = (int)(x - (int64_t)q.a * p.units);
-  q.s = slot_of(prefix, p.capacity, q.a);
-  q.row = q.s * p.T + (q.a - prefix[q.s]);
+  q.a = x / p.units;
+  q.u = x - q.a * p.units;
+  q.s = __builtin_amdgcn_readfirstlane(slot_of(prefix, p.capacity, q.a));
+  q.row = __builtin_amdgcn_readfirstlane(q.s * p.T + (q.a - prefix[q.s]));
   q.rowp = (const char*)p.logits + (int64_t)q.row * p.V_pad * Elem<DT>::kBytes;
   return q;
 }
 
-// Chunk c of this lane in the wave's slice starting at wave_base.
+// Chunk c of this lane in the wave's slice starting at wave_base; loff is
+// the chunk's byte offset in the slice, (c * 64 + lane) * 16.  Row pointer
+// and slice start are wave-uniform, so the interior load is an SGPR base plus
+// a 32-bit lane offset.
 template <int DT, bool VEC>
-__device__ __forceinline__ uint4 load_lane_chunk(const char* rowp, int64_t wave_base, int c,
-                                                 int lane, int V, bool interior) {
+__device__ __forceinline__ uint4 load_lane_chunk(const char* rowp, int64_t wave_base, uint32_t loff,
+                                                 int c, int lane, int V, bool interior) {
   using E = Elem<DT>;
-  const int64_t first = wave_base + (int64_t)(c * 64 + lane) * E::kPer;
-  if (VEC && interior) return *(const uint4*)(rowp + first * E::kBytes);
-  return load_chunk<DT, VEC>(rowp, first, V);
+  if (VEC && interior) return *(const uint4*)(rowp + wave_base * E::kBytes + loff);
+  return load_chunk<DT, VEC>(rowp, wave_base + (int64_t)(c * 64 + lane) * E::kPer, V);
 }
 
-// Append the keys a lane holds (0 = none) to its wave's pool in one step;
-// returns false if they do not fit even after a compaction.
-template <int N>
-__device__ __forceinline__ bool pool_append_all(WavePool& wp, uint64_t (&keys)[N], int lane) {
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < N; ++j) cnt += keys[j] != 0ull;
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const uint64_t m = __ballot((cnt >> b) & 1);
-    pre += lanes_below(m) << b;
-    tot += __popcll(m) << b;
-  }
-  if (tot == 0) return true;
-  if (wp.count + tot > kWavePool) {
-    pool_compact(wp, lane);
-    cnt = 0;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      if (wp.have_bar && keys[j] <= wp.bar) keys[j] = 0ull;
-      cnt += keys[j] != 0ull;
+// Admission of a lane into a pool: by 64-bit key above a bar, or (a part's
+// first unit) by value at or above a threshold.
+struct Admit {
+  bool by_key;
+  uint64_t bar;
+  float tau;
+};
+__device__ __forceinline__ bool admitted(const Admit& ad, float x, uint64_t key) {
+  return ad.by_key ? key > ad.bar : x >= ad.tau;
+}
+
+// Hot chunks of the current unit, copied to the wave's LDS stash in
+// compacted order (n may exceed kStash: then the stash is incomplete).
+struct Stage {
+  uint4* stash;
+  int16_t* off;
+  int n;
+};
+__device__ __forceinline__ void stage_chunk(Stage& st, const uint4& r, bool hot, int c, int lane) {
+  const uint64_t m = __ballot(hot);
+  if (m != 0ull) {
+    const int n = __popcll(m);
+    if (st.n + n <= kStash && hot) {
+      const int pos = st.n + lanes_below(m);
+      st.stash[pos] = r;
+      st.off[pos] = (int16_t)(c * 64 + lane);
     }
-    pre = 0;
-    tot = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint64_t m = __ballot((cnt >> b) & 1);
-      pre += lanes_below(m) << b;
-      tot += __popcll(m) << b;
-    }
-    if (wp.count + tot > kWavePool) return false;
+    st.n += n;
   }
-  int pos = wp.count + pre;
-#pragma unroll
-  for (int j = 0; j < N; ++j)
-    if (keys[j] != 0ull) wp.keys[pos++] = keys[j];
-  wp.count += tot;
-  return true;
 }
 
 // One unit's statistics pass over a wave's registers: exp2 against the
 // running max (or the unit's first chunk max), lane and chunk maxima on the
 // side.  With ROLL each chunk's registers are refilled with the same chunk of
 // the next unit as soon as they have been used, so a unit's loads are always
-// in flight behind the current unit's arithmetic.
+// in flight behind the current unit's arithmetic; with STAGE a chunk whose
+// maximum passes tau is stashed first.
 struct PassOut {
   float acc, lm, mref, nb;
 };
 
-template <int DT, bool VEC, bool ROLL>
+template <int DT, bool VEC, bool ROLL, bool STAGE>
 __device__ __forceinline__ PassOut unit_pass(uint4 (&raw)[kChunks], float (&cm)[kChunks],
                                              float m_l, const char* next_rowp, int64_t next_base,
-                                             bool next_interior, int V, int lane) {
+                                             bool next_interior, int V, int lane, float tau,
+                                             bool strict, bool interior, int64_t wave_base,
+                                             Stage& st) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   PassOut o;
@@ -704,74 +736,186 @@ __device__ __forceinline__ PassOut unit_pass(uint4 (&raw)[kChunks], float (&cm)[
     }
     cm[c] = mc;
     o.lm = fmaxf(o.lm, mc);
+    if (STAGE) {
+      bool hot = strict ? mc > tau : mc >= tau;
+      if (!interior) hot = hot && wave_base + (int64_t)(c * 64 + lane) * kPer < V;
+      stage_chunk(st, raw[c], hot, c, lane);
+    }
     if (ROLL) {
-      int64_t nbase = next_base;
-      asm volatile("" : "+v"(nbase) : "v"(o.acc), "v"(o.lm));
-      raw[c] = load_lane_chunk<DT, VEC>(next_rowp, nbase, c, lane, V, next_interior);
+      uint32_t loff = (uint32_t)(c * 1024 + lane * 16);
+      asm volatile("" : "+v"(loff) : "v"(o.acc), "v"(o.lm));
+      raw[c] = load_lane_chunk<DT, VEC>(next_rowp, next_base, loff, c, lane, V, next_interior);
     }
   }
   return o;
 }
 
-// Four workgroups (16 waves) per CU: 128 VGPRs per lane.
-template <int DT, bool VEC, bool FUSED>
+// Expand the stashed chunks one lane per element into the pool.
+template <int DT>
+__device__ __forceinline__ void expand_stash(WavePool& wp, const Stage& st, int64_t wave_base,
+                                             int V, int lane, const Admit& ad) {
+  using E = Elem<DT>;
+  constexpr int kPer = E::kPer;
+  wave_sync();
+  const int total = st.n * kPer;
+  for (int b = 0; b < total; b += 64) {
+    const int e = b + lane;
+    uint64_t k = 0ull;
+    if (e < total) {
+      const int i = e / kPer, j = e - (e / kPer) * kPer;
+      const int64_t id = wave_base + (int64_t)st.off[i] * kPer + j;
+      const uint32_t bits = DT == 1 ? (uint32_t)((const uint16_t*)&st.stash[i])[j] << 16
+                                    : ((const uint32_t*)&st.stash[i])[j];
+      const float x = __uint_as_float(bits);
+      const uint64_t key = make_key(x, (uint32_t)id);
+      if (id < V && admitted(ad, x, key)) k = key;
+    }
+    pool_append(wp, k, lane);
+  }
+  wave_sync();  // the next unit may overwrite the stash
+}
+
+// Every chunk of the wave's slice, read again from memory (the stash
+// overflowed: more hot chunks than it holds, e.g. a run of ties).  One key
+// per lane per step keeps the register footprint small; the next chunk's
+// load is in flight while a chunk is expanded.
+template <int DT, bool VEC>
+__device__ __forceinline__ void expand_global(WavePool& wp, const char* rowp, int64_t wave_base, int V,
+                                           int lane, const Admit& ad) {
+  using E = Elem<DT>;
+  constexpr int kPer = E::kPer;
+  uint4 r = load_chunk<DT, VEC>(rowp, wave_base + (int64_t)lane * kPer, V);
+  for (int c = 0; c < kChunks; ++c) {
+    const int64_t first = wave_base + (int64_t)(c * 64 + lane) * kPer;
+    const uint4 cur = r;
+    if (c + 1 < kChunks) r = load_chunk<DT, VEC>(rowp, first + 64 * kPer, V);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float x = E::get(cur, j);
+      const uint64_t key = make_key(x, (uint32_t)(first + j));
+      pool_append(wp, (first + j < V && admitted(ad, x, key)) ? key : 0ull, lane);
+    }
+  }
+}
+
+// The lane index as a value the compiler cannot prove loop-invariant: lane
+// offsets derived from it are recomputed where used instead of being hoisted
+// out of the round loop and spilled.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
+__device__ __forceinline__ uint64_t lds_load64(const uint64_t* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store64(uint64_t* a, uint64_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Four waves per workgroup, four workgroups per CU: 128 VGPRs per lane.
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void reduce_kernel(
     Params p) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   constexpr int kWaveElems = 64 * kChunks * kPer;
   constexpr int kUnitElems = kWaves * kWaveElems;
-  __shared__ Smem sh;
+  __shared__ ReduceSmem sh;
   extern __shared__ int prefix[];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane_id = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = p.V, U = p.units;
-  const int total = build_prefix(p, prefix, sh);
+  if (tid < kWaves) sh.qbar[tid] = 0ull;  // ordered by the barriers below
+  const int total = build_prefix<kWaves>(p, prefix, sh.scan);
+  // This workgroup's range of the N < 2^31 units (the host checks N).
   const int64_t N = (int64_t)total * U;
-  const int64_t G = p.grid;
-  const int64_t x0 = (int64_t)blockIdx.x * N / G;
-  const int64_t x1 = ((int64_t)blockIdx.x + 1) * N / G;
+  const int x0 = (int)((int64_t)blockIdx.x * N / p.workers);
+  const int x1 = (int)(((int64_t)blockIdx.x + 1) * N / p.workers);
   if (x0 >= x1) return;
 
   UnitPos cur = locate<DT>(p, prefix, x0);
   int part_u0 = cur.u;
   uint4 raw[kChunks];
   {
-    const int64_t wb = (int64_t)cur.u * kUnitElems + (int64_t)w * kWaveElems;
+    const int wb = cur.u * kUnitElems + w * kWaveElems;
     const bool interior = wb + kWaveElems <= V;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c)
-      raw[c] = load_lane_chunk<DT, VEC>(cur.rowp, wb, c, lane, V, interior);
+      raw[c] = load_lane_chunk<DT, VEC>(cur.rowp, wb, (uint32_t)(c * 1024 + lane_id * 16), c,
+                                        lane_id, V, interior);
   }
+  int n_sel = p.id_counts[cur.s];
+  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
+  bool natural = p.K > 0 && n_sel == 0;
 
   // Per lane: running max m_l and the sum, relative to m_l, of exp over the
   // lane's values except one occurrence of m_l (whose term is exactly 1 and
   // is added back when the lanes are combined).
   float m_l = kNegInf, s_l = 0.0f;
-  WavePool wp{&sh.pool[w][0], 0, false, 0ull};
-  int n_sel = p.id_counts[cur.s];
-  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
-  bool natural = p.K > 0 && n_sel == 0;
+  WavePool wp{&sh.pool[w][0], 0, false, 0ull, 0ull};
+  Stage st{&sh.stash[w][0], &sh.stash_off[w][0], 0};
+  uint64_t published = 0ull;
+  // Value bar of the part's first unit as a key: a later lane passes it iff
+  // its value is strictly larger (0: no such bar).
+  uint64_t first_bar = 0ull;
 
-  for (int64_t x = x0; x < x1; ++x) {
+  for (int x = x0; x < x1; ++x) {
+    const int lane = opaque_lane(lane_id);
     const bool has_next = x + 1 < x1;
     UnitPos nxt = cur;
     if (has_next) {
-      if (cur.u + 1 < U) {
-        nxt.u = cur.u + 1;
-      } else {
-        nxt = locate<DT>(p, prefix, x + 1);
-      }
+      if (cur.u + 1 < U) nxt.u = cur.u + 1;
+      else nxt = locate<DT>(p, prefix, x + 1);
     }
     const bool part_ends = !has_next || nxt.a != cur.a;
-    const int64_t wave_base = (int64_t)cur.u * kUnitElems + (int64_t)w * kWaveElems;
-    const int64_t next_base = (int64_t)nxt.u * kUnitElems + (int64_t)w * kWaveElems;
+    const bool part_starts = cur.u == part_u0;
+    const int wave_base = cur.u * kUnitElems + w * kWaveElems;
+    const int next_base = nxt.u * kUnitElems + w * kWaveElems;
+    const bool interior = wave_base + kWaveElems <= V;
     const bool next_interior = next_base + kWaveElems <= V;
 
+    // ---- admission bar known before the pass: the part's first-unit value
+    // bar, the wave's own 32nd-best key, and the smallest of the four
+    // published 8th-best keys (32 keys of the part lie at or above it).
+    Admit ad{false, 0ull, kNegInf};
+    float tau = kNegInf;
+    bool strict = false;
+    if (natural && !part_starts) {
+      uint64_t bq = lds_load64(&sh.qbar[0]);
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) {
+        const uint64_t b = lds_load64(&sh.qbar[i]);
+        bq = b < bq ? b : bq;
+      }
+      uint64_t bar = wp.have_bar ? wp.bar : 0ull;
+      bar = bq > bar ? bq : bar;
+      bar = first_bar > bar ? first_bar : bar;
+      bar = readlane64(bar, 0);  // every lane read the same words
+      if (bar != 0ull) {
+        ad.by_key = true;
+        ad.bar = bar;
+        tau = key_value(bar);
+        // A lane of this unit equal in value to the bar has a larger ID
+        // whenever the bar's lane precedes the wave's slice.
+        strict = key_id(bar) < (uint32_t)wave_base;
+      }
+    }
+    const bool roll = has_next && (!natural || ad.by_key);
+
+    st.n = 0;
     float cm[kChunks];
-    const PassOut po =
-        has_next ? unit_pass<DT, VEC, true>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V, lane)
-                 : unit_pass<DT, VEC, false>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V, lane);
+    PassOut po;
+    if (!roll)
+      po = unit_pass<DT, VEC, false, false>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V,
+                                            lane, tau, strict, interior, wave_base, st);
+    else if (natural)
+      po = unit_pass<DT, VEC, true, true>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V,
+                                          lane, tau, strict, interior, wave_base, st);
+    else
+      po = unit_pass<DT, VEC, true, false>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V,
+                                           lane, tau, strict, interior, wave_base, st);
     const float lm = po.lm;
 
     // ---- fold the unit into the lane's running (max, sum)
@@ -804,60 +948,53 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
     // ---- candidates for this wave's pool
     if (natural) {
-      // Threshold: after the pool's first compaction, its 32nd-best key (a
-      // later lane equal to that key's value has a larger ID and cannot
-      // beat it, so values must be strictly larger); before it, the wave's
-      // 32nd-largest lane maximum (lane maxima are distinct lanes), or -inf
-      // when fewer than 32 lanes hold any of the vocabulary.
-      const bool strict = wp.have_bar;
-      float tau = kNegInf;
-      if (strict) {
-        tau = key_value(wp.bar);
-      } else {
-        const int64_t rem = (int64_t)V - wave_base;
-        const int vl = rem <= 0 ? 0 : (rem >= 64 * kPer ? 64 : (int)((rem + kPer - 1) / kPer));
-        if (vl >= kKeep) tau = key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, kKeep));
+      if (part_starts) {
+        // The part's first unit, still in registers.  Its threshold T is
+        // the smallest over the workgroup's waves of each wave's k-th
+        // largest lane maximum, k = ceil(32 / waves holding vocabulary):
+        // lane maxima are distinct lanes, so at least 32 lanes of the unit
+        // reach T.  A wave with fewer than k such lanes makes T = -inf.
+        const int ubase = cur.u * kUnitElems;
+        const int nw = V - ubase >= kUnitElems ? kWaves
+                                               : (V - ubase + kWaveElems - 1) / kWaveElems;
+        const int k = (kKeep + nw - 1) / nw;
+        const int rem = V - wave_base;
+        const int vl = rem <= 0 ? 0 : (rem >= 64 * kPer ? 64 : (rem + kPer - 1) / kPer);
+        float tw = __builtin_huge_valf();  // waves without vocabulary do not vote
+        if (vl > 0)
+          tw = vl >= k ? key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, k)) : kNegInf;
+        if (lane == 0) sh.tw[w] = tw;
+        __syncthreads();
+        tau = fminf(fminf(sh.tw[0], sh.tw[1]), fminf(sh.tw[2], sh.tw[3]));
+        __syncthreads();  // sh.tw is rewritten at the next part
+        ad.by_key = false;
+        ad.tau = tau;
+        strict = false;
+        first_bar = tau == kNegInf ? 0ull : ((uint64_t)ukey32(tau) << 32) | 0xFFFFFFFFull;
       }
-      // Stage the offsets of hot chunks (maximum passes tau), then expand
-      // them 64 at a time, one reloaded chunk per lane.
-      if (__ballot(strict ? lm > tau : lm >= tau) != 0ull) {
-        int nh = 0;
+      if (!roll) {
+        // Registers still hold the unit: stash its hot chunks, then start
+        // loading the next unit.
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
-          const int64_t first = wave_base + (int64_t)(c * 64 + lane) * kPer;
-          const bool hot = first < V && (strict ? cm[c] > tau : cm[c] >= tau);
-          const uint64_t m = __ballot(hot);
-          if (hot) sh.stage_off[w][nh + lanes_below(m)] = (int32_t)first;
-          nh += __popcll(m);
+          bool hot = strict ? cm[c] > tau : cm[c] >= tau;
+          if (!interior) hot = hot && wave_base + (c * 64 + lane) * kPer < V;
+          stage_chunk(st, raw[c], hot, c, lane);
         }
-        wave_sync();
-        for (int b = 0; b < nh; b += 64) {
-          const bool mine = b + lane < nh;
-          const int64_t first = mine ? (int64_t)sh.stage_off[w][b + lane] : 0;
-          const uint4 r = mine ? load_chunk<DT, VEC>(cur.rowp, first, V) : make_uint4(0u, 0u, 0u, 0u);
-          uint64_t keys[kPer];
+        if (has_next) {
 #pragma unroll
-          for (int j = 0; j < kPer; ++j) {
-            const float xv = E::get(r, j);
-            const int64_t id = first + j;
-            const uint64_t k = make_key(xv, (uint32_t)id);
-            const bool pass = mine && id < V && (wp.have_bar ? k > wp.bar : xv >= tau);
-            keys[j] = pass ? k : 0ull;
-          }
-          if (!pool_append_all(wp, keys, lane)) {
-            // More qualifying lanes than a pool holds even after compaction
-            // (ties at the threshold): one key per lane per step.
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-              uint64_t k = keys[j];
-              if (wp.have_bar && k <= wp.bar) k = 0ull;
-              pool_append(wp, k, lane);
-            }
-          }
+          for (int c = 0; c < kChunks; ++c)
+            raw[c] = load_lane_chunk<DT, VEC>(nxt.rowp, next_base, (uint32_t)(c * 1024 + lane * 16),
+                                              c, lane, V, next_interior);
         }
-        wave_sync();
       }
-      if (!wp.have_bar && wp.count >= kKeep) pool_compact(wp, lane);
+      if (st.n > kStash) expand_global<DT, VEC>(wp, cur.rowp, wave_base, V, lane, ad);
+      else if (st.n > 0) expand_stash<DT>(wp, st, wave_base, V, lane, ad);
+      if (wp.count >= kCompactAt) pool_compact(wp, lane);
+      if (wp.b8 != published) {
+        published = wp.b8;
+        if (lane == 0) lds_store64(&sh.qbar[w], published);
+      }
     }
 
     if (part_ends) {
@@ -877,16 +1014,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         if (lane < kKeep && lane >= wp.count) wp.keys[lane] = 0ull;
       }
       __syncthreads();
-      const int u1 = cur.u + 1;
-      PartRecord* rec = p.records + (int64_t)cur.row * U + part_u0;
       if (w == 0) {
+        PartRecord* rec = p.records + (int64_t)cur.row * U + part_u0;
         uint64_t top = 0ull;
         int held = 0;
         if (natural) {
           top = lane < kKeep ? sh.pool[0][lane] : 0ull;
 #pragma unroll
-          for (int q = 1; q < kWaves; ++q)
-            top = merge_top32(top, lane < kKeep ? sh.pool[q][lane] : 0ull, lane);
+          for (int i = 1; i < kWaves; ++i)
+            top = merge_top32(top, lane < kKeep ? sh.pool[i][lane] : 0ull, lane);
           held = __popcll(__ballot(lane < kKeep && top != 0ull));
         }
         if (lane < kKeep) rec->keys[lane] = top;
@@ -898,26 +1034,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
             for (int i = 0; i < kWaves; ++i)
               if (sh.wm[i] != kNegInf)
                 S += sh.ws[i] * __builtin_amdgcn_exp2f((sh.wm[i] - M) * kLog2e);
-          const int64_t lo = (int64_t)part_u0 * kUnitElems;
-          const int64_t hi = (int64_t)u1 * kUnitElems < V ? (int64_t)u1 * kUnitElems : V;
+          const int lo = part_u0 * kUnitElems;
+          const int hi = (cur.u + 1) * kUnitElems < V ? (cur.u + 1) * kUnitElems : V;
           rec->m = M;
           rec->s = S;
           rec->n = held;
-          rec->flags = (hi - lo <= kKeep) ? kRecComplete : 0;
-        }
-        if (FUSED) {
-          // Publish the record, then count this part's units on the ticket.
-          __threadfence();
-          if (lane == 0)
-            sh.ticket_old = atomicAdd(&p.tickets[cur.row], (uint32_t)(u1 - part_u0));
+          rec->flags = hi - lo <= kKeep ? kRecComplete : 0;
         }
       }
-      __syncthreads();
-      if (FUSED && sh.ticket_old + (uint32_t)(u1 - part_u0) == (uint32_t)U) {
-        __threadfence();  // acquire the other parts' records
-        merge_row<DT>(p, sh, N, cur.row, cur.a, cur.s, n_sel, natural);
-        if (tid == 0) p.tickets[cur.row] = 0u;
-      }
+      if (lane == 0) lds_store64(&sh.qbar[w], 0ull);
+      __syncthreads();  // pools, wm/ws and qbar are reused by the next part
       // ---- next part
       if (has_next) {
         m_l = kNegInf;
@@ -925,6 +1051,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         wp.count = 0;
         wp.have_bar = false;
         wp.bar = 0ull;
+        wp.b8 = 0ull;
+        published = 0ull;
+        first_bar = 0ull;
         part_u0 = nxt.u;
         n_sel = p.id_counts[nxt.s];
         n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
@@ -935,65 +1064,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   }
 }
 
-// Separate merge launch (when the plan does not fuse): one workgroup per
-// physical row.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void merge_kernel(Params p) {
-  __shared__ Smem sh;
-  extern __shared__ int prefix[];
-  const int total = build_prefix(p, prefix, sh);
-  const int row = blockIdx.x;
-  const int s = row / p.T, t = row - s * p.T;
-  if (t >= slot_rows(p, s)) return;
-  int n_sel = p.id_counts[s];
-  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
-  merge_row<DT>(p, sh, (int64_t)total * p.units, row, prefix[s] + t, s, n_sel,
-                p.K > 0 && n_sel == 0);
-}
-
-__global__ void reset_kernel(uint32_t* t, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    t[i] = 0u;
-}
-
 template <int DT, bool VEC>
 hipError_t launch_typed(const Params& p, hipStream_t st) {
-  const size_t lds = reduce_lds_bytes(p.capacity);
-  if (p.fused) {
-    hipLaunchKernelGGL((reduce_kernel<DT, VEC, true>), dim3((uint32_t)p.grid), dim3(kBlock), lds,
-                       st, p);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL((reduce_kernel<DT, VEC, false>), dim3((uint32_t)p.grid), dim3(kBlock), lds,
-                     st, p);
+  const size_t lds = prefix_lds_bytes(p.capacity);
+  hipLaunchKernelGGL((reduce_kernel<DT, VEC>), dim3((uint32_t)p.workers), dim3(kBlock), lds, st,
+                     p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.capacity * p.T;
-  hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)rows), dim3(kBlock), lds, st, p);
+  hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)rows), dim3(kMergeBlock), lds, st, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t reduce_lds_bytes(int capacity) { return (size_t)(capacity + 1) * sizeof(int); }
+size_t prefix_lds_bytes(int capacity) { return (size_t)(capacity + 1) * sizeof(int); }
 
 int reduce_occupancy(int dtype, bool vector_rows, int capacity) {
-  // Sized for the default (separate merge) kernel; the fused variant is
-  // launched with the same grid.
   int n = 0;
-  const size_t lds = reduce_lds_bytes(capacity);
+  const size_t lds = prefix_lds_bytes(capacity);
   hipError_t e;
   if (dtype == 1)
-    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          &n, reduce_kernel<1, true, false>, kBlock, lds)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          &n, reduce_kernel<1, false, false>, kBlock, lds);
+    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<1, true>,
+                                                                   kBlock, lds)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<1, false>,
+                                                                   kBlock, lds);
   else
-    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          &n, reduce_kernel<0, true, false>, kBlock, lds)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          &n, reduce_kernel<0, false, false>, kBlock, lds);
+    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<0, true>,
+                                                                   kBlock, lds)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<0, false>,
+                                                                   kBlock, lds);
   return e == hipSuccess ? n : 0;
 }
 
@@ -1005,15 +1105,6 @@ int launch_reduce(const Params& p, int dtype, bool vector_rows, void* stream) {
   else
     e = vector_rows ? launch_typed<0, true>(p, st) : launch_typed<0, false>(p, st);
   return (int)e;
-}
-
-int launch_reset(uint32_t* tickets, int64_t n, void* stream) {
-  if (n <= 0) return 0;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(reset_kernel, dim3((uint32_t)blocks), dim3(256), 0, (hipStream_t)stream,
-                     tickets, n);
-  return (int)hipGetLastError();
 }
 
 }  // namespace flp

@@ -32,8 +32,8 @@
  *
  * Threading and memory: every device buffer is owned by the caller.  The
  * library keeps no pointer after a call returns and never allocates, frees,
- * synchronizes or compiles at run time, so flare_logprobs_run may be captured
- * in a HIP graph.  Calls on one stream are ordered; concurrent calls need
+ * synchronizes or compiles at run time, and records no memset, so
+ * flare_logprobs_run may be captured in a HIP graph.  Calls on one stream are ordered; concurrent calls need
  * distinct workspaces.  The inputs are only read.
  */
 #ifndef FLARE_LOGPROBS_H
@@ -69,8 +69,8 @@ enum flare_status {
 /*
  * A plan is a host value filled by flare_logprobs_plan.  It owns nothing and
  * needs no destruction.  Fields after `device` are chosen by the library and
- * are informational, except workspace_bytes, which the caller must allocate,
- * and `fused`, which the caller may set to 0 or 1 before flare_logprobs_run.
+ * are informational, except workspace_bytes, which the caller must allocate.
+ * flare_logprobs_run rejects a plan whose fields were altered.
  */
 typedef struct flare_logprobs_plan {
   uint32_t abi_version;
@@ -83,18 +83,16 @@ typedef struct flare_logprobs_plan {
   int32_t device;        /* HIP device ordinal, or -1 for a host-only plan */
   int32_t unit_elems;    /* vocabulary lanes one workgroup holds at a time */
   int32_t units;         /* units per row, ceil(V / unit_elems), at most 64 */
-  int32_t block;         /* threads per workgroup */
-  int32_t grid;          /* workgroups of the persistent launch */
+  int32_t block;         /* threads per reduction workgroup */
+  int32_t grid;          /* reduction workgroups of the persistent launch */
   int32_t vector_rows;   /* 1 if V_pad * element size is a multiple of 16 */
   int32_t cu_count;      /* compute units of `device` (256 if host-only) */
-  int32_t fused;         /* 0: a second launch merges every row (default);
-                            1: the workgroup that finishes a row merges it
-                            in the same launch, behind agent-scope fences */
+  int32_t ranges;        /* contiguous unit ranges of the launch (== grid) */
   int32_t reserved0;
   uint64_t workspace_bytes; /* bytes of device workspace the caller provides */
   uint64_t record_offset;   /* per-(row, unit) part records */
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
-  uint64_t ticket_offset;   /* uint32[capacity * T]: arrival counters */
+  uint64_t reserved1;
   uint32_t reserved[8];
 } flare_logprobs_plan_t;
 
@@ -123,9 +121,11 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
  *   emitted_counts  device int32 [capacity]: committed prefix length per slot
  *   tokens          device int32 [capacity, T]: chosen token of each position
  *   out             device int32 [capacity, T, 258]: one output frame
- *   workspace       device, plan->workspace_bytes, 16-byte aligned, zeroed
- *                   once before first use (the library leaves it reusable)
- * Host-checkable errors return before anything is launched.
+ *   workspace       device, plan->workspace_bytes, 16-byte aligned; needs no
+ *                   initialisation (every word read is written first in the
+ *                   same call)
+ * Two kernels run in order on the stream: the reduction, then the per-row
+ * merge.  Host-checkable errors return before anything is launched.
  */
 int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
                        int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
@@ -133,14 +133,6 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
                        const int32_t* ids, const int32_t* emitted_counts,
                        const int32_t* tokens, int32_t K, int32_t* out,
                        void* workspace, void* hip_stream);
-
-/*
- * Return a workspace to its initial state (all arrival counters zero) with
- * a fill kernel on `hip_stream`; needed only after a run was abandoned
- * mid-flight.  Safe to capture in a HIP graph.
- */
-int flare_logprobs_workspace_reset(const flare_logprobs_plan_t* plan, void* workspace,
-                                   void* hip_stream);
 
 /* Human-readable name of a flare_status value (static storage). */
 const char* flare_status_string(int status);

@@ -23,11 +23,10 @@ def to_device(w: synth.Workload, dev="cuda"):
                 requested=g(w.requested), id_counts=g(w.id_counts), ids=g(w.ids))
 
 
-def make_plan(spec: synth.Spec, K: int | None = None, fused: bool = False):
+def make_plan(spec: synth.Spec, K: int | None = None):
     return flp.Plan(spec.capacity, spec.T, spec.V, spec.V_pad,
                     dtype=torch.bfloat16 if spec.dtype == synth.BF16 else torch.float32,
-                    K=spec.K if K is None else K, device=torch.cuda.current_device(),
-                    fused=fused)
+                    K=spec.K if K is None else K, device=torch.cuda.current_device())
 
 
 def run_gpu(w: synth.Workload, dev_inputs=None, plan=None, ws=None, logits=None):

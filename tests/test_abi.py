@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"flare_logprobs_plan", "flare_logprobs_run", "flare_logprobs_workspace_reset",
+    assert {"flare_logprobs_plan", "flare_logprobs_run",
             "flare_status_string", "flare_logprobs_abi_version"} <= set(names)
 
 
@@ -64,10 +64,9 @@ def test_plan_host_only_geometry(flp):
     rc, p = host_plan(flp)
     assert rc == 0
     assert p.units == 16 and p.unit_elems == 16384 and p.block == 256 and p.vector_rows == 1
-    assert p.cu_count == 256 and p.abi_version == 1 and p.grid == 1024 and p.fused == 0
+    assert p.cu_count == 256 and p.abi_version == 1 and p.grid == 1024 and p.ranges == 1024
     rows = 128 * 8
-    assert p.lse_offset >= rows * 16 * 272 and p.ticket_offset >= p.lse_offset + 4 * rows
-    assert p.workspace_bytes >= p.ticket_offset + 4 * rows
+    assert p.lse_offset >= rows * 16 * 272 and p.workspace_bytes >= p.lse_offset + 4 * rows
     rc, p = host_plan(flp, capacity=1024, T=4, V=262144, V_pad=262144, dtype=0)
     assert rc == 0 and p.units == 32 and p.unit_elems == 8192
     rc, p = host_plan(flp, V=37, V_pad=41)
@@ -129,22 +128,19 @@ def test_run_rejects_bad_dtype_and_stale_plan(flp):
 
 def test_run_rejects_corrupt_plan(flp):
     rc, plan = host_plan(flp)
-    plan.fused = 2
+    plan.ranges = 3
     assert run_status(flp, plan) == 3
     rc, plan = host_plan(flp)
     plan.grid = 0
+    assert run_status(flp, plan) == 3
+    rc, plan = host_plan(flp)
+    plan.block = 1024
     assert run_status(flp, plan) == 3
 
 
 def test_run_rejects_misaligned_workspace(flp):
     rc, plan = host_plan(flp)
     assert run_status(flp, plan, workspace=FAKE + 4) == 1
-
-
-def test_reset_rejects_null(flp):
-    rc, plan = host_plan(flp)
-    assert flp.lib().flare_logprobs_workspace_reset(ctypes.byref(plan), None, None) == 1
-    assert flp.lib().flare_logprobs_workspace_reset(None, FAKE, None) == 1
 
 
 def test_binding_names_mirror_the_abi(flp):

@@ -261,19 +261,24 @@ def test_unaligned_base_pointer(oracle_handle):
 
 
 @pytest.mark.parametrize("name", ["C3", "C4", "C5"])
-def test_fused_merge_mode(oracle_handle, name):
-    """The in-launch merge (plan.fused = 1) gives the same frame as the
-    oracle and as the separate merge launch."""
+def test_workspace_needs_no_initialisation(oracle_handle, name):
+    """A workspace full of garbage (every byte 0xFF, then a random fill)
+    gives the oracle's frame: the library reads no workspace word before it
+    writes it in the same call."""
     spec = synth.CONFIGS[name].with_(capacity={"C3": 6, "C4": 10, "C5": 3}[name])
-    announce(f"fused merge mode {name} cap={spec.capacity}")
+    announce(f"garbage workspace {name} cap={spec.capacity}")
     w = synth.make(spec)
     d = H.to_device(w)
-    got_f, lse_f = H.run_gpu(w, d, plan=H.make_plan(spec, fused=True))
-    got_s, lse_s = H.run_gpu(w, d, plan=H.make_plan(spec, fused=False))
+    plan = H.make_plan(spec)
     ref = H.oracle_frame(oracle_handle, w)
-    H.compare_words(got_f, ref, f"{name} fused")
-    assert np.array_equal(got_f, got_s)
-    assert np.array_equal(lse_f.view(np.int32), lse_s.view(np.int32))
+    ws = plan.workspace()
+    ws.fill_(0xFF)
+    got, _ = H.run_gpu(w, d, plan=plan, ws=ws)
+    H.compare_words(got, ref, f"{name} 0xFF workspace")
+    g = torch.Generator(device="cpu").manual_seed(11)
+    ws.copy_(torch.randint(0, 256, (ws.numel(),), generator=g, dtype=torch.uint8))
+    got2, _ = H.run_gpu(w, d, plan=plan, ws=ws)
+    assert np.array_equal(got, got2)
 
 
 # -------------------------------------------------- repeatability and graphs
