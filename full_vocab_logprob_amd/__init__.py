@@ -46,8 +46,8 @@ class PlanStruct(ctypes.Structure):
                 ("vector_rows", ctypes.c_int32), ("cu_count", ctypes.c_int32),
                 ("ranges", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
-                ("lse_offset", ctypes.c_uint64), ("reserved1", ctypes.c_uint64),
-                ("reserved", ctypes.c_uint32 * 8)]
+                ("lse_offset", ctypes.c_uint64), ("index_offset", ctypes.c_uint64),
+                ("start_offset", ctypes.c_uint64), ("reserved", ctypes.c_uint32 * 6)]
 
 
 class FlareError(RuntimeError):

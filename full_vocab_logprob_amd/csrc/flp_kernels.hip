@@ -307,54 +307,76 @@ __device__ __forceinline__ uint32_t wave_kth_largest16(uint32_t key, bool voter,
   return prefix;
 }
 
-// ------------------------------------------------------- per-wave key pool
-// Each wave keeps, for the part it is reducing, a pool of candidate raw keys
-// that always contains the best 32 keys of the wave's lanes seen so far.
-// Compaction keeps exactly those 32 and makes their 32nd the admission bar.
-constexpr int kWavePool = 128;
+// ------------------------------------------------------ per-wave best 32
+// Each wave keeps the best 32 raw keys of the part it is reducing as a list
+// sorted descending across lanes 0..31 (0 marks an empty slot; lanes 32..63
+// hold scratch).  A unit's new candidates are gathered in an LDS buffer and
+// then inserted: a few one at a time (a ballot gives the position, a wave
+// shift opens the slot), more by sorting them and merging.
+constexpr int kCandBuf = 128;   // candidate slots per wave
+constexpr int kInsertMax = 12;  // larger batches are sorted and merged
 
-struct WavePool {
-  uint64_t* keys;  // this wave's kWavePool slots in LDS
-  int count;
-  bool have_bar;
-  uint64_t bar;    // 32nd-best key after the last compaction
-  uint64_t b8;     // 8th-best key after the last compaction (0: fewer than 8)
+struct Best32 {
+  uint64_t top;  // lane i < 32: the i-th best key
+  int n;         // keys held (wave-uniform)
+  uint64_t bar;  // the 32nd-best key once n == 32, else 0 (wave-uniform)
 };
 
-__device__ __forceinline__ void pool_compact(WavePool& wp, int lane) {
-  wave_sync();
-  uint64_t a = lane < wp.count ? wp.keys[lane] : 0ull;
-  a = sort64_desc(a, lane);
-  if (wp.count > 64) {
-    uint64_t b = 64 + lane < wp.count ? wp.keys[64 + lane] : 0ull;
-    b = sort64_desc(b, lane);
-    a = merge_top32(a, b, lane);
-  }
-  wave_sync();
-  if (lane < kKeep) wp.keys[lane] = a;
-  wave_sync();
-  wp.b8 = wp.count >= 8 ? readlane64(a, 7) : 0ull;
-  if (wp.count >= kKeep) {
-    wp.have_bar = true;
-    wp.bar = readlane64(a, kKeep - 1);
-    wp.count = kKeep;
-  }
+// Value held by lane - 1 (0 in lane 0).
+__device__ __forceinline__ uint64_t wave_shr1_64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x138, 0xf, 0xf, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x138, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// Append one key per lane (0 = none).
-__device__ __forceinline__ void pool_append(WavePool& wp, uint64_t k, int lane) {
+// Insert the wave-uniform key k if it ranks among the best 32.
+__device__ __forceinline__ void best_insert(Best32& b, uint64_t k, int lane) {
+  const int p = __popc((uint32_t)__ballot(b.top > k));  // better keys in lanes 0..31
+  if (p >= kKeep) return;
+  const uint64_t shifted = wave_shr1_64(b.top);
+  b.top = lane < p ? b.top : (lane == p ? k : shifted);
+  b.n = b.n < kKeep ? b.n + 1 : kKeep;
+}
+
+struct CandBuf {
+  uint64_t* keys;  // this wave's kCandBuf slots in LDS
+  int count;
+};
+
+// Move the buffered candidates into the list and empty the buffer.
+__device__ __forceinline__ void cand_flush(CandBuf& cb, Best32& b, int lane) {
+  if (cb.count == 0) return;
+  wave_sync();
+  if (cb.count <= kInsertMax) {
+    const uint64_t mine = lane < cb.count ? cb.keys[lane] : 0ull;
+    for (int i = 0; i < cb.count; ++i) best_insert(b, readlane64(mine, i), lane);
+  } else {
+    for (int base = 0; base < cb.count; base += 64) {
+      const uint64_t v = base + lane < cb.count ? cb.keys[base + lane] : 0ull;
+      b.top = merge_top32(b.top, sort64_desc(v, lane), lane);
+    }
+    b.n = __popc((uint32_t)__ballot(b.top != 0ull));
+  }
+  wave_sync();
+  cb.count = 0;
+  b.bar = b.n >= kKeep ? readlane64(b.top, kKeep - 1) : 0ull;
+}
+
+// Buffer one key per lane (0 = none).
+__device__ __forceinline__ void cand_append(CandBuf& cb, Best32& b, uint64_t k, int lane) {
   uint64_t m = __ballot(k != 0ull);
   if (m == 0ull) return;
   int n = __popcll(m);
-  if (wp.count + n > kWavePool) {
-    pool_compact(wp, lane);
-    if (wp.have_bar && k <= wp.bar) k = 0ull;
+  if (cb.count + n > kCandBuf) {
+    cand_flush(cb, b, lane);
+    if (k <= b.bar) k = 0ull;
     m = __ballot(k != 0ull);
     if (m == 0ull) return;
     n = __popcll(m);
   }
-  if (k != 0ull) wp.keys[wp.count + lanes_below(m)] = k;
-  wp.count += n;
+  if (k != 0ull) cb.keys[cb.count + lanes_below(m)] = k;
+  cb.count += n;
 }
 
 // ------------------------------------------------------------ row mapping
@@ -415,41 +437,11 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
   return lo;
 }
 
-// Is global unit x the first unit of some workgroup's range (W ranges)?
-__device__ __forceinline__ bool range_start(int64_t x, int64_t N, int64_t W) {
-  const int64_t k = (x * W + N - 1) / N;
-  return k <= W && (k * N) / W == x;
-}
-
 // ==================================================================== merge
-constexpr int kMergeWaves = kMergeBlock / 64;
-
-struct MergeSmem {
-  uint64_t batch[kMergeBlock + 2];  // 256 keys, then the unsafe-part mask and F_K
-  float L;
-  int n_parts;
-  int unsafe_any;
-  int16_t part_u0[kMaxUnits + 1];
-  int scan[kMergeWaves];
-};
-
-// Sort each wave's 64 keys of batch[0, 256), then fold them into wave 0's
-// running best-32 `top` (lanes 0..31).  All threads; three barriers.
-__device__ __forceinline__ void fold_batch(uint64_t* batch, uint64_t& top, int lane, int w) {
-  __syncthreads();
-  uint64_t v = sort64_desc(batch[w * 64 + lane], lane);
-  batch[w * 64 + lane] = v;
-  __syncthreads();
-  if (w == 0) {
-    top = merge_top32(top, v, lane);
-#pragma unroll
-    for (int q = 1; q < kMergeWaves; ++q) top = merge_top32(top, batch[q * 64 + lane], lane);
-  }
-  __syncthreads();
-}
-
-// Merge row `row` (active row a, slot s): L from its parts in part order,
-// the chosen and selected gathers, and the natural top K.
+// One wave per row, four rows per workgroup: L from the row's parts in part
+// order, the chosen and selected gathers, and the natural top K.  The
+// reduction left each active row's index among the active rows and their
+// count in the workspace, which locate the row's parts without a scan.
 //
 // Exactness guard.  A part keeps its best 32 raw keys; let c be the 32nd,
 // with value x_c.  With F the final key (reported value, then smaller ID),
@@ -460,177 +452,179 @@ __device__ __forceinline__ void fold_batch(uint64_t* batch, uint64_t& top, int l
 // and r(pred(x_c)) < v_K no dropped lane can enter the top K.  A part that
 // fails either test is rescanned lane by lane with final keys; F_K over a
 // subset never exceeds the true K-th key, so the test stays sound.
+constexpr int kMergeWaves = kMergeBlock / 64;
+
 template <int DT>
-__device__ void merge_row(const Params& p, MergeSmem& sh, int64_t N, int row, int a, int s,
-                          int n_sel, bool natural) {
+__global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kUnitElems = kUnitThreads * kChunks * E::kPer;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ int16_t part_u0_all[kMergeWaves][kMaxUnits + 1];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = (int)blockIdx.x * kMergeWaves + wv;
+  if (row >= p.capacity * p.T) return;
+  const int s = row / p.T, t = row - s * p.T;
+  // Every input word this row needs, loaded at once (the index words are
+  // only meaningful for an active row).
+  const int req = p.requested[s], emi = p.emitted[s], cnt = p.id_counts[s];
+  const int a = p.row_index[row];
+  const int tok = p.tokens[row];
+  if (req == 0 || t >= (emi < 0 ? 0 : (emi > p.T ? p.T : emi))) return;
+  const int n_sel = cnt < 0 ? 0 : (cnt > 128 ? 128 : cnt);
+  const bool natural = p.K > 0 && n_sel == 0;
   const int V = p.V, U = p.units;
   const PartRecord* rec = p.records + (int64_t)row * U;
   const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * E::kBytes;
   int32_t* out = p.out + (int64_t)row * kRowWords;
-  const int tok = p.tokens[row];
-  const int sel_id = tid < n_sel ? p.ids[(int64_t)s * 128 + tid] : 0;
+  int16_t* part_u0 = part_u0_all[wv];
 
-  // ---- the row's parts (one lane per unit) and L (one lane per part)
-  if (w == 0) {
-    const bool start = lane < U && (lane == 0 || range_start((int64_t)a * U + lane, N, p.workers));
-    const uint64_t m = __ballot(start);
-    const int np = __popcll(m);
-    if (start) sh.part_u0[lanes_below(m)] = (int16_t)lane;
-    if (lane == 0) {
-      sh.n_parts = np;
-      sh.part_u0[np] = (int16_t)U;
-      sh.unsafe_any = 0;
-    }
-    wave_sync();
-    float pm = kNegInf, ps = 0.0f;
-    if (lane < np) {
-      const PartRecord& r = rec[sh.part_u0[lane]];
-      pm = r.m;
-      ps = r.s;
-    }
-    const float M = wave_max(pm, lane);
-    float term = 0.0f;
-    if (lane < np && pm != kNegInf) term = ps * __builtin_amdgcn_exp2f((pm - M) * kLog2e);
-    const float S = wave_sum(term, lane);
-    const float L = M + logf(S);
-    if (lane == 0) {
-      sh.L = L;
-      p.lse[row] = L;
+  // ---- the row's parts (one lane per unit)
+  const bool start = lane < U && (lane == 0 || p.unit_start[(int64_t)a * U + lane] != 0);
+  const uint64_t starts = __ballot(start);
+  const int np = __popcll(starts);
+  if (start) part_u0[lanes_below(starts)] = (int16_t)lane;
+  if (lane == 0) part_u0[np] = (int16_t)U;
+  wave_sync();
+  const int u0 = lane < np ? part_u0[lane] : 0;
+
+  // ---- record and logit loads, issued together: the part statistics, the
+  // first two parts' kept keys and each part's guard words
+  float pm = kNegInf, ps = 0.0f;
+  uint64_t c_key = 0ull;
+  int32_t c_flags = kRecComplete;
+  if (lane < np) {
+    pm = rec[u0].m;
+    ps = rec[u0].s;
+    c_key = rec[u0].keys[kKeep - 1];
+    c_flags = rec[u0].flags;
+  }
+  const uint64_t raw0 = (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
+  float x_tok = 0.0f;
+  if (lane == 0 && tok >= 0 && tok < V) x_tok = load_elem<DT>(rowp, tok);
+  int sel_id[2] = {0, 0};
+  float x_sel[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    if (j < n_sel) {
+      sel_id[h] = p.ids[(int64_t)s * 128 + j];
+      if (sel_id[h] >= 0 && sel_id[h] < V) x_sel[h] = load_elem<DT>(rowp, sel_id[h]);
     }
   }
-  __syncthreads();
-  const float L = sh.L;
-  const int np = sh.n_parts;
 
-  // ---- chosen token and selected IDs
-  if (tid == 0) {
-    uint32_t bits = kNanBits;
-    if (tok >= 0 && tok < V) bits = __float_as_uint(reported(load_elem<DT>(rowp, tok), L));
+  // ---- L, one lane per part
+  const float M = wave_max(pm, lane);
+  float term = 0.0f;
+  if (lane < np && pm != kNegInf) term = ps * __builtin_amdgcn_exp2f((pm - M) * kLog2e);
+  const float L = M + logf(wave_sum(term, lane));
+  if (lane == 0) {
+    p.lse[row] = L;
     out[0] = tok;
-    out[1] = (int32_t)bits;
+    out[1] = (int32_t)(tok >= 0 && tok < V ? __float_as_uint(reported(x_tok, L)) : kNanBits);
   }
-  if (tid < n_sel) {
-    uint32_t bits = kNanBits;
-    if (sel_id >= 0 && sel_id < V) bits = __float_as_uint(reported(load_elem<DT>(rowp, sel_id), L));
-    *(int2*)(out + 2 + 2 * tid) = make_int2(sel_id, (int32_t)bits);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    if (j < n_sel) {
+      const uint32_t bits = sel_id[h] >= 0 && sel_id[h] < V ? __float_as_uint(reported(x_sel[h], L))
+                                                            : kNanBits;
+      *(int2*)(out + 2 + 2 * j) = make_int2(sel_id[h], (int32_t)bits);
+    }
   }
-  if (natural) {
-    const int K = p.K;
-    const int Keff = K < V ? K : V;
-    uint64_t* batch = sh.batch;
-    uint64_t top = 0ull;  // wave 0: best 32 final keys so far, lanes 0..31
-    // ---- kept candidates, 8 parts (256 keys) per batch, re-keyed by F
-    for (int pb = 0; pb < np; pb += kMergeBlock / kKeep) {
-      const int part = pb + (tid >> 5), k = tid & 31;
+  if (!natural) return;
+
+  // ---- kept candidates re-keyed by F, two parts (64 keys) per step
+  const int K = p.K;
+  const int Keff = K < V ? K : V;
+  uint64_t top = sort64_desc(raw0 != 0ull ? final_key(raw0, L) : 0ull, lane);
+  for (int pb = 2; pb < np; pb += 2) {
+    const int part = pb + (lane >> 5);
+    uint64_t f = 0ull;
+    if (part < np) {
+      const uint64_t raw = rec[part_u0[part]].keys[lane & 31];
+      if (raw != 0ull) f = final_key(raw, L);
+    }
+    top = merge_top32(top, sort64_desc(f, lane), lane);
+  }
+  // ---- guard, one lane per part
+  const uint64_t FK = readlane64(top, Keff - 1);
+  bool bad = false;
+  if (lane < np && !(c_flags & kRecComplete)) {
+    const float xc = key_value(c_key);
+    bool ok = final_key(c_key, L) <= FK;
+    if (ok && xc != kNegInf) ok = ukey32(reported(E::pred(xc), L)) < (uint32_t)(FK >> 32);
+    bad = !ok;
+  }
+  const uint64_t unsafe = __ballot(bad);
+  if (unsafe != 0ull) {
+    // Rebuild from the safe parts' candidates plus every lane of each unsafe
+    // part whose final key reaches FK.
+    top = 0ull;
+    for (int pb = 0; pb < np; pb += 2) {
+      const int part = pb + (lane >> 5);
       uint64_t f = 0ull;
-      if (part < np) {
-        const uint64_t raw = rec[sh.part_u0[part]].keys[k];
+      if (part < np && !((unsafe >> part) & 1ull)) {
+        const uint64_t raw = rec[part_u0[part]].keys[lane & 31];
         if (raw != 0ull) f = final_key(raw, L);
       }
-      batch[tid] = f;
-      fold_batch(batch, top, lane, w);
+      top = merge_top32(top, sort64_desc(f, lane), lane);
     }
-    // ---- guard, one lane per part (wave 0 holds the K-th key)
-    if (w == 0) {
-      const uint64_t FK = readlane64(top, Keff - 1);
-      const uint32_t vK = (uint32_t)(FK >> 32);
-      bool bad = false;
-      if (lane < np) {
-        const PartRecord& r = rec[sh.part_u0[lane]];
-        if (!(r.flags & kRecComplete)) {
-          const uint64_t c = r.keys[kKeep - 1];
-          const float xc = key_value(c);
-          bool ok = final_key(c, L) <= FK;
-          if (ok && xc != kNegInf) ok = ukey32(reported(E::pred(xc), L)) < vK;
-          bad = !ok;
-        }
-      }
-      const uint64_t m = __ballot(bad);
-      if (lane == 0) {
-        sh.unsafe_any = m != 0ull;
-        batch[kMergeBlock] = m;
-        batch[kMergeBlock + 1] = FK;
-      }
-    }
-    __syncthreads();
-    if (sh.unsafe_any) {
-      // Rebuild from the safe parts' candidates plus every lane of each
-      // unsafe part whose final key reaches FK.
-      const uint64_t unsafe = batch[kMergeBlock];
-      const uint64_t FK = batch[kMergeBlock + 1];
-      top = 0ull;
-      for (int pb = 0; pb < np; pb += kMergeBlock / kKeep) {
-        const int part = pb + (tid >> 5), k = tid & 31;
+    for (int part = 0; part < np; ++part) {
+      if (!((unsafe >> part) & 1ull)) continue;
+      const int lo = part_u0[part] * kUnitElems;
+      int hi = part_u0[part + 1] * kUnitElems;
+      hi = hi < V ? hi : V;
+      for (int b = lo; b < hi; b += 64) {
+        const int i = b + lane;
         uint64_t f = 0ull;
-        if (part < np && !((unsafe >> part) & 1ull)) {
-          const uint64_t raw = rec[sh.part_u0[part]].keys[k];
-          if (raw != 0ull) f = final_key(raw, L);
+        if (i < hi) {
+          f = make_key(reported(load_elem<DT>(rowp, i), L), (uint32_t)i);
+          if (f < FK) f = 0ull;
         }
-        batch[tid] = f;
-        fold_batch(batch, top, lane, w);
+        if (__ballot(f != 0ull) != 0ull) top = merge_top32(top, sort64_desc(f, lane), lane);
       }
-      for (int part = 0; part < np; ++part) {
-        if (!((unsafe >> part) & 1ull)) continue;
-        const int64_t lo = (int64_t)sh.part_u0[part] * kUnitElems;
-        int64_t hi = (int64_t)sh.part_u0[part + 1] * kUnitElems;
-        hi = hi < V ? hi : V;
-        for (int64_t b = lo; b < hi; b += kMergeBlock) {
-          const int64_t i = b + tid;
-          uint64_t f = 0ull;
-          if (i < hi) {
-            f = make_key(reported(load_elem<DT>(rowp, i), L), (uint32_t)i);
-            if (f < FK) f = 0ull;
-          }
-          batch[tid] = f;
-          fold_batch(batch, top, lane, w);
-        }
-      }
-    }
-    if (w == 0 && lane < K) {
-      int32_t id = -1;
-      uint32_t bits = kNanBits;
-      if (lane < Keff) {
-        id = (int32_t)key_id(top);
-        bits = __float_as_uint(unkey32((uint32_t)(top >> 32)));
-      }
-      *(int2*)(out + 2 + 2 * lane) = make_int2(id, (int32_t)bits);
     }
   }
-}
-
-// One workgroup per physical row; rows outside the committed prefix exit.
-template <int DT>
-__global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
-  __shared__ MergeSmem sh;
-  extern __shared__ int prefix[];
-  const int total = build_prefix<kMergeWaves>(p, prefix, sh.scan);
-  const int row = blockIdx.x;
-  const int s = row / p.T, t = row - s * p.T;
-  if (t >= slot_rows(p, s)) return;
-  int n_sel = p.id_counts[s];
-  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
-  merge_row<DT>(p, sh, (int64_t)total * p.units, row, prefix[s] + t, s, n_sel,
-                p.K > 0 && n_sel == 0);
+  if (lane < K) {
+    int32_t id = -1;
+    uint32_t bits = kNanBits;
+    if (lane < Keff) {
+      id = (int32_t)key_id(top);
+      bits = __float_as_uint(unkey32((uint32_t)(top >> 32)));
+    }
+    *(int2*)(out + 2 + 2 * lane) = make_int2(id, (int32_t)bits);
+  }
 }
 
 // ================================================================== reduce
 constexpr int kWaves = kBlock / 64;  // 4 waves share each unit
 constexpr int kStash = 64;           // hot chunks a wave can stash per unit
-constexpr int kCompactAt = 56;       // pool size that triggers a compaction
 
 struct ReduceSmem {
-  uint64_t pool[kWaves][kWavePool];  // per-wave candidate pools
-  uint4 stash[kWaves][kStash];       // hot chunks of the unit being reduced
-  int16_t stash_off[kWaves][kStash]; // their chunk index c * 64 + lane
-  uint64_t qbar[kWaves];             // each wave's 8th-best key of its part (0: none)
-  float tw[kWaves];                  // first-unit thresholds of the waves
-  float wm[kWaves];                  // a part's per-wave max and scaled sum
-  float ws[kWaves];
+  uint64_t pool[kWaves][kCandBuf];       // per-wave candidate buffers
+  uint64_t flush_keys[2][kWaves][kKeep]; // a part's sorted best 32 per wave, by part parity
+  uint4 stash[kWaves][kStash];           // hot chunks of the unit being reduced
+  int16_t stash_off[kWaves][kStash];     // their chunk index c * 64 + lane
+  uint64_t qbar[kWaves];                 // each wave's published 8th-best key (see pub_key)
+  float wm[2][kWaves];                   // a part's per-wave max and scaled sum
+  float ws[2][kWaves];
+  int arrive[2];                         // waves that flushed the part of this parity
+  int merged;                            // parts of the range merged into records
   int scan[kWaves];
 };
+
+// A published 8th-best key carries the number of the part it belongs to, so
+// a wave never reads another part's bar: (value key << 32) | (part mod 4096)
+// << 20 | ID, with IDs below 2^20 (at most 64 units of 16,384 lanes).
+__device__ __forceinline__ uint64_t pub_key(uint64_t key, int part) {
+  return (key & 0xFFFFFFFF00000000ull) | ((uint64_t)(part & 0xFFF) << 20) |
+         (uint64_t)(key_id(key) & 0xFFFFFu);
+}
+// The key published for `part`, or 0.
+__device__ __forceinline__ uint64_t pub_read(uint64_t pub, int part) {
+  if (pub == 0ull || (int)((pub >> 20) & 0xFFF) != (part & 0xFFF)) return 0ull;
+  return (pub & 0xFFFFFFFF00000000ull) | (uint64_t)(~(uint32_t)(pub & 0xFFFFFu));
+}
 
 // Where a unit sits: active row a, unit u of that row, slot s, logit row.
 struct UnitPos {
@@ -752,8 +746,8 @@ __device__ __forceinline__ PassOut unit_pass(uint4 (&raw)[kChunks], float (&cm)[
 
 // Expand the stashed chunks one lane per element into the pool.
 template <int DT>
-__device__ __forceinline__ void expand_stash(WavePool& wp, const Stage& st, int64_t wave_base,
-                                             int V, int lane, const Admit& ad) {
+__device__ __forceinline__ void expand_stash(CandBuf& cb, Best32& best, const Stage& st,
+                                             int64_t wave_base, int V, int lane, const Admit& ad) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   wave_sync();
@@ -770,7 +764,7 @@ __device__ __forceinline__ void expand_stash(WavePool& wp, const Stage& st, int6
       const uint64_t key = make_key(x, (uint32_t)id);
       if (id < V && admitted(ad, x, key)) k = key;
     }
-    pool_append(wp, k, lane);
+    cand_append(cb, best, k, lane);
   }
   wave_sync();  // the next unit may overwrite the stash
 }
@@ -780,8 +774,8 @@ __device__ __forceinline__ void expand_stash(WavePool& wp, const Stage& st, int6
 // per lane per step keeps the register footprint small; the next chunk's
 // load is in flight while a chunk is expanded.
 template <int DT, bool VEC>
-__device__ __forceinline__ void expand_global(WavePool& wp, const char* rowp, int64_t wave_base, int V,
-                                           int lane, const Admit& ad) {
+__device__ __forceinline__ void expand_global(CandBuf& cb, Best32& best, const char* rowp,
+                                              int64_t wave_base, int V, int lane, const Admit& ad) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   uint4 r = load_chunk<DT, VEC>(rowp, wave_base + (int64_t)lane * kPer, V);
@@ -793,7 +787,7 @@ __device__ __forceinline__ void expand_global(WavePool& wp, const char* rowp, in
     for (int j = 0; j < kPer; ++j) {
       const float x = E::get(cur, j);
       const uint64_t key = make_key(x, (uint32_t)(first + j));
-      pool_append(wp, (first + j < V && admitted(ad, x, key)) ? key : 0ull, lane);
+      cand_append(cb, best, (first + j < V && admitted(ad, x, key)) ? key : 0ull, lane);
     }
   }
 }
@@ -828,12 +822,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = p.V, U = p.units;
   if (tid < kWaves) sh.qbar[tid] = 0ull;  // ordered by the barriers below
+  if (tid < 2) sh.arrive[tid] = 0;
+  if (tid == 0) sh.merged = 0;
   const int total = build_prefix<kWaves>(p, prefix, sh.scan);
   // This workgroup's range of the N < 2^31 units (the host checks N).
   const int64_t N = (int64_t)total * U;
   const int x0 = (int)((int64_t)blockIdx.x * N / p.workers);
   const int x1 = (int)(((int64_t)blockIdx.x + 1) * N / p.workers);
   if (x0 >= x1) return;
+  // Mark which of the range's units begins it, for the merge.
+  for (int x = x0 + tid; x < x1; x += kBlock) p.unit_start[x] = x == x0 ? 1 : 0;
 
   UnitPos cur = locate<DT>(p, prefix, x0);
   int part_u0 = cur.u;
@@ -854,12 +852,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   // lane's values except one occurrence of m_l (whose term is exactly 1 and
   // is added back when the lanes are combined).
   float m_l = kNegInf, s_l = 0.0f;
-  WavePool wp{&sh.pool[w][0], 0, false, 0ull, 0ull};
+  Best32 best{0ull, 0, 0ull};
+  CandBuf cb{&sh.pool[w][0], 0};
   Stage st{&sh.stash[w][0], &sh.stash_off[w][0], 0};
   uint64_t published = 0ull;
-  // Value bar of the part's first unit as a key: a later lane passes it iff
-  // its value is strictly larger (0: no such bar).
-  uint64_t first_bar = 0ull;
+  int part_seq = 0;  // parts of the range finished by this wave
 
   for (int x = x0; x < x1; ++x) {
     const int lane = opaque_lane(lane_id);
@@ -876,22 +873,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     const bool interior = wave_base + kWaveElems <= V;
     const bool next_interior = next_base + kWaveElems <= V;
 
-    // ---- admission bar known before the pass: the part's first-unit value
-    // bar, the wave's own 32nd-best key, and the smallest of the four
-    // published 8th-best keys (32 keys of the part lie at or above it).
+    // ---- admission bar known before the pass: the wave's own 32nd-best
+    // key, or the smallest of the four waves' published 8th-best keys of
+    // this part (32 keys of the part lie at or above it), the larger.
     Admit ad{false, 0ull, kNegInf};
     float tau = kNegInf;
     bool strict = false;
     if (natural && !part_starts) {
-      uint64_t bq = lds_load64(&sh.qbar[0]);
+      uint64_t bq = pub_read(lds_load64(&sh.qbar[0]), part_seq);
 #pragma unroll
       for (int i = 1; i < kWaves; ++i) {
-        const uint64_t b = lds_load64(&sh.qbar[i]);
+        const uint64_t b = pub_read(lds_load64(&sh.qbar[i]), part_seq);
         bq = b < bq ? b : bq;
       }
-      uint64_t bar = wp.have_bar ? wp.bar : 0ull;
+      uint64_t bar = best.bar;
       bar = bq > bar ? bq : bar;
-      bar = first_bar > bar ? first_bar : bar;
       bar = readlane64(bar, 0);  // every lane read the same words
       if (bar != 0ull) {
         ad.by_key = true;
@@ -949,28 +945,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // ---- candidates for this wave's pool
     if (natural) {
       if (part_starts) {
-        // The part's first unit, still in registers.  Its threshold T is
-        // the smallest over the workgroup's waves of each wave's k-th
-        // largest lane maximum, k = ceil(32 / waves holding vocabulary):
-        // lane maxima are distinct lanes, so at least 32 lanes of the unit
-        // reach T.  A wave with fewer than k such lanes makes T = -inf.
-        const int ubase = cur.u * kUnitElems;
-        const int nw = V - ubase >= kUnitElems ? kWaves
-                                               : (V - ubase + kWaveElems - 1) / kWaveElems;
-        const int k = (kKeep + nw - 1) / nw;
+        // The part's first unit, still in registers: the threshold is the
+        // wave's 32nd-largest lane maximum (lane maxima are distinct lanes),
+        // or -inf when fewer than 32 lanes hold any of the vocabulary.
         const int rem = V - wave_base;
         const int vl = rem <= 0 ? 0 : (rem >= 64 * kPer ? 64 : (rem + kPer - 1) / kPer);
-        float tw = __builtin_huge_valf();  // waves without vocabulary do not vote
-        if (vl > 0)
-          tw = vl >= k ? key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, k)) : kNegInf;
-        if (lane == 0) sh.tw[w] = tw;
-        __syncthreads();
-        tau = fminf(fminf(sh.tw[0], sh.tw[1]), fminf(sh.tw[2], sh.tw[3]));
-        __syncthreads();  // sh.tw is rewritten at the next part
+        tau = kNegInf;
+        if (vl >= kKeep)
+          tau = key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, kKeep));
         ad.by_key = false;
         ad.tau = tau;
         strict = false;
-        first_bar = tau == kNegInf ? 0ull : ((uint64_t)ukey32(tau) << 32) | 0xFFFFFFFFull;
       }
       if (!roll) {
         // Registers still hold the unit: stash its hot chunks, then start
@@ -988,72 +973,82 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
                                               c, lane, V, next_interior);
         }
       }
-      if (st.n > kStash) expand_global<DT, VEC>(wp, cur.rowp, wave_base, V, lane, ad);
-      else if (st.n > 0) expand_stash<DT>(wp, st, wave_base, V, lane, ad);
-      if (wp.count >= kCompactAt) pool_compact(wp, lane);
-      if (wp.b8 != published) {
-        published = wp.b8;
-        if (lane == 0) lds_store64(&sh.qbar[w], published);
+      if (st.n > kStash) expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
+      else if (st.n > 0) expand_stash<DT>(cb, best, st, wave_base, V, lane, ad);
+      cand_flush(cb, best, lane);
+      const uint64_t b8 = best.n >= 8 ? readlane64(best.top, 7) : 0ull;
+      if (b8 != published) {
+        published = b8;
+        if (lane == 0) lds_store64(&sh.qbar[w], pub_key(published, part_seq));
       }
     }
 
     if (part_ends) {
-      // ---- part record: combine lanes, then waves
+      // ---- this wave's share of the part record, in the buffers of the
+      // part's parity once the part two back has been merged out of them
+      const int b = part_seq & 1;
+      if (part_seq >= 2) {
+        while (__hip_atomic_load(&sh.merged, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+               part_seq - 1)
+          __builtin_amdgcn_s_sleep(2);
+      }
       {
         const float M = wave_max(m_l, lane);
         float term = 0.0f;
         if (m_l != kNegInf) term = (1.0f + s_l) * __builtin_amdgcn_exp2f((m_l - M) * kLog2e);
         const float S = wave_sum(term, lane);
         if (lane == 0) {
-          sh.wm[w] = M;
-          sh.ws[w] = S;
+          sh.wm[b][w] = M;
+          sh.ws[b][w] = S;
         }
       }
-      if (natural) {
-        if (wp.count > 0) pool_compact(wp, lane);
-        if (lane < kKeep && lane >= wp.count) wp.keys[lane] = 0ull;
-      }
-      __syncthreads();
-      if (w == 0) {
+      if (natural && lane < kKeep) sh.flush_keys[b][w][lane] = best.top;
+      // The last wave to arrive merges the four shares into the record.
+      int old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(&sh.arrive[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if (old == kWaves - 1) {
         PartRecord* rec = p.records + (int64_t)cur.row * U + part_u0;
         uint64_t top = 0ull;
         int held = 0;
         if (natural) {
-          top = lane < kKeep ? sh.pool[0][lane] : 0ull;
+          top = lane < kKeep ? sh.flush_keys[b][0][lane] : 0ull;
 #pragma unroll
           for (int i = 1; i < kWaves; ++i)
-            top = merge_top32(top, lane < kKeep ? sh.pool[i][lane] : 0ull, lane);
+            top = merge_top32(top, lane < kKeep ? sh.flush_keys[b][i][lane] : 0ull, lane);
           held = __popcll(__ballot(lane < kKeep && top != 0ull));
         }
         if (lane < kKeep) rec->keys[lane] = top;
         if (lane == 0) {
-          float M = sh.wm[0];
-          for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[i]);
+          float M = sh.wm[b][0];
+          for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[b][i]);
           float S = 0.0f;
           if (M != kNegInf)
             for (int i = 0; i < kWaves; ++i)
-              if (sh.wm[i] != kNegInf)
-                S += sh.ws[i] * __builtin_amdgcn_exp2f((sh.wm[i] - M) * kLog2e);
+              if (sh.wm[b][i] != kNegInf)
+                S += sh.ws[b][i] * __builtin_amdgcn_exp2f((sh.wm[b][i] - M) * kLog2e);
           const int lo = part_u0 * kUnitElems;
           const int hi = (cur.u + 1) * kUnitElems < V ? (cur.u + 1) * kUnitElems : V;
           rec->m = M;
           rec->s = S;
           rec->n = held;
           rec->flags = hi - lo <= kKeep ? kRecComplete : 0;
+          p.row_index[cur.row] = cur.a;
+          sh.arrive[b] = 0;
+          __hip_atomic_store(&sh.merged, part_seq + 1, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
         }
       }
-      if (lane == 0) lds_store64(&sh.qbar[w], 0ull);
-      __syncthreads();  // pools, wm/ws and qbar are reused by the next part
+      ++part_seq;
       // ---- next part
       if (has_next) {
         m_l = kNegInf;
         s_l = 0.0f;
-        wp.count = 0;
-        wp.have_bar = false;
-        wp.bar = 0ull;
-        wp.b8 = 0ull;
+        best.top = 0ull;
+        best.n = 0;
+        best.bar = 0ull;
         published = 0ull;
-        first_bar = 0ull;
         part_u0 = nxt.u;
         n_sel = p.id_counts[nxt.s];
         n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
@@ -1072,7 +1067,8 @@ hipError_t launch_typed(const Params& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.capacity * p.T;
-  hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)rows), dim3(kMergeBlock), lds, st, p);
+  hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(kMergeBlock), 0, st, p);
   return hipGetLastError();
 }
 

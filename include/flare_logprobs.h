@@ -92,8 +92,9 @@ typedef struct flare_logprobs_plan {
   uint64_t workspace_bytes; /* bytes of device workspace the caller provides */
   uint64_t record_offset;   /* per-(row, unit) part records */
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
-  uint64_t reserved1;
-  uint32_t reserved[8];
+  uint64_t index_offset;    /* int32[capacity * T]: row order of the reduction */
+  uint64_t start_offset;    /* uint8[capacity * T * units]: unit-range starts */
+  uint32_t reserved[6];
 } flare_logprobs_plan_t;
 
 /*

@@ -50,8 +50,8 @@ def test_abi_version_and_status_strings(flp):
 
 
 def test_plan_struct_layout_matches_header(flp):
-    # 16 int32-sized fields, 4 uint64, 8 reserved uint32
-    assert ctypes.sizeof(flp.PlanStruct) == 16 * 4 + 4 * 8 + 8 * 4
+    # 16 int32-sized fields, 5 uint64, 6 reserved uint32
+    assert ctypes.sizeof(flp.PlanStruct) == 16 * 4 + 5 * 8 + 6 * 4
 
 
 def host_plan(flp, capacity=128, T=8, V=248320, V_pad=248320, dtype=1, K=20):
@@ -66,7 +66,9 @@ def test_plan_host_only_geometry(flp):
     assert p.units == 16 and p.unit_elems == 16384 and p.block == 256 and p.vector_rows == 1
     assert p.cu_count == 256 and p.abi_version == 1 and p.grid == 1024 and p.ranges == 1024
     rows = 128 * 8
-    assert p.lse_offset >= rows * 16 * 272 and p.workspace_bytes >= p.lse_offset + 4 * rows
+    assert p.lse_offset >= rows * 16 * 272 and p.index_offset >= p.lse_offset + 4 * rows
+    assert p.start_offset >= p.index_offset + 4 * rows
+    assert p.workspace_bytes >= p.start_offset + rows * 16
     rc, p = host_plan(flp, capacity=1024, T=4, V=262144, V_pad=262144, dtype=0)
     assert rc == 0 and p.units == 32 and p.unit_elems == 8192
     rc, p = host_plan(flp, V=37, V_pad=41)
