@@ -78,14 +78,18 @@ __device__ __forceinline__ uint64_t final_key(uint64_t raw, float L) {
   return ((uint64_t)ukey32(reported(key_value(raw), L)) << 32) | (raw & 0xFFFFFFFFull);
 }
 
+// Sixteen bytes of one lane as a native vector, so that a chunk stays one
+// register tuple (loads, LDS copies and the ordering asm below take it whole).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------- dtype traits
 template <int DT> struct Elem;
 template <> struct Elem<1> {  // bf16
   static constexpr int kPer = 8;
   static constexpr int kBytes = 2;
   static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
-  __device__ static __forceinline__ float get(const uint4& r, int j) {
-    const uint32_t w = (j >> 1) == 0 ? r.x : (j >> 1) == 1 ? r.y : (j >> 1) == 2 ? r.z : r.w;
+  __device__ static __forceinline__ float get(const u32x4& r, int j) {
+    const uint32_t w = r[j >> 1];
     return __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
   }
   __device__ static __forceinline__ uint32_t load_bits(const char* row, int64_t i) {
@@ -103,8 +107,8 @@ template <> struct Elem<0> {  // fp32
   static constexpr int kPer = 4;
   static constexpr int kBytes = 4;
   static constexpr uint32_t kNegInfWord = 0xFF800000u;
-  __device__ static __forceinline__ float get(const uint4& r, int j) {
-    const uint32_t w = j == 0 ? r.x : j == 1 ? r.y : j == 2 ? r.z : r.w;
+  __device__ static __forceinline__ float get(const u32x4& r, int j) {
+    const uint32_t w = r[j];
     return __uint_as_float(w);
   }
   __device__ static __forceinline__ uint32_t load_bits(const char* row, int64_t i) {
@@ -127,41 +131,35 @@ __device__ __forceinline__ float key_floor16(uint32_t k16) {
 
 // Chunk holding lanes [first, first + kPer) of a row; lanes >= V read -inf.
 template <int DT, bool VEC>
-__device__ __forceinline__ uint4 load_chunk(const char* row, int64_t first, int V) {
+__device__ __forceinline__ u32x4 load_chunk(const char* row, int64_t first, int V) {
   using E = Elem<DT>;
-  uint4 r;
-  r.x = r.y = r.z = r.w = E::kNegInfWord;
+  u32x4 r = {E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord};
   if (first >= V) return r;
   if (VEC) {
-    r = *(const uint4*)(row + first * E::kBytes);
+    r = *(const u32x4*)(row + first * E::kBytes);
     if (first + E::kPer > V) {
       const int nv = (int)(V - first);
-      uint32_t* w = &r.x;
 #pragma unroll
       for (int j = 0; j < E::kPer; ++j) {
         if (j >= nv) {
-          if (DT == 1) {
-            uint32_t& word = w[j >> 1];
-            word = (j & 1) ? ((word & 0x0000FFFFu) | 0xFF800000u) : ((word & 0xFFFF0000u) | 0xFF80u);
-          } else {
-            w[j] = 0xFF800000u;
-          }
+          if (DT == 1)
+            r[j >> 1] = (j & 1) ? ((r[j >> 1] & 0x0000FFFFu) | 0xFF800000u)
+                                : ((r[j >> 1] & 0xFFFF0000u) | 0xFF80u);
+          else
+            r[j] = 0xFF800000u;
         }
       }
     }
   } else {
-    uint32_t* w = &r.x;
 #pragma unroll
     for (int j = 0; j < E::kPer; ++j) {
       const int64_t i = first + j;
       if (i < V) {
         const uint32_t b = E::load_bits(row, i);
-        if (DT == 1) {
-          uint32_t& word = w[j >> 1];
-          word = (j & 1) ? ((word & 0x0000FFFFu) | (b << 16)) : ((word & 0xFFFF0000u) | b);
-        } else {
-          w[j] = b;
-        }
+        if (DT == 1)
+          r[j >> 1] = (j & 1) ? ((r[j >> 1] & 0x0000FFFFu) | (b << 16)) : ((r[j >> 1] & 0xFFFF0000u) | b);
+        else
+          r[j] = b;
       }
     }
   }
@@ -603,9 +601,10 @@ constexpr int kStash = 64;           // hot chunks a wave can stash per unit
 struct ReduceSmem {
   uint64_t pool[kWaves][kCandBuf];       // per-wave candidate buffers
   uint64_t flush_keys[2][kWaves][kKeep]; // a part's sorted best 32 per wave, by part parity
-  uint4 stash[kWaves][kStash];           // hot chunks of the unit being reduced
+  u32x4 stash[kWaves][kStash];           // hot chunks of the unit being reduced
   int16_t stash_off[kWaves][kStash];     // their chunk index c * 64 + lane
   uint64_t qbar[kWaves];                 // each wave's published 8th-best key (see pub_key)
+  float tw[2][kWaves];                   // a part's first-unit thresholds, by part parity
   float wm[2][kWaves];                   // a part's per-wave max and scaled sum
   float ws[2][kWaves];
   int arrive[2];                         // waves that flushed the part of this parity
@@ -648,10 +647,10 @@ __device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, in
 // and slice start are wave-uniform, so the interior load is an SGPR base plus
 // a 32-bit lane offset.
 template <int DT, bool VEC>
-__device__ __forceinline__ uint4 load_lane_chunk(const char* rowp, int64_t wave_base, uint32_t loff,
+__device__ __forceinline__ u32x4 load_lane_chunk(const char* rowp, int64_t wave_base, uint32_t loff,
                                                  int c, int lane, int V, bool interior) {
   using E = Elem<DT>;
-  if (VEC && interior) return *(const uint4*)(rowp + wave_base * E::kBytes + loff);
+  if (VEC && interior) return *(const u32x4*)(rowp + wave_base * E::kBytes + loff);
   return load_chunk<DT, VEC>(rowp, wave_base + (int64_t)(c * 64 + lane) * E::kPer, V);
 }
 
@@ -669,42 +668,121 @@ __device__ __forceinline__ bool admitted(const Admit& ad, float x, uint64_t key)
 // Hot chunks of the current unit, copied to the wave's LDS stash in
 // compacted order (n may exceed kStash: then the stash is incomplete).
 struct Stage {
-  uint4* stash;
+  u32x4* stash;
   int16_t* off;
   int n;
 };
-__device__ __forceinline__ void stage_chunk(Stage& st, const uint4& r, bool hot, int c, int lane) {
+__device__ __forceinline__ void stage_chunk(Stage& st, const u32x4& r, bool hot, int c, int lane) {
   const uint64_t m = __ballot(hot);
   if (m != 0ull) {
     const int n = __popcll(m);
-    if (st.n + n <= kStash && hot) {
-      const int pos = st.n + lanes_below(m);
-      st.stash[pos] = r;
-      st.off[pos] = (int16_t)(c * 64 + lane);
+    if (st.n + n <= kStash) {
+      if (hot) {
+        const int pos = st.n + lanes_below(m);
+        st.stash[pos] = r;
+        st.off[pos] = (int16_t)(c * 64 + lane);
+      }
     }
     st.n += n;
   }
 }
 
+// Record a hot chunk's offset only (its data is read again later).
+__device__ __forceinline__ void stage_offset(Stage& st, bool hot, int c, int lane) {
+  const uint64_t m = __ballot(hot);
+  if (m != 0ull) {
+    const int n = __popcll(m);
+    if (st.n + n <= kStash) {
+      if (hot) st.off[st.n + lanes_below(m)] = (int16_t)(c * 64 + lane);
+    }
+    st.n += n;
+  }
+}
+
+// Chunk test of the stash: a chunk is hot when its maximum exceeds `above`
+// (the threshold itself when equality does not admit, else the float just
+// below it), or, for a -inf threshold that admits equality, whenever it
+// holds vocabulary (its first lane is below vlim, the slice's lane count).
+struct HotTest {
+  float above;
+  bool every_lane;
+  int vlim;
+};
+__device__ __forceinline__ HotTest hot_test(float tau, bool strict, int vlim) {
+  HotTest h{tau, false, vlim};
+  if (!strict) {
+    if (tau == kNegInf) {
+      h.every_lane = true;
+    } else if (tau == 0.0f) {
+      h.above = -__uint_as_float(1u);  // -0 and +0 both admit
+    } else if (tau < __builtin_huge_valf()) {
+      const uint32_t b = __float_as_uint(tau);
+      h.above = __uint_as_float(tau > 0.0f ? b - 1u : b + 1u);
+    } else {
+      h.above = __uint_as_float(0x7F7FFFFFu);
+    }
+  }
+  return h;
+}
+template <int kPer>
+__device__ __forceinline__ bool is_hot(const HotTest& h, float mc, int c, int lane) {
+  return h.every_lane ? (c * 64 + lane) * kPer < h.vlim : mc > h.above;
+}
+
+// Lanes at or past V of the chunk whose first lane is `first` read -inf.
+template <int DT>
+__device__ __forceinline__ u32x4 mask_tail(u32x4 r, int first, int V) {
+#pragma unroll
+  for (int j = 0; j < Elem<DT>::kPer; ++j) {
+    if (first + j >= V) {
+      if (DT == 1)
+        r[j >> 1] = (j & 1) ? ((r[j >> 1] & 0x0000FFFFu) | 0xFF800000u)
+                            : ((r[j >> 1] & 0xFFFF0000u) | 0xFF80u);
+      else
+        r[j] = 0xFF800000u;
+    }
+  }
+  return r;
+}
+
+// Refill chunk c of this lane with the next unit's slice at next_base.  With
+// aligned rows every lane loads unconditionally, so the registers have one
+// definition and the compiler's wait counts stay exact (no copies, no early
+// waits); a lane past V, or every lane when there is no next unit (`live`
+// false), reads the row's first chunk instead, which its wave's lanes share,
+// and is masked or ignored.  Unaligned rows read lane by lane.
+template <int DT, bool VEC>
+__device__ __forceinline__ void refill_chunk(u32x4& r, const char* next_rowp, int next_base, int c,
+                                             int lane, int V, bool live) {
+  using E = Elem<DT>;
+  const int first = next_base + (c * 64 + lane) * E::kPer;
+  if (VEC) {
+    r = *(const u32x4*)(next_rowp + (int64_t)(live && first < V ? first : 0) * E::kBytes);
+  } else if (live) {
+    r = load_chunk<DT, false>(next_rowp, first, V);
+  }
+}
+
 // One unit's statistics pass over a wave's registers: exp2 against the
 // running max (or the unit's first chunk max), lane and chunk maxima on the
-// side.  With ROLL each chunk's registers are refilled with the same chunk of
-// the next unit as soon as they have been used, so a unit's loads are always
-// in flight behind the current unit's arithmetic; with STAGE a chunk whose
-// maximum passes tau is stashed first.
+// side.  Each chunk's registers are refilled with the same chunk of the next
+// unit as soon as they have been used, so a unit's loads are always in
+// flight behind the current unit's arithmetic; with `stage` a chunk whose
+// maximum passes the test is stashed first.
 struct PassOut {
   float acc, lm, mref, nb;
 };
 
-template <int DT, bool VEC, bool ROLL, bool STAGE>
-__device__ __forceinline__ PassOut unit_pass(uint4 (&raw)[kChunks], float (&cm)[kChunks],
-                                             float m_l, const char* next_rowp, int64_t next_base,
-                                             bool next_interior, int V, int lane, float tau,
-                                             bool strict, bool interior, int64_t wave_base,
+template <int DT, bool VEC>
+__device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[kChunks],
+                                             float m_l, bool tail, int wave_base,
+                                             const char* next_rowp, int next_base, bool has_next,
+                                             int V, int lane, bool stage, const HotTest& ht,
                                              Stage& st) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   PassOut o;
+  if (VEC && tail) raw[0] = mask_tail<DT>(raw[0], wave_base + lane * kPer, V);
   float c0 = E::get(raw[0], 0);
 #pragma unroll
   for (int j = 1; j < kPer; ++j) c0 = fmaxf(c0, E::get(raw[0], j));
@@ -716,11 +794,11 @@ __device__ __forceinline__ PassOut unit_pass(uint4 (&raw)[kChunks], float (&cm)[
   for (int c = 0; c < kChunks; ++c) {
     // Empty asm statements only add data dependencies: chunk c is not
     // unpacked before chunk c - 1 is summed, and its registers are refilled
-    // only after it is summed.  Without them the compiler hoists every
-    // unpack (or every refill) and keeps two units live at once.
-    if (c > 0)
-      asm volatile("" : "+v"(raw[c].x), "+v"(raw[c].y), "+v"(raw[c].z), "+v"(raw[c].w)
-                   : "v"(o.acc), "v"(o.lm));
+    // only after their last use, so the refill lands in the same registers.
+    if (c > 0) {
+      asm volatile("" : "+v"(raw[c]) : "v"(o.acc), "v"(o.lm));
+      if (VEC && tail) raw[c] = mask_tail<DT>(raw[c], wave_base + (c * 64 + lane) * kPer, V);
+    }
     float mc = kNegInf;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -730,18 +808,37 @@ __device__ __forceinline__ PassOut unit_pass(uint4 (&raw)[kChunks], float (&cm)[
     }
     cm[c] = mc;
     o.lm = fmaxf(o.lm, mc);
-    if (STAGE) {
-      bool hot = strict ? mc > tau : mc >= tau;
-      if (!interior) hot = hot && wave_base + (int64_t)(c * 64 + lane) * kPer < V;
-      stage_chunk(st, raw[c], hot, c, lane);
-    }
-    if (ROLL) {
-      uint32_t loff = (uint32_t)(c * 1024 + lane * 16);
-      asm volatile("" : "+v"(loff) : "v"(o.acc), "v"(o.lm));
-      raw[c] = load_lane_chunk<DT, VEC>(next_rowp, next_base, loff, c, lane, V, next_interior);
+    if (stage) stage_chunk(st, raw[c], mc > ht.above, c, lane);
+    {
+      int lane_dep = lane;
+      asm volatile("" : "+v"(lane_dep) : "v"(o.acc), "v"(o.lm), "v"(raw[c]));
+      refill_chunk<DT, VEC>(raw[c], next_rowp, next_base, c, lane_dep, V, has_next);
     }
   }
   return o;
+}
+
+// Expand hot chunks of the unit just reduced, named by their stash offsets,
+// reading them again from memory (the registers already hold the next unit).
+template <int DT, bool VEC>
+__device__ __forceinline__ void expand_reload(CandBuf& cb, Best32& best, const Stage& st,
+                                              const char* rowp, int wave_base, int V, int lane,
+                                              const Admit& ad) {
+  using E = Elem<DT>;
+  constexpr int kPer = E::kPer;
+  wave_sync();
+  for (int b = 0; b < st.n; b += 64) {
+    const bool mine = b + lane < st.n;
+    const int first = mine ? wave_base + (int)st.off[b + lane] * kPer : 0;
+    const u32x4 r = mine ? load_chunk<DT, VEC>(rowp, first, V) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const float x = E::get(r, j);
+      const uint64_t key = make_key(x, (uint32_t)(first + j));
+      cand_append(cb, best, (mine && first + j < V && admitted(ad, x, key)) ? key : 0ull, lane);
+    }
+  }
+  wave_sync();
 }
 
 // Expand the stashed chunks one lane per element into the pool.
@@ -778,10 +875,10 @@ __device__ __forceinline__ void expand_global(CandBuf& cb, Best32& best, const c
                                               int64_t wave_base, int V, int lane, const Admit& ad) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
-  uint4 r = load_chunk<DT, VEC>(rowp, wave_base + (int64_t)lane * kPer, V);
+  u32x4 r = load_chunk<DT, VEC>(rowp, wave_base + (int64_t)lane * kPer, V);
   for (int c = 0; c < kChunks; ++c) {
     const int64_t first = wave_base + (int64_t)(c * 64 + lane) * kPer;
-    const uint4 cur = r;
+    const u32x4 cur = r;
     if (c + 1 < kChunks) r = load_chunk<DT, VEC>(rowp, first + 64 * kPer, V);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -790,6 +887,9 @@ __device__ __forceinline__ void expand_global(CandBuf& cb, Best32& best, const c
       cand_append(cb, best, (first + j < V && admitted(ad, x, key)) ? key : 0ull, lane);
     }
   }
+  // Leave no load outstanding, so that the stream's wait counts stay exact
+  // where this rare path rejoins it.
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // The lane index as a value the compiler cannot prove loop-invariant: lane
@@ -835,15 +935,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
   UnitPos cur = locate<DT>(p, prefix, x0);
   int part_u0 = cur.u;
-  uint4 raw[kChunks];
-  {
-    const int wb = cur.u * kUnitElems + w * kWaveElems;
-    const bool interior = wb + kWaveElems <= V;
+  u32x4 raw[kChunks];
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c)
-      raw[c] = load_lane_chunk<DT, VEC>(cur.rowp, wb, (uint32_t)(c * 1024 + lane_id * 16), c,
-                                        lane_id, V, interior);
-  }
+  for (int c = 0; c < kChunks; ++c)
+    refill_chunk<DT, VEC>(raw[c], cur.rowp, cur.u * kUnitElems + w * kWaveElems, c, lane_id, V, true);
   int n_sel = p.id_counts[cur.s];
   n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
   bool natural = p.K > 0 && n_sel == 0;
@@ -857,6 +952,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   Stage st{&sh.stash[w][0], &sh.stash_off[w][0], 0};
   uint64_t published = 0ull;
   int part_seq = 0;  // parts of the range finished by this wave
+  // The part's first-unit threshold as a key bar: a later lane passes it iff
+  // its value is strictly larger (0: none).
+  uint64_t first_bar = 0ull;
 
   for (int x = x0; x < x1; ++x) {
     const int lane = opaque_lane(lane_id);
@@ -870,8 +968,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     const bool part_starts = cur.u == part_u0;
     const int wave_base = cur.u * kUnitElems + w * kWaveElems;
     const int next_base = nxt.u * kUnitElems + w * kWaveElems;
-    const bool interior = wave_base + kWaveElems <= V;
-    const bool next_interior = next_base + kWaveElems <= V;
+    const bool tail = wave_base + kWaveElems > V;  // the slice reaches past V
 
     // ---- admission bar known before the pass: the wave's own 32nd-best
     // key, or the smallest of the four waves' published 8th-best keys of
@@ -880,15 +977,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     float tau = kNegInf;
     bool strict = false;
     if (natural && !part_starts) {
-      uint64_t bq = pub_read(lds_load64(&sh.qbar[0]), part_seq);
+      // Every lane reads the same words; decode them as scalars.
+      uint64_t bq = pub_read(readlane64(lds_load64(&sh.qbar[0]), 0), part_seq);
 #pragma unroll
       for (int i = 1; i < kWaves; ++i) {
-        const uint64_t b = pub_read(lds_load64(&sh.qbar[i]), part_seq);
+        const uint64_t b = pub_read(readlane64(lds_load64(&sh.qbar[i]), 0), part_seq);
         bq = b < bq ? b : bq;
       }
       uint64_t bar = best.bar;
       bar = bq > bar ? bq : bar;
-      bar = readlane64(bar, 0);  // every lane read the same words
+      bar = first_bar > bar ? first_bar : bar;
       if (bar != 0ull) {
         ad.by_key = true;
         ad.bar = bar;
@@ -898,20 +996,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         strict = key_id(bar) < (uint32_t)wave_base;
       }
     }
-    const bool roll = has_next && (!natural || ad.by_key);
+    const int vlim = V - wave_base <= 0 ? 0 : (V - wave_base < kWaveElems ? V - wave_base : kWaveElems);
+    HotTest ht = hot_test(tau, strict, vlim);
+    // Stash while streaming only with a bar that a chunk maximum can test.
+    const bool stage = natural && ad.by_key && !ht.every_lane;
 
     st.n = 0;
     float cm[kChunks];
-    PassOut po;
-    if (!roll)
-      po = unit_pass<DT, VEC, false, false>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V,
-                                            lane, tau, strict, interior, wave_base, st);
-    else if (natural)
-      po = unit_pass<DT, VEC, true, true>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V,
-                                          lane, tau, strict, interior, wave_base, st);
-    else
-      po = unit_pass<DT, VEC, true, false>(raw, cm, m_l, nxt.rowp, next_base, next_interior, V,
-                                           lane, tau, strict, interior, wave_base, st);
+    const PassOut po = unit_pass<DT, VEC>(raw, cm, m_l, tail, wave_base, nxt.rowp, next_base,
+                                          has_next, V, lane, stage, ht, st);
     const float lm = po.lm;
 
     // ---- fold the unit into the lane's running (max, sum)
@@ -924,7 +1017,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         nbr = -lm * kLog2e;
         acc = 0.0f;
         for (int c = 0; c < kChunks; ++c) {
-          const uint4 r2 =
+          const u32x4 r2 =
               load_chunk<DT, VEC>(cur.rowp, wave_base + (int64_t)(c * 64 + lane) * kPer, V);
 #pragma unroll
           for (int j = 0; j < kPer; ++j)
@@ -945,36 +1038,38 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // ---- candidates for this wave's pool
     if (natural) {
       if (part_starts) {
-        // The part's first unit, still in registers: the threshold is the
-        // wave's 32nd-largest lane maximum (lane maxima are distinct lanes),
-        // or -inf when fewer than 32 lanes hold any of the vocabulary.
-        const int rem = V - wave_base;
-        const int vl = rem <= 0 ? 0 : (rem >= 64 * kPer ? 64 : (rem + kPer - 1) / kPer);
-        tau = kNegInf;
-        if (vl >= kKeep)
-          tau = key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, kKeep));
+        // The part's first unit.  Its threshold is the smallest over the
+        // workgroup's waves of each wave's k-th largest lane maximum,
+        // k = ceil(32 / waves holding vocabulary): lane maxima are distinct
+        // lanes, so at least 32 lanes of the unit reach it.  A wave with
+        // fewer than k such lanes makes it -inf.  The registers already
+        // hold the next unit, so the hot chunks are read again.
+        const int ubase = cur.u * kUnitElems;
+        const int nw = V - ubase >= kUnitElems ? kWaves : (V - ubase + kWaveElems - 1) / kWaveElems;
+        const int k = (kKeep + nw - 1) / nw;
+        const int vl = vlim <= 0 ? 0 : (vlim + kPer - 1) / kPer < 64 ? (vlim + kPer - 1) / kPer : 64;
+        float tw = __builtin_huge_valf();  // a wave without vocabulary does not vote
+        if (vl > 0)
+          tw = vl >= k ? key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, k)) : kNegInf;
+        const int par = part_seq & 1;
+        if (lane == 0) sh.tw[par][w] = tw;
+        __syncthreads();
+        tau = fminf(fminf(sh.tw[par][0], sh.tw[par][1]), fminf(sh.tw[par][2], sh.tw[par][3]));
         ad.by_key = false;
         ad.tau = tau;
-        strict = false;
-      }
-      if (!roll) {
-        // Registers still hold the unit: stash its hot chunks, then start
-        // loading the next unit.
+        ht = hot_test(tau, false, vlim);
+        first_bar = tau == kNegInf ? 0ull : ((uint64_t)ukey32(tau) << 32) | 0xFFFFFFFFull;
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-          bool hot = strict ? cm[c] > tau : cm[c] >= tau;
-          if (!interior) hot = hot && wave_base + (c * 64 + lane) * kPer < V;
-          stage_chunk(st, raw[c], hot, c, lane);
-        }
-        if (has_next) {
-#pragma unroll
-          for (int c = 0; c < kChunks; ++c)
-            raw[c] = load_lane_chunk<DT, VEC>(nxt.rowp, next_base, (uint32_t)(c * 1024 + lane * 16),
-                                              c, lane, V, next_interior);
-        }
+        for (int c = 0; c < kChunks; ++c) stage_offset(st, is_hot<kPer>(ht, cm[c], c, lane), c, lane);
+        if (st.n > kStash) expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
+        else if (st.n > 0) expand_reload<DT, VEC>(cb, best, st, cur.rowp, wave_base, V, lane, ad);
+      } else if (!stage || st.n > kStash) {
+        // No bar a chunk maximum can test, or more hot chunks than the stash
+        // holds: every lane of the slice, read again.
+        expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
+      } else if (st.n > 0) {
+        expand_stash<DT>(cb, best, st, wave_base, V, lane, ad);
       }
-      if (st.n > kStash) expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
-      else if (st.n > 0) expand_stash<DT>(cb, best, st, wave_base, V, lane, ad);
       cand_flush(cb, best, lane);
       const uint64_t b8 = best.n >= 8 ? readlane64(best.top, 7) : 0ull;
       if (b8 != published) {
@@ -1049,6 +1144,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         best.n = 0;
         best.bar = 0ull;
         published = 0ull;
+        first_bar = 0ull;
         part_u0 = nxt.u;
         n_sel = p.id_counts[nxt.s];
         n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
