@@ -51,6 +51,8 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   if (units > flp::kMaxUnits) return FLARE_ERR_UNSUPPORTED_SIZE;
   if (rows * units > (int64_t)0x7FFFFFFF) return FLARE_ERR_UNSUPPORTED_SIZE;
   const bool vec = ((int64_t)V_pad * flp::elem_bytes(dtype)) % 16 == 0;
+  // Row byte offsets inside a buffer resource are 32-bit.
+  if ((int64_t)V_pad * flp::elem_bytes(dtype) > (int64_t)0x7FFFFFFF) return FLARE_ERR_UNSUPPORTED_SIZE;
 
   int32_t cus = 256, per_cu = 4;
   if (device >= 0) {

@@ -745,19 +745,26 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 r, int first, int V) {
   return r;
 }
 
+// A buffer resource over one logit row: loads past its `bytes` return zero
+// without touching memory (the hardware range check covers the per-lane
+// offset).  bytes = 0 makes every load a no-op.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const char* rowp, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)rowp, (short)0, bytes, 0x00020000);
+}
+
 // Refill chunk c of this lane with the next unit's slice at next_base.  With
-// aligned rows every lane loads unconditionally, so the registers have one
-// definition and the compiler's wait counts stay exact (no copies, no early
-// waits); a lane past V, or every lane when there is no next unit (`live`
-// false), reads the row's first chunk instead, which its wave's lanes share,
-// and is masked or ignored.  Unaligned rows read lane by lane.
+// aligned rows every lane issues the same buffer load unconditionally, so the
+// registers have one definition and the compiler's wait counts stay exact
+// (no copies, no early waits); lanes past the row read zeros and are masked
+// when the unit is reduced.  Unaligned rows read lane by lane.
 template <int DT, bool VEC>
-__device__ __forceinline__ void refill_chunk(u32x4& r, const char* next_rowp, int next_base, int c,
-                                             int lane, int V, bool live) {
+__device__ __forceinline__ void refill_chunk(u32x4& r, __amdgpu_buffer_rsrc_t rsrc,
+                                             const char* next_rowp, int next_base, int c, int lane,
+                                             int V, bool live) {
   using E = Elem<DT>;
   const int first = next_base + (c * 64 + lane) * E::kPer;
   if (VEC) {
-    r = *(const u32x4*)(next_rowp + (int64_t)(live && first < V ? first : 0) * E::kBytes);
+    r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, first * E::kBytes, 0, 0));
   } else if (live) {
     r = load_chunk<DT, false>(next_rowp, first, V);
   }
@@ -776,6 +783,7 @@ struct PassOut {
 template <int DT, bool VEC>
 __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[kChunks],
                                              float m_l, bool tail, int wave_base,
+                                             __amdgpu_buffer_rsrc_t next_rsrc,
                                              const char* next_rowp, int next_base, bool has_next,
                                              int V, int lane, bool stage, const HotTest& ht,
                                              Stage& st) {
@@ -812,7 +820,7 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
     {
       int lane_dep = lane;
       asm volatile("" : "+v"(lane_dep) : "v"(o.acc), "v"(o.lm), "v"(raw[c]));
-      refill_chunk<DT, VEC>(raw[c], next_rowp, next_base, c, lane_dep, V, has_next);
+      refill_chunk<DT, VEC>(raw[c], next_rsrc, next_rowp, next_base, c, lane_dep, V, has_next);
     }
   }
   return o;
@@ -935,10 +943,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
   UnitPos cur = locate<DT>(p, prefix, x0);
   int part_u0 = cur.u;
+  const int row_bytes = (int)(p.V_pad * E::kBytes);
   u32x4 raw[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c)
-    refill_chunk<DT, VEC>(raw[c], cur.rowp, cur.u * kUnitElems + w * kWaveElems, c, lane_id, V, true);
+    refill_chunk<DT, VEC>(raw[c], row_rsrc(cur.rowp, row_bytes), cur.rowp,
+                          cur.u * kUnitElems + w * kWaveElems, c, lane_id, V, true);
   int n_sel = p.id_counts[cur.s];
   n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
   bool natural = p.K > 0 && n_sel == 0;
@@ -1003,8 +1013,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
     st.n = 0;
     float cm[kChunks];
-    const PassOut po = unit_pass<DT, VEC>(raw, cm, m_l, tail, wave_base, nxt.rowp, next_base,
-                                          has_next, V, lane, stage, ht, st);
+    const PassOut po =
+        unit_pass<DT, VEC>(raw, cm, m_l, tail, wave_base, row_rsrc(nxt.rowp, has_next ? row_bytes : 0),
+                           nxt.rowp, next_base, has_next, V, lane, stage, ht, st);
     const float lm = po.lm;
 
     // ---- fold the unit into the lane's running (max, sum)
