@@ -797,14 +797,13 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
   o.mref = fmaxf(m_l, c0);
   o.nb = -o.mref * kLog2e;
   o.acc = 0.0f;
-  o.lm = kNegInf;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     // Empty asm statements only add data dependencies: chunk c is not
     // unpacked before chunk c - 1 is summed, and its registers are refilled
     // only after their last use, so the refill lands in the same registers.
     if (c > 0) {
-      asm volatile("" : "+v"(raw[c]) : "v"(o.acc), "v"(o.lm));
+      asm volatile("" : "+v"(raw[c]) : "v"(o.acc), "v"(cm[c - 1]));
       if (VEC && tail) raw[c] = mask_tail<DT>(raw[c], wave_base + (c * 64 + lane) * kPer, V);
     }
     float mc = kNegInf;
@@ -815,14 +814,16 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
       o.acc += __builtin_amdgcn_exp2f(__builtin_fmaf(xv, kLog2e, o.nb));
     }
     cm[c] = mc;
-    o.lm = fmaxf(o.lm, mc);
     if (stage) stage_chunk(st, raw[c], mc > ht.above, c, lane);
     {
       int lane_dep = lane;
-      asm volatile("" : "+v"(lane_dep) : "v"(o.acc), "v"(o.lm), "v"(raw[c]));
+      asm volatile("" : "+v"(lane_dep) : "v"(o.acc), "v"(mc), "v"(raw[c]));
       refill_chunk<DT, VEC>(raw[c], next_rsrc, next_rowp, next_base, c, lane_dep, V, has_next);
     }
   }
+  // The lane maximum from the chunk maxima (max3 chains, no per-chunk update).
+  o.lm = fmaxf(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])),
+               fmaxf(fmaxf(cm[4], cm[5]), fmaxf(cm[6], cm[7])));
   return o;
 }
 
@@ -908,6 +909,19 @@ __device__ __forceinline__ int opaque_lane(int lane) {
   return lane;
 }
 
+// Issue priority 3 - q for a workgroup in quarter q of its unit range.  The
+// wave arbiter of a CU favours the oldest waves, so with equal priorities
+// the workgroups dispatched first race through their ranges while the
+// youngest lag and set the end of the launch; lowering the priority as a
+// range is consumed hands issue slots to the workgroups that are behind.
+__device__ __forceinline__ void progress_priority(int done, int count) {
+  const int q = (int)(((int64_t)done * 4) / count);
+  if (q == 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ uint64_t lds_load64(const uint64_t* a) {
   return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -967,6 +981,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   uint64_t first_bar = 0ull;
 
   for (int x = x0; x < x1; ++x) {
+    progress_priority(x - x0, x1 - x0);
     const int lane = opaque_lane(lane_id);
     const bool has_next = x + 1 < x1;
     UnitPos nxt = cur;
