@@ -9,14 +9,19 @@ never read), K=20 natural alternatives.  Inputs are seeded synthetic logits
 copies of the logits keep the 256 MB Infinity Cache from serving repeats.
 
 Prints one JSON line: rows/s over the whole timed region, the roofline of the
-reduction launch (algorithmic bytes / mean launch time, from HIP events on the
-launch stream), and the CPU oracle timed on a bounded sample of the same rows.
+reduction launch (algorithmic bytes / its mean duration, from HIP events around
+that launch on the launch stream), and the CPU oracle timed on a bounded sample
+of the same rows.  The HBM traffic of the reduction launch comes from the
+rocprofv3 counter summary under profiles/, and only while the kernel source is
+the one those counters were taken on.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,6 +29,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+KERNEL_SOURCES = ("full_vocab_logprob_amd/csrc/flp_kernels.hip",
+                  "full_vocab_logprob_amd/csrc/flp_internal.h")
+TRAFFIC_SUMMARY = "profiles/reduce_kernel_speculative_verify_bf16_K20.txt"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str):
+    """HBM bytes per reduction launch from the committed counter summary, or
+    None when the summary is missing, covers another workload, or was taken
+    on a different kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, flags=re.M))
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if fields.get("workload") != config:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -86,8 +121,9 @@ def main():
     out = plan.new_out(int(synth.POISON))
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        plan.run(copies[i % len(copies)], tokens, emitted, requested, id_counts, ids, out, ws)
+    def step(i, phase="all"):
+        plan.run(copies[i % len(copies)], tokens, emitted, requested, id_counts, ids, out, ws,
+                 phase=phase)
 
     for i in range(args.warmup):
         step(i)
@@ -110,30 +146,41 @@ def main():
             assert np.all((d <= 2e-5) | (g_[1::2] == words[1::2])), f"values differ on row {r}"
             checked += 1
 
-    # Timed region: K steps between synchronizations; per-launch HIP events
-    # on the launch stream give the kernel's mean duration.
+    # Timed region 1: K whole calls back to back between synchronizations,
+    # events only at its ends: the throughput.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step(args.warmup + i)
-        ev[i][1].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    mean_launch_ms = sum(launch_ms) / K
-    med_launch_ms = launch_ms[K // 2]
     ms_per_step = total_ms / K
     rows_per_s = active * K / (total_ms / 1e3)
-    achieved_gbps = algo_bytes / (mean_launch_ms / 1e3) / 1e9
+
+    # Timed region 2: the same K calls made as their two launches, with an
+    # event pair around each launch on the launch stream: the reduction
+    # kernel's mean duration (the roofline) and the merge's.
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(args.warmup + i, "reduce")
+        ev[i][1].record(stream)
+        step(args.warmup + i, "merge")
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    reduce_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    merge_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    mean_reduce_ms = sum(reduce_ms) / K
+    mean_merge_ms = sum(merge_ms) / K
+    achieved_gbps = algo_bytes / (mean_reduce_ms / 1e3) / 1e9
+    traffic = measured_traffic(spec.name)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -177,10 +224,12 @@ def main():
                                f"{'bf16' if bf16 else 'fp32'}, emitted 1..{spec.T}, K={spec.K}",
                    "active_rows": active, "capacity": spec.capacity, "T": spec.T, "V": spec.V,
                    "K": spec.K, "copies": len(copies), "oracle_rows_checked": checked},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbps, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved_gbps / PEAK_HBM_GBPS, "traffic": None},
-        "launch_ms": {"mean": mean_launch_ms, "median": med_launch_ms,
-                      "p10": launch_ms[K // 10], "p90": launch_ms[(9 * K) // 10]},
+        "roofline": {"bound": "hbm", "kernel": "reduce_kernel", "achieved": achieved_gbps,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic},
+        "reduce_ms": {"mean": mean_reduce_ms, "median": reduce_ms[K // 2],
+                      "p10": reduce_ms[K // 10], "p90": reduce_ms[(9 * K) // 10]},
+        "merge_ms": {"mean": mean_merge_ms, "median": merge_ms[K // 2]},
         "algorithmic_bytes_per_launch": algo_bytes,
         "wall_s": wall,
         "cpu_baseline": cpu,

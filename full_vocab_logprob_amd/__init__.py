@@ -9,7 +9,8 @@ shared library is missing the import of a binding function raises.
     ws = plan.workspace()
     plan.run(logits, tokens, emitted_counts, requested, id_counts, ids, out, ws)
 
-The functions ``flare_logprobs_plan``, ``flare_logprobs_run``,
+The functions ``flare_logprobs_plan``, ``flare_logprobs_run`` (and its two
+launches ``flare_logprobs_reduce`` and ``flare_logprobs_merge``),
 ``flare_status_string`` and ``flare_logprobs_abi_version`` mirror the C entry
 points one to one.
 """
@@ -71,11 +72,12 @@ def lib() -> ctypes.CDLL:
         L.flare_logprobs_plan.restype = c.c_int
         L.flare_logprobs_plan.argtypes = [c.POINTER(PlanStruct), c.c_int32, c.c_int32, c.c_int32,
                                           c.c_int32, c.c_int32, c.c_int32, c.c_int32]
-        L.flare_logprobs_run.restype = c.c_int
-        L.flare_logprobs_run.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64,
-                                         c.c_int32, c.c_int32, c.c_void_p, c.c_void_p,
-                                         c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32,
-                                         c.c_void_p, c.c_void_p, c.c_void_p]
+        for name in ("flare_logprobs_run", "flare_logprobs_reduce", "flare_logprobs_merge"):
+            f = getattr(L, name)
+            f.restype = c.c_int
+            f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
+                          c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                          c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
         L.flare_status_string.restype = c.c_char_p
         L.flare_status_string.argtypes = [c.c_int]
         L.flare_logprobs_abi_version.restype = c.c_uint32
@@ -124,18 +126,41 @@ def _stream(stream) -> int | None:
     return int(stream)
 
 
+def _call(name: str, plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+          requested, id_counts, ids, emitted_counts, tokens, K: int, out, workspace,
+          stream) -> None:
+    rc = getattr(lib(), name)(ctypes.byref(plan), _ptr(logits), dtype_code(dtype), rows, V,
+                              V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids),
+                              _ptr(emitted_counts), _ptr(tokens), K, _ptr(out),
+                              _ptr(workspace), _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, name)
+
+
 def flare_logprobs_run(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
                        requested, id_counts, ids, emitted_counts, tokens, K: int, out,
                        workspace, stream=None) -> None:
     """Launch one reduction on `stream` (default: torch's current stream).
     Tensor arguments are passed by device pointer; the C library checks the
     scalars against the plan before anything is launched."""
-    rc = lib().flare_logprobs_run(ctypes.byref(plan), _ptr(logits), dtype_code(dtype), rows, V,
-                                  V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids),
-                                  _ptr(emitted_counts), _ptr(tokens), K, _ptr(out),
-                                  _ptr(workspace), _stream(stream))
-    if rc != 0:
-        raise FlareError(rc, "flare_logprobs_run")
+    _call("flare_logprobs_run", plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+          emitted_counts, tokens, K, out, workspace, stream)
+
+
+def flare_logprobs_reduce(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                          requested, id_counts, ids, emitted_counts, tokens, K: int, out,
+                          workspace, stream=None) -> None:
+    """The first launch of flare_logprobs_run (same arguments)."""
+    _call("flare_logprobs_reduce", plan, logits, dtype, rows, V, V_pad, requested, id_counts,
+          ids, emitted_counts, tokens, K, out, workspace, stream)
+
+
+def flare_logprobs_merge(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                         requested, id_counts, ids, emitted_counts, tokens, K: int, out,
+                         workspace, stream=None) -> None:
+    """The second launch of flare_logprobs_run (same arguments, after reduce)."""
+    _call("flare_logprobs_merge", plan, logits, dtype, rows, V, V_pad, requested, id_counts,
+          ids, emitted_counts, tokens, K, out, workspace, stream)
 
 
 def _check(t: torch.Tensor, name: str, dtype, numel: int, device) -> None:
@@ -180,7 +205,11 @@ class Plan:
                           device=self.device)
 
     def run(self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
-            stream=None) -> torch.Tensor:
+            stream=None, phase: str = "all") -> torch.Tensor:
+        """One call: both launches (phase "all"), or only the first ("reduce")
+        or the second ("merge") of them."""
+        fn = {"all": flare_logprobs_run, "reduce": flare_logprobs_reduce,
+              "merge": flare_logprobs_merge}[phase]
         dev = self.device
         rows = self.capacity * self.T
         _check(logits, "logits", self.torch_dtype, rows * self.V_pad, dev)
@@ -191,7 +220,6 @@ class Plan:
         _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
         _check(out, "out", torch.int32, rows * ROW_WORDS, dev)
         _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
-        flare_logprobs_run(self.raw, logits, self.torch_dtype, rows, self.V, self.V_pad,
-                           requested, id_counts, ids, emitted_counts, tokens, self.K, out,
-                           workspace, stream)
+        fn(self.raw, logits, self.torch_dtype, rows, self.V, self.V_pad, requested, id_counts, ids,
+           emitted_counts, tokens, self.K, out, workspace, stream)
         return out

@@ -98,11 +98,14 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   return FLARE_OK;
 }
 
-int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
-                       int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
-                       const int32_t* id_counts, const int32_t* ids,
-                       const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
-                       int32_t* out, void* workspace, void* hip_stream) {
+}  // extern "C"
+
+// Validate one call's arguments against its plan and launch `phases`.
+static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
+                      int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
+                      const int32_t* id_counts, const int32_t* ids,
+                      const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
+                      int32_t* out, void* workspace, void* hip_stream, int phases) {
   if (!plan || !logits || !requested || !id_counts || !ids || !emitted_counts || !tokens ||
       !out || !workspace)
     return FLARE_ERR_INVALID_ARGUMENT;
@@ -138,8 +141,38 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, in
   p.workers = plan->ranges;
 
   const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
-  const int e = flp::launch_reduce(p, dtype, vec, hip_stream);
+  const int e = flp::launch(p, dtype, vec, phases, hip_stream);
   return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
+}
+
+extern "C" {
+
+int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
+                       int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
+                       const int32_t* id_counts, const int32_t* ids,
+                       const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
+                       int32_t* out, void* workspace, void* hip_stream) {
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, K, out, workspace, hip_stream,
+                    flp::kPhaseReduce | flp::kPhaseMerge);
+}
+
+int flare_logprobs_reduce(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
+                          int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
+                          const int32_t* id_counts, const int32_t* ids,
+                          const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
+                          int32_t* out, void* workspace, void* hip_stream) {
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, K, out, workspace, hip_stream, flp::kPhaseReduce);
+}
+
+int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
+                         int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
+                         const int32_t* id_counts, const int32_t* ids,
+                         const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
+                         int32_t* out, void* workspace, void* hip_stream) {
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, K, out, workspace, hip_stream, flp::kPhaseMerge);
 }
 
 }  // extern "C"

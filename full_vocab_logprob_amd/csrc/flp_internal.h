@@ -54,8 +54,11 @@ struct Params {
   int32_t workers;  // workgroups of the persistent launch (one unit range each)
 };
 
+// Launches of one call; `phases` is a mask of kPhaseReduce and kPhaseMerge.
+constexpr int kPhaseReduce = 1;
+constexpr int kPhaseMerge = 2;
 // Launcher implemented in flp_kernels.hip; returns a hipError_t as int.
-int launch_reduce(const Params& p, int dtype, bool vector_rows, void* stream);
+int launch(const Params& p, int dtype, bool vector_rows, int phases, void* stream);
 // Resident reduction workgroups per CU (0 on error).
 int reduce_occupancy(int dtype, bool vector_rows, int capacity);
 size_t prefix_lds_bytes(int capacity);

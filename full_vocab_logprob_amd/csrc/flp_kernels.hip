@@ -1182,12 +1182,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 }
 
 template <int DT, bool VEC>
-hipError_t launch_typed(const Params& p, hipStream_t st) {
-  const size_t lds = prefix_lds_bytes(p.capacity);
-  hipLaunchKernelGGL((reduce_kernel<DT, VEC>), dim3((uint32_t)p.workers), dim3(kBlock), lds, st,
-                     p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
+  if (phases & kPhaseReduce) {
+    const size_t lds = prefix_lds_bytes(p.capacity);
+    hipLaunchKernelGGL((reduce_kernel<DT, VEC>), dim3((uint32_t)p.workers), dim3(kBlock), lds,
+                       st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(phases & kPhaseMerge)) return hipSuccess;
   const int64_t rows = (int64_t)p.capacity * p.T;
   hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)),
                      dim3(kMergeBlock), 0, st, p);
@@ -1215,13 +1218,13 @@ int reduce_occupancy(int dtype, bool vector_rows, int capacity) {
   return e == hipSuccess ? n : 0;
 }
 
-int launch_reduce(const Params& p, int dtype, bool vector_rows, void* stream) {
+int launch(const Params& p, int dtype, bool vector_rows, int phases, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dtype == 1)
-    e = vector_rows ? launch_typed<1, true>(p, st) : launch_typed<1, false>(p, st);
+    e = vector_rows ? launch_typed<1, true>(p, phases, st) : launch_typed<1, false>(p, phases, st);
   else
-    e = vector_rows ? launch_typed<0, true>(p, st) : launch_typed<0, false>(p, st);
+    e = vector_rows ? launch_typed<0, true>(p, phases, st) : launch_typed<0, false>(p, phases, st);
   return (int)e;
 }
 

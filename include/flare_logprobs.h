@@ -135,6 +135,31 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
                        const int32_t* tokens, int32_t K, int32_t* out,
                        void* workspace, void* hip_stream);
 
+/*
+ * The two launches of flare_logprobs_run, for callers that want to order
+ * other work between them or time them apart (design page, tiled-reduction
+ * paragraph: the per-tile statistics and best-key launches, then the final
+ * merge launch).  flare_logprobs_reduce streams the logits once and writes
+ * each part's statistics and best raw keys to the workspace;
+ * flare_logprobs_merge reads them and writes `out` (and each row's L).  Both
+ * take run's arguments and validate them the same way; a merge must follow
+ * its reduce on the same stream with the same arguments and workspace, and
+ * nothing else may use that workspace in between.  Reduce then merge gives
+ * the same frame, bit for bit, as one run.
+ */
+int flare_logprobs_reduce(const flare_logprobs_plan_t* plan, const void* logits,
+                          int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                          const int32_t* requested, const int32_t* id_counts,
+                          const int32_t* ids, const int32_t* emitted_counts,
+                          const int32_t* tokens, int32_t K, int32_t* out,
+                          void* workspace, void* hip_stream);
+int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits,
+                         int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                         const int32_t* requested, const int32_t* id_counts,
+                         const int32_t* ids, const int32_t* emitted_counts,
+                         const int32_t* tokens, int32_t K, int32_t* out,
+                         void* workspace, void* hip_stream);
+
 /* Human-readable name of a flare_status value (static storage). */
 const char* flare_status_string(int status);
 

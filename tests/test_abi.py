@@ -32,8 +32,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"flare_logprobs_plan", "flare_logprobs_run",
-            "flare_status_string", "flare_logprobs_abi_version"} <= set(names)
+    assert {"flare_logprobs_plan", "flare_logprobs_run", "flare_logprobs_reduce",
+            "flare_logprobs_merge", "flare_status_string",
+            "flare_logprobs_abi_version"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(flp):
@@ -93,12 +94,25 @@ def test_plan_null_pointer(flp):
 FAKE = 0x10000  # never dereferenced: every case below fails validation first
 
 
+ENTRY = "flare_logprobs_run"
+
+
+@pytest.fixture(params=["flare_logprobs_run", "flare_logprobs_reduce", "flare_logprobs_merge"],
+                autouse=False)
+def entry(request):
+    """Every call taking run's arguments validates them the same way."""
+    global ENTRY
+    ENTRY = request.param
+    yield request.param
+    ENTRY = "flare_logprobs_run"
+
+
 def run_status(flp, plan, **over):
     args = dict(logits=FAKE, dtype=plan.dtype, rows=plan.capacity * plan.T, V=plan.V,
                 V_pad=plan.V_pad, requested=FAKE, id_counts=FAKE, ids=FAKE, emitted=FAKE,
                 tokens=FAKE, K=plan.K, out=FAKE, workspace=FAKE, stream=None)
     args.update(over)
-    return flp.lib().flare_logprobs_run(
+    return getattr(flp.lib(), ENTRY)(
         ctypes.byref(plan), args["logits"], args["dtype"], args["rows"], args["V"],
         args["V_pad"], args["requested"], args["id_counts"], args["ids"], args["emitted"],
         args["tokens"], args["K"], args["out"], args["workspace"], args["stream"])
@@ -106,7 +120,7 @@ def run_status(flp, plan, **over):
 
 @pytest.mark.parametrize("field", ["logits", "requested", "id_counts", "ids", "emitted",
                                    "tokens", "out", "workspace"])
-def test_run_rejects_null_pointers(flp, field):
+def test_run_rejects_null_pointers(flp, entry, field):
     rc, plan = host_plan(flp)
     assert rc == 0
     assert run_status(flp, plan, **{field: None}) == 1
@@ -114,7 +128,7 @@ def test_run_rejects_null_pointers(flp, field):
 
 @pytest.mark.parametrize("over", [dict(dtype=0), dict(V=1000), dict(V_pad=248321), dict(K=5),
                                   dict(rows=1023)])
-def test_run_rejects_plan_mismatch(flp, over):
+def test_run_rejects_plan_mismatch(flp, entry, over):
     rc, plan = host_plan(flp)
     assert run_status(flp, plan, **over) == 3
 
@@ -128,7 +142,7 @@ def test_run_rejects_bad_dtype_and_stale_plan(flp):
                                         0, FAKE, FAKE, None) == 1
 
 
-def test_run_rejects_corrupt_plan(flp):
+def test_run_rejects_corrupt_plan(flp, entry):
     rc, plan = host_plan(flp)
     plan.ranges = 3
     assert run_status(flp, plan) == 3
@@ -140,7 +154,7 @@ def test_run_rejects_corrupt_plan(flp):
     assert run_status(flp, plan) == 3
 
 
-def test_run_rejects_misaligned_workspace(flp):
+def test_run_rejects_misaligned_workspace(flp, entry):
     rc, plan = host_plan(flp)
     assert run_status(flp, plan, workspace=FAKE + 4) == 1
 

@@ -294,6 +294,30 @@ def test_repeatable_bit_identical():
     assert np.array_equal(a, b) and np.array_equal(la.view(np.int32), lb.view(np.int32))
 
 
+def test_reduce_then_merge_equals_run(oracle_handle):
+    """The two launches called apart, with other stream work between them,
+    give run's frame bit for bit (and the oracle's)."""
+    spec = synth.CONFIGS["C4"].with_(capacity=12, seed=45)
+    w = synth.make(spec)
+    d = H.to_device(w)
+    plan = H.make_plan(spec)
+    announce("reduce + merge vs run C4 cap=12")
+    a, la = H.run_gpu(w, d, plan)
+    ws = plan.workspace()
+    out = plan.new_out(H.POISON)
+    args = (d["logits"], d["tokens"], d["emitted"], d["requested"], d["id_counts"], d["ids"], out,
+            ws)
+    plan.run(*args, phase="reduce")
+    scratch = torch.ones(1 << 20, device=out.device).neg_()  # unrelated work in between
+    plan.run(*args, phase="merge")
+    torch.cuda.synchronize()
+    del scratch
+    b = out.cpu().numpy()
+    assert np.array_equal(a, b)
+    assert np.array_equal(la.view(np.int32), plan.lse(ws).cpu().numpy().view(np.int32))
+    H.compare_words(b, H.oracle_frame(oracle_handle, w), "reduce + merge")
+
+
 def test_hip_graph_replay_matches_eager():
     spec = synth.CONFIGS["C4"].with_(capacity=8, seed=44)
     w = synth.make(spec)
