@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="C3")
     ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--K", type=int, default=None,
+                    help="override the configuration's K (throughput sweeps, e.g. K=0)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--check-rows", type=int, default=4,
@@ -98,6 +100,8 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     spec = synth.CONFIGS[args.config]
+    if args.K is not None:
+        spec = spec.with_(K=args.K)
     bf16 = spec.dtype == synth.BF16
     print(f"[bench] generating {spec.name}: {spec.description}", file=sys.stderr, flush=True)
     w = synth.make(spec)
@@ -138,7 +142,9 @@ def main():
         o = oracle.get()
         for r in act_rows[:: max(1, len(act_rows) // args.check_rows)][: args.check_rows]:
             sl, t = divmod(int(r), spec.T)
-            words, _ = o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, V=spec.V)
+            n_sel = int(np.clip(w.id_counts[sl], 0, 128))
+            sel = w.ids[sl * 128: sl * 128 + n_sel] if n_sel > 0 else None
+            words, _ = o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, sel=sel, V=spec.V)
             g_ = got[sl, t, :len(words)]
             assert np.array_equal(g_[0::2], words[0::2]), f"bench check: ids differ on row {r}"
             d = np.abs(g_[1::2].view(np.float32).astype(np.float64)
@@ -190,7 +196,9 @@ def main():
         c0 = time.perf_counter()
         while n < len(act_rows) and time.perf_counter() - c0 < args.cpu_seconds:
             r = int(act_rows[n])
-            o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, V=spec.V)
+            n_sel = int(np.clip(w.id_counts[r // spec.T], 0, 128))
+            o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, V=spec.V,
+                  sel=w.ids[(r // spec.T) * 128:(r // spec.T) * 128 + n_sel] if n_sel else None)
             n += 1
         dt = time.perf_counter() - c0
         cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",

@@ -379,9 +379,9 @@ __device__ __forceinline__ void cand_append(CandBuf& cb, Best32& b, uint64_t k, 
 
 // ------------------------------------------------------------ row mapping
 __device__ __forceinline__ int slot_rows(const Params& p, int s) {
-  if (p.requested[s] == 0) return 0;
-  const int e = p.emitted[s];
-  return e < 0 ? 0 : (e > p.T ? p.T : e);
+  // Both words are loaded together (one round trip).
+  const int r = p.requested[s], e = p.emitted[s];
+  return r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
 }
 
 // prefix[s] = active rows of slots before s; prefix[capacity] = total.  All
@@ -752,6 +752,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const char* rowp, int
   return __builtin_amdgcn_make_buffer_rsrc((void*)rowp, (short)0, bytes, 0x00020000);
 }
 
+// Cache policy of the stream's loads: streaming (each logit is read once).
+constexpr int kSlc = 2;
+
 // Refill chunk c of this lane with the next unit's slice at next_base.  With
 // aligned rows every lane issues the same buffer load unconditionally, so the
 // registers have one definition and the compiler's wait counts stay exact
@@ -764,7 +767,7 @@ __device__ __forceinline__ void refill_chunk(u32x4& r, __amdgpu_buffer_rsrc_t rs
   using E = Elem<DT>;
   const int first = next_base + (c * 64 + lane) * E::kPer;
   if (VEC) {
-    r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, first * E::kBytes, 0, 0));
+    r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, first * E::kBytes, 0, kSlc));
   } else if (live) {
     r = load_chunk<DT, false>(next_rowp, first, V);
   }
