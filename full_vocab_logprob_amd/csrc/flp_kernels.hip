@@ -361,8 +361,11 @@ __device__ __forceinline__ void cand_flush(CandBuf& cb, Best32& b, int lane) {
   b.bar = b.n >= kKeep ? readlane64(b.top, kKeep - 1) : 0ull;
 }
 
-// Buffer one key per lane (0 = none).
+// Buffer one key per lane (0 = none).  A key at or below the list's 32nd
+// is dropped at once: it can no longer enter the list (a run of equal values,
+// -inf lanes say, then costs one flush instead of one per buffer).
 __device__ __forceinline__ void cand_append(CandBuf& cb, Best32& b, uint64_t k, int lane) {
+  if (k <= b.bar) k = 0ull;
   uint64_t m = __ballot(k != 0ull);
   if (m == 0ull) return;
   int n = __popcll(m);
