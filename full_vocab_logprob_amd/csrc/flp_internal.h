@@ -22,16 +22,18 @@ constexpr int elem_bytes(int dtype) { return dtype == 1 ? 2 : 4; }
 // One part's contribution to a row: a part is the run of consecutive units
 // of one row that one workgroup reduced.  m is the part's max, s the sum of
 // exp(x - m) over its lanes, keys its best raw keys (value, then smaller ID)
-// sorted descending.  Stored at records[row * units + first unit of part].
+// sorted descending, cut a bound on every key it dropped: each lane it did
+// not keep has a raw key <= cut (0: the part kept every lane).  Stored at
+// records[row * units + first unit of part].
 struct PartRecord {
   float m;
   float s;
   int32_t n;      // keys held (kKeep unless the part has fewer lanes)
-  int32_t flags;  // kRecComplete: every lane of the part is held
+  int32_t flags;  // reserved (0)
+  uint64_t cut;
   uint64_t keys[kKeep];
 };
-static_assert(sizeof(PartRecord) == 272, "record layout");
-constexpr int32_t kRecComplete = 1;
+static_assert(sizeof(PartRecord) == 280, "record layout");
 
 struct Params {
   const void* logits;

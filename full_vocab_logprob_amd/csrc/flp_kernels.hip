@@ -21,13 +21,15 @@
 //   Natural-mode rows also feed a per-wave LDS pool of 64-bit raw keys
 //   (value, then smaller ID) that always holds the wave's best 32: chunks
 //   whose maximum passes the admission bar are copied to an LDS stash as they
-//   stream by and expanded one lane per element afterwards.  A part's first
-//   unit sets the bar at the smallest of the waves' k-th largest lane maxima
-//   (32 lanes in all reach it; ballot radix select); later the bar is the
-//   largest of that value bar, the wave's own 32nd-best key and the smallest
+//   stream by and expanded one lane per element afterwards.  In a part's first
+//   unit each wave sets its stash bar after the first chunk (the k-th largest
+//   of that chunk's lane maxima, k = ceil(32 / waves)) and admits lanes at or
+//   above its k-th largest lane maximum of the whole slice; later the bar is
+//   the largest of that value, the wave's own 32nd-best key and the smallest
 //   of the four waves' published 8th-best keys.  Compaction sorts 64-key
-//   lists in registers.  At the end of a part wave 0 merges the four waves'
-//   sorted best 32 into the part record (m, s, best 32 raw keys).
+//   lists in registers.  At the end of a part the last wave to arrive merges
+//   the four waves' sorted best 32 into the part record (m, s, best 32 raw
+//   keys, and a cut bounding every key the part dropped).
 //
 // merge_kernel: one workgroup per row merges the row's part records: L from
 // the parts in part order, the chosen and selected gathers, and the natural
@@ -444,18 +446,52 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
 // reduction left each active row's index among the active rows and their
 // count in the workspace, which locate the row's parts without a scan.
 //
-// Exactness guard.  A part keeps its best 32 raw keys; let c be the 32nd,
-// with value x_c.  With F the final key (reported value, then smaller ID),
-// F_K the K-th best final key among all kept candidates and v_K its value,
-// every lane e that the part dropped has either x_e == x_c and a larger ID
-// (so F(e) < F(c)) or x_e <= pred(x_c) (so its value is at most
-// r(pred(x_c)), r(x) = fl32(x - L) being monotone).  Hence if F(c) <= F_K
-// and r(pred(x_c)) < v_K no dropped lane can enter the top K.  A part that
-// fails either test is rescanned lane by lane with final keys; F_K over a
-// subset never exceeds the true K-th key, so the test stays sound.
+// Exactness guard.  Every lane a part did not keep has a raw key at most the
+// part's cut c (value x_c): the part's 32nd kept key, or a wave's first-unit
+// bar, whichever is larger.  With F the final key (reported value, then
+// smaller ID), F_K the K-th best final key among all kept candidates and v_K
+// its value, such a lane e has either x_e == x_c and a larger ID (so
+// F(e) <= F(c)) or x_e <= pred(x_c) (so its value is at most r(pred(x_c)),
+// r(x) = fl32(x - L) being monotone).  Hence if F(c) <= F_K and
+// r(pred(x_c)) < v_K no dropped lane can enter the top K.  A part that fails
+// either test is rescanned lane by lane with final keys; F_K over a subset
+// never exceeds the true K-th key, so the test stays sound.
 constexpr int kMergeWaves = kMergeBlock / 64;
 
-template <int DT>
+// Every lane [lo, hi) of a row whose final key reaches thr, merged into the
+// sorted best 32 in `top`; thr rises to the K-th kept key as it fills.  One
+// 16-byte chunk per lane per step, the next one in flight.
+template <int DT, bool VEC>
+__device__ __forceinline__ void rescan_lanes(uint64_t& top, uint64_t& thr, const char* rowp, int lo,
+                                             int hi, float L, int Keff, int lane) {
+  using E = Elem<DT>;
+  constexpr int kPer = E::kPer;
+  constexpr int kStep = 64 * kPer;
+  u32x4 nx = lo + lane * kPer < hi ? load_chunk<DT, VEC>(rowp, lo + lane * kPer, hi)
+                                   : u32x4{0u, 0u, 0u, 0u};
+  for (int b = lo; b < hi; b += kStep) {
+    const u32x4 cur = nx;
+    const int nf = b + kStep + lane * kPer;
+    if (b + kStep < hi) nx = nf < hi ? load_chunk<DT, VEC>(rowp, nf, hi) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = b + lane * kPer + j;
+      uint64_t f = 0ull;
+      if (i < hi) {
+        f = make_key(reported(E::get(cur, j), L), (uint32_t)i);
+        if (f < thr) f = 0ull;
+      }
+      if (__ballot(f != 0ull) != 0ull) {
+        top = merge_top32(top, sort64_desc(f, lane), lane);
+        // The list only improves: its K-th key is a floor for the rest.
+        const uint64_t kth = readlane64(top, Keff - 1);
+        thr = kth > thr ? kth : thr;
+      }
+    }
+  }
+}
+
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kUnitElems = kUnitThreads * kChunks * E::kPer;
@@ -492,12 +528,10 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // first two parts' kept keys and each part's guard words
   float pm = kNegInf, ps = 0.0f;
   uint64_t c_key = 0ull;
-  int32_t c_flags = kRecComplete;
   if (lane < np) {
     pm = rec[u0].m;
     ps = rec[u0].s;
-    c_key = rec[u0].keys[kKeep - 1];
-    c_flags = rec[u0].flags;
+    c_key = rec[u0].cut;
   }
   const uint64_t raw0 = (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
   float x_tok = 0.0f;
@@ -550,7 +584,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // ---- guard, one lane per part
   const uint64_t FK = readlane64(top, Keff - 1);
   bool bad = false;
-  if (lane < np && !(c_flags & kRecComplete)) {
+  if (lane < np && c_key != 0ull) {
     const float xc = key_value(c_key);
     bool ok = final_key(c_key, L) <= FK;
     if (ok && xc != kNegInf) ok = ukey32(reported(E::pred(xc), L)) < (uint32_t)(FK >> 32);
@@ -570,20 +604,13 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       }
       top = merge_top32(top, sort64_desc(f, lane), lane);
     }
+    uint64_t thr = FK;
     for (int part = 0; part < np; ++part) {
       if (!((unsafe >> part) & 1ull)) continue;
       const int lo = part_u0[part] * kUnitElems;
       int hi = part_u0[part + 1] * kUnitElems;
       hi = hi < V ? hi : V;
-      for (int b = lo; b < hi; b += 64) {
-        const int i = b + lane;
-        uint64_t f = 0ull;
-        if (i < hi) {
-          f = make_key(reported(load_elem<DT>(rowp, i), L), (uint32_t)i);
-          if (f < FK) f = 0ull;
-        }
-        if (__ballot(f != 0ull) != 0ull) top = merge_top32(top, sort64_desc(f, lane), lane);
-      }
+      rescan_lanes<DT, VEC>(top, thr, rowp, lo, hi, L, Keff, lane);
     }
   }
   if (lane < K) {
@@ -599,15 +626,17 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
 
 // ================================================================== reduce
 constexpr int kWaves = kBlock / 64;  // 4 waves share each unit
-constexpr int kStash = 64;           // hot chunks a wave can stash per unit
+constexpr int kStash = 128;          // hot chunks a wave can stash per unit
 
 struct ReduceSmem {
   uint64_t pool[kWaves][kCandBuf];       // per-wave candidate buffers
   uint64_t flush_keys[2][kWaves][kKeep]; // a part's sorted best 32 per wave, by part parity
   u32x4 stash[kWaves][kStash];           // hot chunks of the unit being reduced
+  float stash_max[kWaves][kStash];       // their maxima
   int16_t stash_off[kWaves][kStash];     // their chunk index c * 64 + lane
+  int16_t stash_sel[kWaves][kStash];     // entries selected for expansion
   uint64_t qbar[kWaves];                 // each wave's published 8th-best key (see pub_key)
-  float tw[2][kWaves];                   // a part's first-unit thresholds, by part parity
+  uint64_t flush_cut[2][kWaves];         // a part's per-wave cut, by part parity
   float wm[2][kWaves];                   // a part's per-wave max and scaled sum
   float ws[2][kWaves];
   int arrive[2];                         // waves that flushed the part of this parity
@@ -672,10 +701,13 @@ __device__ __forceinline__ bool admitted(const Admit& ad, float x, uint64_t key)
 // compacted order (n may exceed kStash: then the stash is incomplete).
 struct Stage {
   u32x4* stash;
+  float* max;
   int16_t* off;
+  int16_t* sel;
   int n;
 };
-__device__ __forceinline__ void stage_chunk(Stage& st, const u32x4& r, bool hot, int c, int lane) {
+__device__ __forceinline__ void stage_chunk(Stage& st, const u32x4& r, float mc, bool hot, int c,
+                                            int lane) {
   const uint64_t m = __ballot(hot);
   if (m != 0ull) {
     const int n = __popcll(m);
@@ -683,20 +715,9 @@ __device__ __forceinline__ void stage_chunk(Stage& st, const u32x4& r, bool hot,
       if (hot) {
         const int pos = st.n + lanes_below(m);
         st.stash[pos] = r;
+        st.max[pos] = mc;
         st.off[pos] = (int16_t)(c * 64 + lane);
       }
-    }
-    st.n += n;
-  }
-}
-
-// Record a hot chunk's offset only (its data is read again later).
-__device__ __forceinline__ void stage_offset(Stage& st, bool hot, int c, int lane) {
-  const uint64_t m = __ballot(hot);
-  if (m != 0ull) {
-    const int n = __popcll(m);
-    if (st.n + n <= kStash) {
-      if (hot) st.off[st.n + lanes_below(m)] = (int16_t)(c * 64 + lane);
     }
     st.n += n;
   }
@@ -786,13 +807,19 @@ struct PassOut {
   float acc, lm, mref, nb;
 };
 
+// With `provisional` (a part's first unit, no bar yet) the stash bar is set
+// after the first chunk: the kq-th largest of its 64 lane maxima (a lower
+// bound read from the 16-bit key prefix; -inf when fewer than kq lanes hold
+// vocabulary).  It is at most the kq-th largest lane maximum of the whole
+// slice, so the stash holds every chunk that bar admits; `ht` and `stage`
+// return its test.
 template <int DT, bool VEC>
 __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[kChunks],
                                              float m_l, bool tail, int wave_base,
                                              __amdgpu_buffer_rsrc_t next_rsrc,
                                              const char* next_rowp, int next_base, bool has_next,
-                                             int V, int lane, bool stage, const HotTest& ht,
-                                             Stage& st) {
+                                             int V, int lane, bool& stage, HotTest& ht, Stage& st,
+                                             bool provisional, int kq) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   PassOut o;
@@ -820,7 +847,15 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
       o.acc += __builtin_amdgcn_exp2f(__builtin_fmaf(xv, kLog2e, o.nb));
     }
     cm[c] = mc;
-    if (stage) stage_chunk(st, raw[c], mc > ht.above, c, lane);
+    if (c == 0 && provisional) {
+      const bool voter = wave_base + lane * kPer < V;
+      const int nv = __popcll(__ballot(voter));
+      const float tau0 =
+          nv >= kq ? key_floor16(wave_kth_largest16(ukey32(mc) >> 16, voter, kq)) : kNegInf;
+      ht = hot_test(tau0, false, ht.vlim);
+      stage = !ht.every_lane;
+    }
+    if (stage) stage_chunk(st, raw[c], mc, mc > ht.above, c, lane);
     {
       int lane_dep = lane;
       asm volatile("" : "+v"(lane_dep) : "v"(o.acc), "v"(mc), "v"(raw[c]));
@@ -833,42 +868,35 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
   return o;
 }
 
-// Expand hot chunks of the unit just reduced, named by their stash offsets,
-// reading them again from memory (the registers already hold the next unit).
-template <int DT, bool VEC>
-__device__ __forceinline__ void expand_reload(CandBuf& cb, Best32& best, const Stage& st,
-                                              const char* rowp, int wave_base, int V, int lane,
-                                              const Admit& ad) {
-  using E = Elem<DT>;
-  constexpr int kPer = E::kPer;
-  wave_sync();
-  for (int b = 0; b < st.n; b += 64) {
-    const bool mine = b + lane < st.n;
-    const int first = mine ? wave_base + (int)st.off[b + lane] * kPer : 0;
-    const u32x4 r = mine ? load_chunk<DT, VEC>(rowp, first, V) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const float x = E::get(r, j);
-      const uint64_t key = make_key(x, (uint32_t)(first + j));
-      cand_append(cb, best, (mine && first + j < V && admitted(ad, x, key)) ? key : 0ull, lane);
-    }
-  }
-  wave_sync();
-}
-
-// Expand the stashed chunks one lane per element into the pool.
+// Expand the stashed chunks one lane per element into the pool.  With
+// `filter` only the chunks whose maximum exceeds `above` (a first unit's
+// stash holds chunks staged against a lower bar): those are first compacted
+// into the wave's LDS index list.
 template <int DT>
 __device__ __forceinline__ void expand_stash(CandBuf& cb, Best32& best, const Stage& st,
-                                             int64_t wave_base, int V, int lane, const Admit& ad) {
+                                             bool filter, float above, int64_t wave_base, int V,
+                                             int lane, const Admit& ad) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
+  constexpr int kPerRound = 64 / kPer;  // entries expanded per 64 lanes
   wave_sync();
-  const int total = st.n * kPer;
-  for (int b = 0; b < total; b += 64) {
-    const int e = b + lane;
+  int cnt = st.n;
+  if (filter) {
+    cnt = 0;
+    for (int b0 = 0; b0 < st.n; b0 += 64) {
+      const int ent = b0 + lane;
+      const bool pass = ent < st.n && st.max[ent] > above;
+      const uint64_t m = __ballot(pass);
+      if (pass) st.sel[cnt + lanes_below(m)] = (int16_t)ent;
+      cnt += __popcll(m);
+    }
+    wave_sync();
+  }
+  for (int s0 = 0; s0 < cnt; s0 += kPerRound) {
+    const int si = s0 + lane / kPer, j = lane % kPer;
     uint64_t k = 0ull;
-    if (e < total) {
-      const int i = e / kPer, j = e - (e / kPer) * kPer;
+    if (si < cnt) {
+      const int i = filter ? (int)st.sel[si] : si;
       const int64_t id = wave_base + (int64_t)st.off[i] * kPer + j;
       const uint32_t bits = DT == 1 ? (uint32_t)((const uint16_t*)&st.stash[i])[j] << 16
                                     : ((const uint32_t*)&st.stash[i])[j];
@@ -979,12 +1007,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   float m_l = kNegInf, s_l = 0.0f;
   Best32 best{0ull, 0, 0ull};
   CandBuf cb{&sh.pool[w][0], 0};
-  Stage st{&sh.stash[w][0], &sh.stash_off[w][0], 0};
+  Stage st{&sh.stash[w][0], &sh.stash_max[w][0], &sh.stash_off[w][0], &sh.stash_sel[w][0], 0};
   uint64_t published = 0ull;
   int part_seq = 0;  // parts of the range finished by this wave
   // The part's first-unit threshold as a key bar: a later lane passes it iff
-  // its value is strictly larger (0: none).
+  // its value is at least the threshold (0: none).
   uint64_t first_bar = 0ull;
+  // Largest key this wave's share of the part may have dropped beyond the
+  // part's 32nd kept key (its first-unit bar).
+  uint64_t cut = 0ull;
 
   for (int x = x0; x < x1; ++x) {
     progress_priority(x - x0, x1 - x0);
@@ -1029,14 +1060,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
     const int vlim = V - wave_base <= 0 ? 0 : (V - wave_base < kWaveElems ? V - wave_base : kWaveElems);
     HotTest ht = hot_test(tau, strict, vlim);
-    // Stash while streaming only with a bar that a chunk maximum can test.
-    const bool stage = natural && ad.by_key && !ht.every_lane;
+    // Stash while streaming only with a bar that a chunk maximum can test; a
+    // part's first unit takes a provisional one from its first chunk.
+    bool stage = natural && ad.by_key && !ht.every_lane;
+    // Keys each wave admits in a part's first unit: ceil(32 / waves holding
+    // vocabulary), so that the part keeps at least 32.
+    const int ubase = cur.u * kUnitElems;
+    const int nw = V - ubase >= kUnitElems ? kWaves : (V - ubase + kWaveElems - 1) / kWaveElems;
+    const int kfirst = (kKeep + nw - 1) / nw;
 
     st.n = 0;
     float cm[kChunks];
     const PassOut po =
         unit_pass<DT, VEC>(raw, cm, m_l, tail, wave_base, row_rsrc(nxt.rowp, has_next ? row_bytes : 0),
-                           nxt.rowp, next_base, has_next, V, lane, stage, ht, st);
+                           nxt.rowp, next_base, has_next, V, lane, stage, ht, st,
+                           natural && part_starts, kfirst);
     const float lm = po.lm;
 
     // ---- fold the unit into the lane's running (max, sum)
@@ -1070,37 +1108,32 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // ---- candidates for this wave's pool
     if (natural) {
       if (part_starts) {
-        // The part's first unit.  Its threshold is the smallest over the
-        // workgroup's waves of each wave's k-th largest lane maximum,
-        // k = ceil(32 / waves holding vocabulary): lane maxima are distinct
-        // lanes, so at least 32 lanes of the unit reach it.  A wave with
-        // fewer than k such lanes makes it -inf.  The registers already
-        // hold the next unit, so the hot chunks are read again.
-        const int ubase = cur.u * kUnitElems;
-        const int nw = V - ubase >= kUnitElems ? kWaves : (V - ubase + kWaveElems - 1) / kWaveElems;
-        const int k = (kKeep + nw - 1) / nw;
+        // The part's first unit: admit lanes at or above the wave's k-th
+        // largest lane maximum (lane maxima are distinct lanes, so at least
+        // k lanes reach it; -inf when fewer than k lanes hold vocabulary).
+        // The stash was filled against a lower bar during the pass.  Lanes
+        // below it are covered by the wave's cut, which the merge's guard
+        // checks against the row's K-th key.
         const int vl = vlim <= 0 ? 0 : (vlim + kPer - 1) / kPer < 64 ? (vlim + kPer - 1) / kPer : 64;
-        float tw = __builtin_huge_valf();  // a wave without vocabulary does not vote
-        if (vl > 0)
-          tw = vl >= k ? key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, k)) : kNegInf;
-        const int par = part_seq & 1;
-        if (lane == 0) sh.tw[par][w] = tw;
-        __syncthreads();
-        tau = fminf(fminf(sh.tw[par][0], sh.tw[par][1]), fminf(sh.tw[par][2], sh.tw[par][3]));
+        tau = kNegInf;
+        if (stage && vl >= kfirst)
+          tau = key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, kfirst));
         ad.by_key = false;
         ad.tau = tau;
-        ht = hot_test(tau, false, vlim);
-        first_bar = tau == kNegInf ? 0ull : ((uint64_t)ukey32(tau) << 32) | 0xFFFFFFFFull;
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) stage_offset(st, is_hot<kPer>(ht, cm[c], c, lane), c, lane);
-        if (st.n > kStash) expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
-        else if (st.n > 0) expand_reload<DT, VEC>(cb, best, st, cur.rowp, wave_base, V, lane, ad);
+        // As a key bar for the part's later units this admits values >= tau
+        // (its low word ~ID = 0 belongs to no lane), so ties at tau stay.
+        first_bar = tau == kNegInf ? 0ull : (uint64_t)ukey32(tau) << 32;
+        cut = first_bar;
+        if (!stage || st.n > kStash) expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
+        else if (st.n > 0)
+          expand_stash<DT>(cb, best, st, true, hot_test(tau, false, vlim).above, wave_base, V, lane,
+                           ad);
       } else if (!stage || st.n > kStash) {
         // No bar a chunk maximum can test, or more hot chunks than the stash
         // holds: every lane of the slice, read again.
         expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
       } else if (st.n > 0) {
-        expand_stash<DT>(cb, best, st, wave_base, V, lane, ad);
+        expand_stash<DT>(cb, best, st, false, 0.0f, wave_base, V, lane, ad);
       }
       cand_flush(cb, best, lane);
       const uint64_t b8 = best.n >= 8 ? readlane64(best.top, 7) : 0ull;
@@ -1130,6 +1163,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         }
       }
       if (natural && lane < kKeep) sh.flush_keys[b][w][lane] = best.top;
+      if (lane == 0) sh.flush_cut[b][w] = natural ? cut : 0ull;
       // The last wave to arrive merges the four shares into the record.
       int old = 0;
       if (lane == 0)
@@ -1147,6 +1181,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
           held = __popcll(__ballot(lane < kKeep && top != 0ull));
         }
         if (lane < kKeep) rec->keys[lane] = top;
+        // Every lane the part dropped has a key at most the part's 32nd kept
+        // key or one of its waves' cuts.
+        uint64_t pcut = held == kKeep ? readlane64(top, kKeep - 1) : 0ull;
         if (lane == 0) {
           float M = sh.wm[b][0];
           for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[b][i]);
@@ -1155,12 +1192,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
             for (int i = 0; i < kWaves; ++i)
               if (sh.wm[b][i] != kNegInf)
                 S += sh.ws[b][i] * __builtin_amdgcn_exp2f((sh.wm[b][i] - M) * kLog2e);
-          const int lo = part_u0 * kUnitElems;
-          const int hi = (cur.u + 1) * kUnitElems < V ? (cur.u + 1) * kUnitElems : V;
+          for (int i = 0; i < kWaves; ++i) pcut = sh.flush_cut[b][i] > pcut ? sh.flush_cut[b][i] : pcut;
           rec->m = M;
           rec->s = S;
           rec->n = held;
-          rec->flags = hi - lo <= kKeep ? kRecComplete : 0;
+          rec->flags = 0;
+          rec->cut = pcut;
           p.row_index[cur.row] = cur.a;
           sh.arrive[b] = 0;
           __hip_atomic_store(&sh.merged, part_seq + 1, __ATOMIC_RELEASE,
@@ -1177,6 +1214,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         best.bar = 0ull;
         published = 0ull;
         first_bar = 0ull;
+        cut = 0ull;
         part_u0 = nxt.u;
         n_sel = p.id_counts[nxt.s];
         n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
@@ -1198,7 +1236,7 @@ hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
   }
   if (!(phases & kPhaseMerge)) return hipSuccess;
   const int64_t rows = (int64_t)p.capacity * p.T;
-  hipLaunchKernelGGL((merge_kernel<DT>), dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)),
+  hipLaunchKernelGGL((merge_kernel<DT, VEC>), dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)),
                      dim3(kMergeBlock), 0, st, p);
   return hipGetLastError();
 }
