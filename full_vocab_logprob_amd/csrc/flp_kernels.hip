@@ -23,10 +23,10 @@
 //   whose maximum passes the admission bar are copied to an LDS stash as they
 //   stream by and expanded one lane per element afterwards.  In a part's first
 //   unit each wave sets its stash bar after the first chunk (the k-th largest
-//   of that chunk's lane maxima, k = ceil(32 / waves)) and admits lanes at or
+//   of that chunk's lane maxima, k = ceil(K / waves)) and admits lanes at or
 //   above its k-th largest lane maximum of the whole slice; later the bar is
-//   the largest of that value, the wave's own 32nd-best key and the smallest
-//   of the four waves' published 8th-best keys.  Compaction sorts 64-key
+//   the largest of that value, the wave's own K-th best key and the smallest
+//   of the four waves' published ceil(K / 4)-th best keys.  Compaction sorts 64-key
 //   lists in registers.  At the end of a part the last wave to arrive merges
 //   the four waves' sorted best 32 into the part record (m, s, best 32 raw
 //   keys, and a cut bounding every key the part dropped).
@@ -319,7 +319,8 @@ constexpr int kInsertMax = 12;  // larger batches are sorted and merged
 struct Best32 {
   uint64_t top;  // lane i < 32: the i-th best key
   int n;         // keys held (wave-uniform)
-  uint64_t bar;  // the 32nd-best key once n == 32, else 0 (wave-uniform)
+  int rank;      // the call's K: only the best K of a part can reach the top K
+  uint64_t bar;  // the rank-th best key once n >= rank, else 0 (wave-uniform)
 };
 
 // Value held by lane - 1 (0 in lane 0).
@@ -360,11 +361,11 @@ __device__ __forceinline__ void cand_flush(CandBuf& cb, Best32& b, int lane) {
   }
   wave_sync();
   cb.count = 0;
-  b.bar = b.n >= kKeep ? readlane64(b.top, kKeep - 1) : 0ull;
+  b.bar = b.n >= b.rank ? readlane64(b.top, b.rank - 1) : 0ull;
 }
 
-// Buffer one key per lane (0 = none).  A key at or below the list's 32nd
-// is dropped at once: it can no longer enter the list (a run of equal values,
+// Buffer one key per lane (0 = none).  A key at or below the list's bar (its
+// K-th key) is dropped at once: it can no longer reach the top K (a run of equal values,
 // -inf lanes say, then costs one flush instead of one per buffer).
 __device__ __forceinline__ void cand_append(CandBuf& cb, Best32& b, uint64_t k, int lane) {
   if (k <= b.bar) k = 0ull;
@@ -447,7 +448,7 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
 // count in the workspace, which locate the row's parts without a scan.
 //
 // Exactness guard.  Every lane a part did not keep has a raw key at most the
-// part's cut c (value x_c): the part's 32nd kept key, or a wave's first-unit
+// part's cut c (value x_c): the part's K-th kept key, or a wave's first-unit
 // bar, whichever is larger.  With F the final key (reported value, then
 // smaller ID), F_K the K-th best final key among all kept candidates and v_K
 // its value, such a lane e has either x_e == x_c and a larger ID (so
@@ -635,7 +636,7 @@ struct ReduceSmem {
   float stash_max[kWaves][kStash];       // their maxima
   int16_t stash_off[kWaves][kStash];     // their chunk index c * 64 + lane
   int16_t stash_sel[kWaves][kStash];     // entries selected for expansion
-  uint64_t qbar[kWaves];                 // each wave's published 8th-best key (see pub_key)
+  uint64_t qbar[kWaves];                 // each wave's published ceil(K/4)-th key (see pub_key)
   uint64_t flush_cut[2][kWaves];         // a part's per-wave cut, by part parity
   float wm[2][kWaves];                   // a part's per-wave max and scaled sum
   float ws[2][kWaves];
@@ -644,7 +645,7 @@ struct ReduceSmem {
   int scan[kWaves];
 };
 
-// A published 8th-best key carries the number of the part it belongs to, so
+// A published key carries the number of the part it belongs to, so
 // a wave never reads another part's bar: (value key << 32) | (part mod 4096)
 // << 20 | ID, with IDs below 2^20 (at most 64 units of 16,384 lanes).
 __device__ __forceinline__ uint64_t pub_key(uint64_t key, int part) {
@@ -1005,7 +1006,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   // lane's values except one occurrence of m_l (whose term is exactly 1 and
   // is added back when the lanes are combined).
   float m_l = kNegInf, s_l = 0.0f;
-  Best32 best{0ull, 0, 0ull};
+  // Bars rank by the call's K (K <= 32): a part's K-th key bounds what can
+  // still enter the row's top K.
+  const int K = p.K;
+  const int kq = (K + kWaves - 1) / kWaves;  // published per-wave rank
+  Best32 best{0ull, 0, K, 0ull};
   CandBuf cb{&sh.pool[w][0], 0};
   Stage st{&sh.stash[w][0], &sh.stash_max[w][0], &sh.stash_off[w][0], &sh.stash_sel[w][0], 0};
   uint64_t published = 0ull;
@@ -1014,7 +1019,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   // its value is at least the threshold (0: none).
   uint64_t first_bar = 0ull;
   // Largest key this wave's share of the part may have dropped beyond the
-  // part's 32nd kept key (its first-unit bar).
+  // part's K-th kept key (its first-unit bar).
   uint64_t cut = 0ull;
 
   for (int x = x0; x < x1; ++x) {
@@ -1032,9 +1037,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     const int next_base = nxt.u * kUnitElems + w * kWaveElems;
     const bool tail = wave_base + kWaveElems > V;  // the slice reaches past V
 
-    // ---- admission bar known before the pass: the wave's own 32nd-best
-    // key, or the smallest of the four waves' published 8th-best keys of
-    // this part (32 keys of the part lie at or above it), the larger.
+    // ---- admission bar known before the pass: the wave's own K-th best
+    // key, or the smallest of the four waves' published ceil(K/4)-th keys of
+    // this part (K keys of the part lie at or above it), the larger.
     Admit ad{false, 0ull, kNegInf};
     float tau = kNegInf;
     bool strict = false;
@@ -1063,11 +1068,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // Stash while streaming only with a bar that a chunk maximum can test; a
     // part's first unit takes a provisional one from its first chunk.
     bool stage = natural && ad.by_key && !ht.every_lane;
-    // Keys each wave admits in a part's first unit: ceil(32 / waves holding
-    // vocabulary), so that the part keeps at least 32.
+    // Keys each wave admits in a part's first unit: ceil(K / waves holding
+    // vocabulary), so that the part keeps at least K.
     const int ubase = cur.u * kUnitElems;
     const int nw = V - ubase >= kUnitElems ? kWaves : (V - ubase + kWaveElems - 1) / kWaveElems;
-    const int kfirst = (kKeep + nw - 1) / nw;
+    const int kfirst = (K + nw - 1) / nw;
 
     st.n = 0;
     float cm[kChunks];
@@ -1136,7 +1141,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         expand_stash<DT>(cb, best, st, false, 0.0f, wave_base, V, lane, ad);
       }
       cand_flush(cb, best, lane);
-      const uint64_t b8 = best.n >= 8 ? readlane64(best.top, 7) : 0ull;
+      const uint64_t b8 = best.n >= kq ? readlane64(best.top, kq - 1) : 0ull;
       if (b8 != published) {
         published = b8;
         if (lane == 0) lds_store64(&sh.qbar[w], pub_key(published, part_seq));
@@ -1181,9 +1186,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
           held = __popcll(__ballot(lane < kKeep && top != 0ull));
         }
         if (lane < kKeep) rec->keys[lane] = top;
-        // Every lane the part dropped has a key at most the part's 32nd kept
+        // Every lane the part dropped has a key at most the part's K-th kept
         // key or one of its waves' cuts.
-        uint64_t pcut = held == kKeep ? readlane64(top, kKeep - 1) : 0ull;
+        uint64_t pcut = held >= K ? readlane64(top, K - 1) : 0ull;
         if (lane == 0) {
           float M = sh.wm[b][0];
           for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[b][i]);

@@ -76,6 +76,14 @@ def test_c5_large_batch_reduced(oracle_handle, variant):
     full_compare(oracle_handle, spec)
 
 
+@pytest.mark.parametrize("K", [2, 5, 13])
+@pytest.mark.parametrize("name", ["C3", "C4"])
+def test_k_sweep_reduced(oracle_handle, name, K):
+    # The admission bars and the parts' cuts rank by K; few rows spread each
+    # row over several parts.
+    full_compare(oracle_handle, synth.CONFIGS[name].with_(capacity=6, K=K, seed=60 + K))
+
+
 def sampled_full_size(o, spec, nsample=24):
     announce(f"full size {spec.name} cap={spec.capacity} T={spec.T} V={spec.V} (sampled rows)")
     w = synth.make(spec)
