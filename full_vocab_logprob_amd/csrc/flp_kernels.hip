@@ -384,14 +384,24 @@ __device__ __forceinline__ void cand_append(CandBuf& cb, Best32& b, uint64_t k, 
 }
 
 // ------------------------------------------------------------ row mapping
-__device__ __forceinline__ int slot_rows(const Params& p, int s) {
-  // Both words are loaded together (one round trip).
-  const int r = p.requested[s], e = p.emitted[s];
-  return r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
+// A prefix word holds the active rows of the slots before s in its low 31
+// bits and, in bit 31, whether slot s selects IDs (its rows then keep no
+// natural candidates).  Keeping that bit in LDS spares the stream a global
+// load at each part end, whose wait would also wait for the next unit's
+// loads already in flight.
+constexpr int kSelBit = (int)0x80000000u;
+constexpr int kRowsMask = 0x7FFFFFFF;
+
+__device__ __forceinline__ int slot_word(const Params& p, int s) {
+  // The three words are loaded together (one round trip).
+  const int r = p.requested[s], e = p.emitted[s], n = p.id_counts[s];
+  const int rows = r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
+  return rows | (n > 0 ? kSelBit : 0);
 }
 
-// prefix[s] = active rows of slots before s; prefix[capacity] = total.  All
-// NW waves of the workgroup take part; `scan` is NW ints of LDS.
+// prefix[s] = active rows of slots before s (with slot s's selection bit);
+// prefix[capacity] = total.  All NW waves of the workgroup take part; `scan`
+// is NW ints of LDS.
 template <int NW>
 __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
   constexpr int NT = NW * 64;
@@ -402,9 +412,9 @@ __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
   const int s1 = s0 + per < cap ? s0 + per : cap;
   int local = 0;
   for (int s = s0; s < s1; ++s) {
-    const int c = slot_rows(p, s);
+    const int c = slot_word(p, s);
     prefix[s] = c;
-    local += c;
+    local += c & kRowsMask;
   }
   // exclusive scan of `local` over the block
   int incl = local;
@@ -423,20 +433,20 @@ __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
   }
   for (int s = s0; s < s1; ++s) {
     const int c = prefix[s];
-    prefix[s] = run;
-    run += c;
+    prefix[s] = run | (c & kSelBit);
+    run += c & kRowsMask;
   }
   if (tid == 0) prefix[cap] = total;
   __syncthreads();
   return total;
 }
 
-// Slot of active row a: the largest s with prefix[s] <= a.
+// Slot of active row a: the largest s whose row count before it is <= a.
 __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
   int lo = 0, hi = cap;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= a) lo = mid; else hi = mid;
+    if ((prefix[mid] & kRowsMask) <= a) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -628,6 +638,18 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
 // ================================================================== reduce
 constexpr int kWaves = kBlock / 64;  // 4 waves share each unit
 constexpr int kStash = 128;          // hot chunks a wave can stash per unit
+constexpr int kRecStage = 8;         // part records staged in LDS before they are written
+
+// A finished part's record, held in LDS until the workgroup writes its
+// records out: global stores issued while the stream's loads are in flight
+// share the in-order memory counter with them and hold up the next waits.
+struct StagedRec {
+  PartRecord rec;
+  int32_t dst;      // record index, row * units + the part's first unit
+  int32_t row;      // logit row, and its index among the active rows
+  int32_t a;
+  int32_t natural;  // whether the kept keys are meaningful
+};
 
 struct ReduceSmem {
   uint64_t pool[kWaves][kCandBuf];       // per-wave candidate buffers
@@ -642,6 +664,8 @@ struct ReduceSmem {
   float ws[2][kWaves];
   int arrive[2];                         // waves that flushed the part of this parity
   int merged;                            // parts of the range merged into records
+  int n_staged;                          // records staged in `staged`
+  StagedRec staged[kRecStage];
   int scan[kWaves];
 };
 
@@ -670,7 +694,7 @@ __device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, in
   q.a = x / p.units;
   q.u = x - q.a * p.units;
   q.s = __builtin_amdgcn_readfirstlane(slot_of(prefix, p.capacity, q.a));
-  q.row = __builtin_amdgcn_readfirstlane(q.s * p.T + (q.a - prefix[q.s]));
+  q.row = __builtin_amdgcn_readfirstlane(q.s * p.T + (q.a - (prefix[q.s] & kRowsMask)));
   q.rowp = (const char*)p.logits + (int64_t)q.row * p.V_pad * Elem<DT>::kBytes;
   return q;
 }
@@ -949,11 +973,18 @@ __device__ __forceinline__ int opaque_lane(int lane) {
 // the workgroups dispatched first race through their ranges while the
 // youngest lag and set the end of the launch; lowering the priority as a
 // range is consumed hands issue slots to the workgroups that are behind.
-__device__ __forceinline__ void progress_priority(int done, int count) {
-  const int q = (int)(((int64_t)done * 4) / count);
-  if (q == 0) __builtin_amdgcn_s_setprio(3);
-  else if (q == 1) __builtin_amdgcn_s_setprio(2);
-  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+// The quarter starts are computed once per range (no division per unit).
+struct Quarters {
+  int q1, q2, q3;
+};
+__device__ __forceinline__ Quarters range_quarters(int x0, int x1) {
+  const int64_t n = x1 - x0;
+  return Quarters{x0 + (int)((n + 3) >> 2), x0 + (int)((2 * n + 3) >> 2), x0 + (int)((3 * n + 3) >> 2)};
+}
+__device__ __forceinline__ void progress_priority(int x, const Quarters& q) {
+  if (x < q.q1) __builtin_amdgcn_s_setprio(3);
+  else if (x < q.q2) __builtin_amdgcn_s_setprio(2);
+  else if (x < q.q3) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
 
@@ -964,9 +995,9 @@ __device__ __forceinline__ void lds_store64(uint64_t* a, uint64_t v) {
   __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Four waves per workgroup, four workgroups per CU: 128 VGPRs per lane.
+// Four waves per workgroup, five workgroups per CU: at most 96 VGPRs per lane.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void reduce_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) void reduce_kernel(
     Params p) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
@@ -981,14 +1012,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   if (tid < kWaves) sh.qbar[tid] = 0ull;  // ordered by the barriers below
   if (tid < 2) sh.arrive[tid] = 0;
   if (tid == 0) sh.merged = 0;
+  if (tid == 0) sh.n_staged = 0;
   const int total = build_prefix<kWaves>(p, prefix, sh.scan);
   // This workgroup's range of the N < 2^31 units (the host checks N).
   const int64_t N = (int64_t)total * U;
   const int x0 = (int)((int64_t)blockIdx.x * N / p.workers);
   const int x1 = (int)(((int64_t)blockIdx.x + 1) * N / p.workers);
   if (x0 >= x1) return;
-  // Mark which of the range's units begins it, for the merge.
-  for (int x = x0 + tid; x < x1; x += kBlock) p.unit_start[x] = x == x0 ? 1 : 0;
 
   UnitPos cur = locate<DT>(p, prefix, x0);
   int part_u0 = cur.u;
@@ -998,9 +1028,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   for (int c = 0; c < kChunks; ++c)
     refill_chunk<DT, VEC>(raw[c], row_rsrc(cur.rowp, row_bytes), cur.rowp,
                           cur.u * kUnitElems + w * kWaveElems, c, lane_id, V, true);
-  int n_sel = p.id_counts[cur.s];
-  n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
-  bool natural = p.K > 0 && n_sel == 0;
+  bool natural = p.K > 0 && (prefix[cur.s] & kSelBit) == 0;
 
   // Per lane: running max m_l and the sum, relative to m_l, of exp over the
   // lane's values except one occurrence of m_l (whose term is exactly 1 and
@@ -1022,8 +1050,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   // part's K-th kept key (its first-unit bar).
   uint64_t cut = 0ull;
 
+  const Quarters quarters = range_quarters(x0, x1);
   for (int x = x0; x < x1; ++x) {
-    progress_priority(x - x0, x1 - x0);
+    progress_priority(x, quarters);
     const int lane = opaque_lane(lane_id);
     const bool has_next = x + 1 < x1;
     UnitPos nxt = cur;
@@ -1044,11 +1073,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     float tau = kNegInf;
     bool strict = false;
     if (natural && !part_starts) {
-      // Every lane reads the same words; decode them as scalars.
-      uint64_t bq = pub_read(readlane64(lds_load64(&sh.qbar[0]), 0), part_seq);
+      // Every lane reads the same words (all four loads in flight at once);
+      // decode them as scalars.
+      uint64_t qv[kWaves];
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) qv[i] = lds_load64(&sh.qbar[i]);
+      uint64_t bq = pub_read(readlane64(qv[0], 0), part_seq);
 #pragma unroll
       for (int i = 1; i < kWaves; ++i) {
-        const uint64_t b = pub_read(readlane64(lds_load64(&sh.qbar[i]), 0), part_seq);
+        const uint64_t b = pub_read(readlane64(qv[i], 0), part_seq);
         bq = b < bq ? b : bq;
       }
       uint64_t bar = best.bar;
@@ -1072,7 +1105,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     // vocabulary), so that the part keeps at least K.
     const int ubase = cur.u * kUnitElems;
     const int nw = V - ubase >= kUnitElems ? kWaves : (V - ubase + kWaveElems - 1) / kWaveElems;
-    const int kfirst = (K + nw - 1) / nw;
+    const int kfirst = nw == kWaves ? kq : (nw == 3 ? (K + 2) / 3 : (nw == 2 ? (K + 1) >> 1 : K));
 
     st.n = 0;
     float cm[kChunks];
@@ -1175,7 +1208,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         old = __hip_atomic_fetch_add(&sh.arrive[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
       old = __builtin_amdgcn_readfirstlane(old);
       if (old == kWaves - 1) {
-        PartRecord* rec = p.records + (int64_t)cur.row * U + part_u0;
+        const int slot = __builtin_amdgcn_readfirstlane(sh.n_staged);
+        StagedRec* sr = &sh.staged[slot];
+        PartRecord* rec = &sr->rec;
         uint64_t top = 0ull;
         int held = 0;
         if (natural) {
@@ -1185,7 +1220,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
             top = merge_top32(top, lane < kKeep ? sh.flush_keys[b][i][lane] : 0ull, lane);
           held = __popcll(__ballot(lane < kKeep && top != 0ull));
         }
-        if (lane < kKeep) rec->keys[lane] = top;
+        if (natural && lane < kKeep) rec->keys[lane] = top;
         // Every lane the part dropped has a key at most the part's K-th kept
         // key or one of its waves' cuts.
         uint64_t pcut = held >= K ? readlane64(top, K - 1) : 0ull;
@@ -1203,10 +1238,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
           rec->n = held;
           rec->flags = 0;
           rec->cut = pcut;
-          p.row_index[cur.row] = cur.a;
+          sr->dst = cur.row * U + part_u0;
+          sr->row = cur.row;
+          sr->a = cur.a;
+          sr->natural = natural;
+          sh.n_staged = (slot + 1 == kRecStage || !has_next) ? 0 : slot + 1;
           sh.arrive[b] = 0;
           __hip_atomic_store(&sh.merged, part_seq + 1, __ATOMIC_RELEASE,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        // Write the staged records out once the stage is full, and at the end
+        // of the range (with the range's part-start flags for the merge).
+        if (slot + 1 == kRecStage || !has_next) {
+          wave_sync();
+          for (int r = 0; r <= slot; ++r) {
+            const StagedRec& s = sh.staged[r];
+            const int words = __builtin_amdgcn_readfirstlane(s.natural) ? 3 + kKeep : 3;
+            if (lane < words)
+              ((uint64_t*)(p.records + __builtin_amdgcn_readfirstlane(s.dst)))[lane] =
+                  ((const uint64_t*)&s.rec)[lane];
+            if (lane == 0) p.row_index[s.row] = s.a;
+          }
+          if (!has_next)
+            for (int y = x0 + lane; y < x1; y += 64) p.unit_start[y] = y == x0 ? 1 : 0;
         }
       }
       ++part_seq;
@@ -1221,9 +1275,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         first_bar = 0ull;
         cut = 0ull;
         part_u0 = nxt.u;
-        n_sel = p.id_counts[nxt.s];
-        n_sel = n_sel < 0 ? 0 : (n_sel > 128 ? 128 : n_sel);
-        natural = p.K > 0 && n_sel == 0;
+        natural = p.K > 0 && (prefix[nxt.s] & kSelBit) == 0;
       }
     }
     cur = nxt;
