@@ -22,12 +22,11 @@
 //   (value, then smaller ID) that always holds the wave's best 32: chunks
 //   whose maximum passes the admission bar are copied to an LDS stash as they
 //   stream by and expanded one lane per element afterwards.  In a part's first
-//   unit each wave sets its stash bar after the first chunk (the k-th largest
-//   of that chunk's lane maxima, k = ceil(K / waves)) and admits lanes at or
-//   above its k-th largest lane maximum of the whole slice; later the bar is
-//   the largest of that value, the wave's own K-th best key and the smallest
-//   of the four waves' published ceil(K / 4)-th best keys.  Compaction sorts 64-key
-//   lists in registers.  At the end of a part the last wave to arrive merges
+//   unit each wave first takes the maxima of its registers and admits lanes
+//   at or above its k-th largest lane maximum (k = ceil(K / waves)); later
+//   the bar is the largest of that value, the wave's own K-th best key and
+//   the smallest of the four waves' published ceil(K / 4)-th best keys.
+//   Compaction sorts 64-key lists in registers.  At the end of a part the last wave to arrive merges
 //   the four waves' sorted best 32 into the part record (m, s, best 32 raw
 //   keys, and a cut bounding every key the part dropped).
 //
@@ -655,9 +654,7 @@ struct ReduceSmem {
   uint64_t pool[kWaves][kCandBuf];       // per-wave candidate buffers
   uint64_t flush_keys[2][kWaves][kKeep]; // a part's sorted best 32 per wave, by part parity
   u32x4 stash[kWaves][kStash];           // hot chunks of the unit being reduced
-  float stash_max[kWaves][kStash];       // their maxima
   int16_t stash_off[kWaves][kStash];     // their chunk index c * 64 + lane
-  int16_t stash_sel[kWaves][kStash];     // entries selected for expansion
   uint64_t qbar[kWaves];                 // each wave's published ceil(K/4)-th key (see pub_key)
   uint64_t flush_cut[2][kWaves];         // a part's per-wave cut, by part parity
   float wm[2][kWaves];                   // a part's per-wave max and scaled sum
@@ -726,13 +723,10 @@ __device__ __forceinline__ bool admitted(const Admit& ad, float x, uint64_t key)
 // compacted order (n may exceed kStash: then the stash is incomplete).
 struct Stage {
   u32x4* stash;
-  float* max;
   int16_t* off;
-  int16_t* sel;
   int n;
 };
-__device__ __forceinline__ void stage_chunk(Stage& st, const u32x4& r, float mc, bool hot, int c,
-                                            int lane) {
+__device__ __forceinline__ void stage_chunk(Stage& st, const u32x4& r, bool hot, int c, int lane) {
   const uint64_t m = __ballot(hot);
   if (m != 0ull) {
     const int n = __popcll(m);
@@ -740,7 +734,6 @@ __device__ __forceinline__ void stage_chunk(Stage& st, const u32x4& r, float mc,
       if (hot) {
         const int pos = st.n + lanes_below(m);
         st.stash[pos] = r;
-        st.max[pos] = mc;
         st.off[pos] = (int16_t)(c * 64 + lane);
       }
     }
@@ -830,24 +823,44 @@ __device__ __forceinline__ void refill_chunk(u32x4& r, __amdgpu_buffer_rsrc_t rs
 // maximum passes the test is stashed first.
 struct PassOut {
   float acc, lm, mref, nb;
+  float tau;  // a first unit's threshold
 };
 
-// With `provisional` (a part's first unit, no bar yet) the stash bar is set
-// after the first chunk: the kq-th largest of its 64 lane maxima (a lower
-// bound read from the 16-bit key prefix; -inf when fewer than kq lanes hold
-// vocabulary).  It is at most the kq-th largest lane maximum of the whole
-// slice, so the stash holds every chunk that bar admits; `ht` and `stage`
-// return its test.
+// With `first` (a part's first unit, no bar yet) the pass sweeps the
+// registers twice: the chunk maxima first, whose kq-th largest lane maximum
+// (read from the 16-bit key prefix; -inf when fewer than kq lanes hold
+// vocabulary) becomes the unit's threshold, then the statistics, staging
+// the chunks that reach the threshold.  The first sweep waits for the whole
+// unit, which only delays that unit's refills.  `ht`, `stage` and `o.tau`
+// return the threshold and its test.
 template <int DT, bool VEC>
 __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[kChunks],
                                              float m_l, bool tail, int wave_base,
                                              __amdgpu_buffer_rsrc_t next_rsrc,
                                              const char* next_rowp, int next_base, bool has_next,
                                              int V, int lane, bool& stage, HotTest& ht, Stage& st,
-                                             bool provisional, int kq) {
+                                             bool first, int kq) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   PassOut o;
+  o.tau = kNegInf;
+  if (first) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      if (VEC && tail) raw[c] = mask_tail<DT>(raw[c], wave_base + (c * 64 + lane) * kPer, V);
+      float mc = E::get(raw[c], 0);
+#pragma unroll
+      for (int j = 1; j < kPer; ++j) mc = fmaxf(mc, E::get(raw[c], j));
+      cm[c] = mc;
+    }
+    const float lm = fmaxf(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])),
+                           fmaxf(fmaxf(cm[4], cm[5]), fmaxf(cm[6], cm[7])));
+    const bool voter = wave_base + lane * kPer < V;
+    const int nv = __popcll(__ballot(voter));
+    o.tau = nv >= kq ? key_floor16(wave_kth_largest16(ukey32(lm) >> 16, voter, kq)) : kNegInf;
+    ht = hot_test(o.tau, false, ht.vlim);
+    stage = !ht.every_lane;
+  }
   if (VEC && tail) raw[0] = mask_tail<DT>(raw[0], wave_base + lane * kPer, V);
   float c0 = E::get(raw[0], 0);
 #pragma unroll
@@ -872,15 +885,7 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
       o.acc += __builtin_amdgcn_exp2f(__builtin_fmaf(xv, kLog2e, o.nb));
     }
     cm[c] = mc;
-    if (c == 0 && provisional) {
-      const bool voter = wave_base + lane * kPer < V;
-      const int nv = __popcll(__ballot(voter));
-      const float tau0 =
-          nv >= kq ? key_floor16(wave_kth_largest16(ukey32(mc) >> 16, voter, kq)) : kNegInf;
-      ht = hot_test(tau0, false, ht.vlim);
-      stage = !ht.every_lane;
-    }
-    if (stage) stage_chunk(st, raw[c], mc, mc > ht.above, c, lane);
+    if (stage) stage_chunk(st, raw[c], mc > ht.above, c, lane);
     {
       int lane_dep = lane;
       asm volatile("" : "+v"(lane_dep) : "v"(o.acc), "v"(mc), "v"(raw[c]));
@@ -893,35 +898,19 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
   return o;
 }
 
-// Expand the stashed chunks one lane per element into the pool.  With
-// `filter` only the chunks whose maximum exceeds `above` (a first unit's
-// stash holds chunks staged against a lower bar): those are first compacted
-// into the wave's LDS index list.
+// Expand the stashed chunks one lane per element into the pool.
 template <int DT>
 __device__ __forceinline__ void expand_stash(CandBuf& cb, Best32& best, const Stage& st,
-                                             bool filter, float above, int64_t wave_base, int V,
-                                             int lane, const Admit& ad) {
+                                             int64_t wave_base, int V, int lane, const Admit& ad) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   constexpr int kPerRound = 64 / kPer;  // entries expanded per 64 lanes
   wave_sync();
-  int cnt = st.n;
-  if (filter) {
-    cnt = 0;
-    for (int b0 = 0; b0 < st.n; b0 += 64) {
-      const int ent = b0 + lane;
-      const bool pass = ent < st.n && st.max[ent] > above;
-      const uint64_t m = __ballot(pass);
-      if (pass) st.sel[cnt + lanes_below(m)] = (int16_t)ent;
-      cnt += __popcll(m);
-    }
-    wave_sync();
-  }
+  const int cnt = st.n;
   for (int s0 = 0; s0 < cnt; s0 += kPerRound) {
-    const int si = s0 + lane / kPer, j = lane % kPer;
+    const int i = s0 + lane / kPer, j = lane % kPer;
     uint64_t k = 0ull;
-    if (si < cnt) {
-      const int i = filter ? (int)st.sel[si] : si;
+    if (i < cnt) {
       const int64_t id = wave_base + (int64_t)st.off[i] * kPer + j;
       const uint32_t bits = DT == 1 ? (uint32_t)((const uint16_t*)&st.stash[i])[j] << 16
                                     : ((const uint32_t*)&st.stash[i])[j];
@@ -1040,7 +1029,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   const int kq = (K + kWaves - 1) / kWaves;  // published per-wave rank
   Best32 best{0ull, 0, K, 0ull};
   CandBuf cb{&sh.pool[w][0], 0};
-  Stage st{&sh.stash[w][0], &sh.stash_max[w][0], &sh.stash_off[w][0], &sh.stash_sel[w][0], 0};
+  Stage st{&sh.stash[w][0], &sh.stash_off[w][0], 0};
   uint64_t published = 0ull;
   int part_seq = 0;  // parts of the range finished by this wave
   // The part's first-unit threshold as a key bar: a later lane passes it iff
@@ -1099,7 +1088,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     const int vlim = V - wave_base <= 0 ? 0 : (V - wave_base < kWaveElems ? V - wave_base : kWaveElems);
     HotTest ht = hot_test(tau, strict, vlim);
     // Stash while streaming only with a bar that a chunk maximum can test; a
-    // part's first unit takes a provisional one from its first chunk.
+    // part's first unit finds its threshold in the pass itself.
     bool stage = natural && ad.by_key && !ht.every_lane;
     // Keys each wave admits in a part's first unit: ceil(K / waves holding
     // vocabulary), so that the part keeps at least K.
@@ -1148,14 +1137,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
       if (part_starts) {
         // The part's first unit: admit lanes at or above the wave's k-th
         // largest lane maximum (lane maxima are distinct lanes, so at least
-        // k lanes reach it; -inf when fewer than k lanes hold vocabulary).
-        // The stash was filled against a lower bar during the pass.  Lanes
-        // below it are covered by the wave's cut, which the merge's guard
-        // checks against the row's K-th key.
-        const int vl = vlim <= 0 ? 0 : (vlim + kPer - 1) / kPer < 64 ? (vlim + kPer - 1) / kPer : 64;
-        tau = kNegInf;
-        if (stage && vl >= kfirst)
-          tau = key_floor16(wave_kth_largest16(ukey32(lm) >> 16, lane < vl, kfirst));
+        // k lanes reach it; -inf when fewer than k lanes hold vocabulary),
+        // which the pass found before staging against it.  Lanes below it
+        // are covered by the wave's cut, which the merge's guard checks
+        // against the row's K-th key.
+        tau = po.tau;
         ad.by_key = false;
         ad.tau = tau;
         // As a key bar for the part's later units this admits values >= tau
@@ -1164,14 +1150,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         cut = first_bar;
         if (!stage || st.n > kStash) expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
         else if (st.n > 0)
-          expand_stash<DT>(cb, best, st, true, hot_test(tau, false, vlim).above, wave_base, V, lane,
-                           ad);
+          expand_stash<DT>(cb, best, st, wave_base, V, lane, ad);
       } else if (!stage || st.n > kStash) {
         // No bar a chunk maximum can test, or more hot chunks than the stash
         // holds: every lane of the slice, read again.
         expand_global<DT, VEC>(cb, best, cur.rowp, wave_base, V, lane, ad);
       } else if (st.n > 0) {
-        expand_stash<DT>(cb, best, st, false, 0.0f, wave_base, V, lane, ad);
+        expand_stash<DT>(cb, best, st, wave_base, V, lane, ad);
       }
       cand_flush(cb, best, lane);
       const uint64_t b8 = best.n >= kq ? readlane64(best.top, kq - 1) : 0ull;
