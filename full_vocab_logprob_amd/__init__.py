@@ -24,7 +24,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libflare_logprobs.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_K = 20
 MAX_IDS = 128
 ROW_WORDS = 258
@@ -47,8 +47,8 @@ class PlanStruct(ctypes.Structure):
                 ("vector_rows", ctypes.c_int32), ("cu_count", ctypes.c_int32),
                 ("ranges", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
-                ("lse_offset", ctypes.c_uint64), ("index_offset", ctypes.c_uint64),
-                ("start_offset", ctypes.c_uint64), ("reserved", ctypes.c_uint32 * 6)]
+                ("lse_offset", ctypes.c_uint64), ("slots_offset", ctypes.c_uint64),
+                ("reserved_offset", ctypes.c_uint64), ("reserved", ctypes.c_uint32 * 6)]
 
 
 class FlareError(RuntimeError):

@@ -90,10 +90,9 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   off = align_up(off + (uint64_t)rows * units * sizeof(flp::PartRecord), kAlign);
   plan->lse_offset = off;
   off = align_up(off + (uint64_t)rows * sizeof(float), kAlign);
-  plan->index_offset = off;
-  off = align_up(off + (uint64_t)rows * sizeof(int32_t), kAlign);
-  plan->start_offset = off;
-  off = align_up(off + (uint64_t)rows * units, kAlign);
+  plan->slots_offset = off;
+  off = align_up(off + ((uint64_t)capacity + 1) * sizeof(int32_t), kAlign);
+  plan->reserved_offset = 0;
   plan->workspace_bytes = off;
   return FLARE_OK;
 }
@@ -130,8 +129,7 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
   p.out = out;
   p.records = (flp::PartRecord*)(ws + plan->record_offset);
   p.lse = (float*)(ws + plan->lse_offset);
-  p.row_index = (int32_t*)(ws + plan->index_offset);
-  p.unit_start = (uint8_t*)(ws + plan->start_offset);
+  p.slot_rows = (int32_t*)(ws + plan->slots_offset);
   p.V_pad = V_pad;
   p.capacity = plan->capacity;
   p.T = plan->T;

@@ -45,8 +45,7 @@ struct Params {
   int32_t* out;
   PartRecord* records;
   float* lse;
-  int32_t* row_index;   // [rows]: index of each active row among the active rows
-  uint8_t* unit_start;  // [rows * units]: 1 where a workgroup's unit range begins
+  int32_t* slot_rows;   // [capacity + 1]: active rows before each slot, then their total
   int64_t V_pad;
   int32_t capacity;
   int32_t T;

@@ -453,8 +453,9 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
 // ==================================================================== merge
 // One wave per row, four rows per workgroup: L from the row's parts in part
 // order, the chosen and selected gathers, and the natural top K.  The
-// reduction left each active row's index among the active rows and their
-// count in the workspace, which locate the row's parts without a scan.
+// reduction left each slot's count of active rows before it, and their
+// total, in the workspace: with them a row finds its index among the active
+// rows, and its parts, from its first loads.
 //
 // Exactness guard.  Every lane a part did not keep has a raw key at most the
 // part's cut c (value x_c): the part's K-th kept key, or a wave's first-unit
@@ -467,6 +468,17 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
 // either test is rescanned lane by lane with final keys; F_K over a subset
 // never exceeds the true K-th key, so the test stays sound.
 constexpr int kMergeWaves = kMergeBlock / 64;
+
+// Whether unit x begins one of the `grid` ranges [floor(g n / grid),
+// floor((g + 1) n / grid)) of n units: with g the smallest index whose range
+// starts at or after x, ceil(x grid / n), it does iff floor(g n / grid) == x.
+// Every product is below 2^53 and every quotient that is not an integer is
+// at least 1/n (resp. 1/grid) away from one, so the double divisions round
+// to the exact ceiling and floor.
+__device__ __forceinline__ bool is_range_start(int x, int n, int grid) {
+  const double g = __builtin_ceil((double)x * (double)grid / (double)n);
+  return __builtin_floor(g * (double)n / (double)grid) == (double)x;
+}
 
 // Every lane [lo, hi) of a row whose final key reaches thr, merged into the
 // sorted best 32 in `top`; thr rises to the K-th kept key as it fills.  One
@@ -511,10 +523,10 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int row = (int)blockIdx.x * kMergeWaves + wv;
   if (row >= p.capacity * p.T) return;
   const int s = row / p.T, t = row - s * p.T;
-  // Every input word this row needs, loaded at once (the index words are
+  // Every input word this row needs, loaded at once (the row counts are
   // only meaningful for an active row).
   const int req = p.requested[s], emi = p.emitted[s], cnt = p.id_counts[s];
-  const int a = p.row_index[row];
+  const int before = p.slot_rows[s], total = p.slot_rows[p.capacity];
   const int tok = p.tokens[row];
   if (req == 0 || t >= (emi < 0 ? 0 : (emi > p.T ? p.T : emi))) return;
   const int n_sel = cnt < 0 ? 0 : (cnt > 128 ? 128 : cnt);
@@ -525,8 +537,12 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   int32_t* out = p.out + (int64_t)row * kRowWords;
   int16_t* part_u0 = part_u0_all[wv];
 
-  // ---- the row's parts (one lane per unit)
-  const bool start = lane < U && (lane == 0 || p.unit_start[(int64_t)a * U + lane] != 0);
+  // ---- the row's parts (one lane per unit): a part starts at the row's
+  // first unit and wherever a workgroup's unit range starts, at
+  // floor(g N / grid) of the N units of the active rows (the reduction's
+  // partition, recomputed exactly in double precision).
+  const int a = before + t;
+  const bool start = lane < U && (lane == 0 || is_range_start(a * U + lane, total * U, p.workers));
   const uint64_t starts = __ballot(start);
   const int np = __popcll(starts);
   if (start) part_u0[lanes_below(starts)] = (int16_t)lane;
@@ -645,8 +661,6 @@ constexpr int kRecStage = 8;         // part records staged in LDS before they a
 struct StagedRec {
   PartRecord rec;
   int32_t dst;      // record index, row * units + the part's first unit
-  int32_t row;      // logit row, and its index among the active rows
-  int32_t a;
   int32_t natural;  // whether the kept keys are meaningful
 };
 
@@ -1003,6 +1017,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   if (tid == 0) sh.merged = 0;
   if (tid == 0) sh.n_staged = 0;
   const int total = build_prefix<kWaves>(p, prefix, sh.scan);
+  // The slots' active-row counts before them, and the total, for the merge.
+  if (blockIdx.x == 0)
+    for (int s = tid; s <= p.capacity; s += kBlock) p.slot_rows[s] = prefix[s] & kRowsMask;
   // This workgroup's range of the N < 2^31 units (the host checks N).
   const int64_t N = (int64_t)total * U;
   const int x0 = (int)((int64_t)blockIdx.x * N / p.workers);
@@ -1224,8 +1241,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
           rec->flags = 0;
           rec->cut = pcut;
           sr->dst = cur.row * U + part_u0;
-          sr->row = cur.row;
-          sr->a = cur.a;
           sr->natural = natural;
           sh.n_staged = (slot + 1 == kRecStage || !has_next) ? 0 : slot + 1;
           sh.arrive[b] = 0;
@@ -1233,7 +1248,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
                              __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         // Write the staged records out once the stage is full, and at the end
-        // of the range (with the range's part-start flags for the merge).
+        // of the range.
         if (slot + 1 == kRecStage || !has_next) {
           wave_sync();
           for (int r = 0; r <= slot; ++r) {
@@ -1242,10 +1257,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
             if (lane < words)
               ((uint64_t*)(p.records + __builtin_amdgcn_readfirstlane(s.dst)))[lane] =
                   ((const uint64_t*)&s.rec)[lane];
-            if (lane == 0) p.row_index[s.row] = s.a;
           }
-          if (!has_next)
-            for (int y = x0 + lane; y < x1; y += 64) p.unit_start[y] = y == x0 ? 1 : 0;
         }
       }
       ++part_seq;

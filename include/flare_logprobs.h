@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FLARE_LOGPROBS_ABI_VERSION 1u
+#define FLARE_LOGPROBS_ABI_VERSION 2u
 #define FLARE_LOGPROBS_MAX_K 20
 #define FLARE_LOGPROBS_MAX_IDS 128
 #define FLARE_LOGPROBS_ROW_WORDS 258 /* 2 + 2 * 128 */
@@ -92,8 +92,8 @@ typedef struct flare_logprobs_plan {
   uint64_t workspace_bytes; /* bytes of device workspace the caller provides */
   uint64_t record_offset;   /* per-(row, unit) part records */
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
-  uint64_t index_offset;    /* int32[capacity * T]: row order of the reduction */
-  uint64_t start_offset;    /* uint8[capacity * T * units]: unit-range starts */
+  uint64_t slots_offset;    /* int32[capacity + 1]: active rows before each slot, then all */
+  uint64_t reserved_offset; /* 0 */
   uint32_t reserved[6];
 } flare_logprobs_plan_t;
 

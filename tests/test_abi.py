@@ -65,11 +65,11 @@ def test_plan_host_only_geometry(flp):
     rc, p = host_plan(flp)
     assert rc == 0
     assert p.units == 16 and p.unit_elems == 16384 and p.block == 256 and p.vector_rows == 1
-    assert p.cu_count == 256 and p.abi_version == 1 and p.grid == 1024 and p.ranges == 1024
+    assert p.cu_count == 256 and p.abi_version == 2 and p.grid == 1024 and p.ranges == 1024
     rows = 128 * 8
-    assert p.lse_offset >= rows * 16 * 272 and p.index_offset >= p.lse_offset + 4 * rows
-    assert p.start_offset >= p.index_offset + 4 * rows
-    assert p.workspace_bytes >= p.start_offset + rows * 16
+    assert p.lse_offset >= rows * 16 * 280 and p.slots_offset >= p.lse_offset + 4 * rows
+    assert p.slots_offset % 16 == 0 and p.reserved_offset == 0
+    assert p.workspace_bytes >= p.slots_offset + 4 * (128 + 1)
     rc, p = host_plan(flp, capacity=1024, T=4, V=262144, V_pad=262144, dtype=0)
     assert rc == 0 and p.units == 32 and p.unit_elems == 8192
     rc, p = host_plan(flp, V=37, V_pad=41)
