@@ -551,7 +551,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int u0 = lane < np ? part_u0[lane] : 0;
 
   // ---- record and logit loads, issued together: the part statistics, the
-  // first two parts' kept keys and each part's guard words
+  // first four parts' kept keys and each part's guard words
   float pm = kNegInf, ps = 0.0f;
   uint64_t c_key = 0ull;
   if (lane < np) {
@@ -560,6 +560,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
     c_key = rec[u0].cut;
   }
   const uint64_t raw0 = (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
+  const uint64_t raw1 = 2 + (lane >> 5) < np ? rec[part_u0[2 + (lane >> 5)]].keys[lane & 31] : 0ull;
   float x_tok = 0.0f;
   if (lane == 0 && tok >= 0 && tok < V) x_tok = load_elem<DT>(rowp, tok);
   int sel_id[2] = {0, 0};
@@ -598,7 +599,9 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int K = p.K;
   const int Keff = K < V ? K : V;
   uint64_t top = sort64_desc(raw0 != 0ull ? final_key(raw0, L) : 0ull, lane);
-  for (int pb = 2; pb < np; pb += 2) {
+  if (np > 2)
+    top = merge_top32(top, sort64_desc(raw1 != 0ull ? final_key(raw1, L) : 0ull, lane), lane);
+  for (int pb = 4; pb < np; pb += 2) {
     const int part = pb + (lane >> 5);
     uint64_t f = 0ull;
     if (part < np) {
