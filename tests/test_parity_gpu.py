@@ -84,6 +84,15 @@ def test_k_sweep_reduced(oracle_handle, name, K):
     full_compare(oracle_handle, synth.CONFIGS[name].with_(capacity=6, K=K, seed=60 + K))
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP32], ids=["bf16", "fp32"])
+def test_many_ranges_per_row(oracle_handle, dtype):
+    # About 1,150 active rows of 4 units each: several workgroup ranges start
+    # inside most rows, at positions the merge recomputes from the partition.
+    spec = synth.CONFIGS["C3"].with_(capacity=256, T=8, V=3 * 16384 + 5, V_pad=3 * 16384 + 8,
+                                     dtype=dtype, seed=91)
+    full_compare(oracle_handle, spec)
+
+
 def sampled_full_size(o, spec, nsample=24):
     announce(f"full size {spec.name} cap={spec.capacity} T={spec.T} V={spec.V} (sampled rows)")
     w = synth.make(spec)
