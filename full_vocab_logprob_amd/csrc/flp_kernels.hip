@@ -804,6 +804,21 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 r, int first, int V) {
   return r;
 }
 
+// Chunk c of a wave covers lanes [cbase, cbase + 64 kPer) of the row, lane l
+// holding [cbase + l kPer, cbase + (l + 1) kPer).  Only the chunk that V
+// falls in is masked lane by lane; a chunk wholly past V reads -inf and one
+// wholly before it is left alone (both tests are wave-uniform).
+template <int DT>
+__device__ __forceinline__ u32x4 mask_chunk(u32x4 r, int cbase, int lane, int V) {
+  constexpr int kPer = Elem<DT>::kPer;
+  if (cbase + 64 * kPer <= V) return r;
+  if (cbase >= V) {
+    const uint32_t ninf = DT == 1 ? 0xFF80FF80u : 0xFF800000u;
+    return u32x4{ninf, ninf, ninf, ninf};
+  }
+  return mask_tail<DT>(r, cbase + lane * kPer, V);
+}
+
 // A buffer resource over one logit row: loads past its `bytes` return zero
 // without touching memory (the hardware range check covers the per-lane
 // offset).  bytes = 0 makes every load a no-op.
@@ -864,7 +879,7 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
   if (first) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      if (VEC && tail) raw[c] = mask_tail<DT>(raw[c], wave_base + (c * 64 + lane) * kPer, V);
+      if (VEC && tail) raw[c] = mask_chunk<DT>(raw[c], wave_base + c * 64 * kPer, lane, V);
       float mc = E::get(raw[c], 0);
 #pragma unroll
       for (int j = 1; j < kPer; ++j) mc = fmaxf(mc, E::get(raw[c], j));
@@ -878,7 +893,7 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
     ht = hot_test(o.tau, false, ht.vlim);
     stage = !ht.every_lane;
   }
-  if (VEC && tail) raw[0] = mask_tail<DT>(raw[0], wave_base + lane * kPer, V);
+  if (VEC && tail) raw[0] = mask_chunk<DT>(raw[0], wave_base, lane, V);
   float c0 = E::get(raw[0], 0);
 #pragma unroll
   for (int j = 1; j < kPer; ++j) c0 = fmaxf(c0, E::get(raw[0], j));
@@ -892,7 +907,7 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
     // only after their last use, so the refill lands in the same registers.
     if (c > 0) {
       asm volatile("" : "+v"(raw[c]) : "v"(o.acc), "v"(cm[c - 1]));
-      if (VEC && tail) raw[c] = mask_tail<DT>(raw[c], wave_base + (c * 64 + lane) * kPer, V);
+      if (VEC && tail) raw[c] = mask_chunk<DT>(raw[c], wave_base + c * 64 * kPer, lane, V);
     }
     float mc = kNegInf;
 #pragma unroll
