@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run a plain elementwise FP32 copy of this many MiB "
                          "three times (scales HBM byte counters; 0 disables it)")
+    ap.add_argument("--graph", type=int, default=1,
+                    help="also time the calls replayed from one captured HIP graph (0: skip)")
     return ap.parse_args()
 
 
@@ -185,6 +187,34 @@ def main():
     merge_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
     mean_reduce_ms = sum(reduce_ms) / K
     mean_merge_ms = sum(merge_ms) / K
+
+    # Timed region 3: the same calls replayed from one HIP graph (one call per
+    # logits copy captured, replayed until about K calls have run).
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(gr, stream=side):
+                for c in range(len(copies)):
+                    plan.run(copies[c], tokens, emitted, requested, id_counts, ids, out, ws)
+        torch.cuda.synchronize()
+        reps = max(1, K // len(copies))
+        for _ in range(2):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        per_call = g0.elapsed_time(g1) / (reps * len(copies))
+        graph = {"ms_per_call": per_call, "rows_per_s": active / (per_call / 1e3),
+                 "calls": reps * len(copies)}
+        del gr
     achieved_gbps = algo_bytes / (mean_reduce_ms / 1e3) / 1e9
     traffic = measured_traffic(spec.name)
 
@@ -238,6 +268,7 @@ def main():
         "reduce_ms": {"mean": mean_reduce_ms, "median": reduce_ms[K // 2],
                       "p10": reduce_ms[K // 10], "p90": reduce_ms[(9 * K) // 10]},
         "merge_ms": {"mean": mean_merge_ms, "median": merge_ms[K // 2]},
+        "graph_replay": graph,
         "algorithmic_bytes_per_launch": algo_bytes,
         "wall_s": wall,
         "cpu_baseline": cpu,
