@@ -9,7 +9,7 @@
 // How.  Every logit is read from HBM once; nothing here is a contraction, so
 // there is no MFMA.  Two launches.
 //
-// reduce_kernel: a persistent launch of `grid` 256-thread workgroups (four
+// reduce_kernel: a persistent launch of `grid` 256-thread workgroups (five
 // per CU).  The work is the concatenation, over active rows, of each row's
 // units (16,384 bf16 or 8,192 FP32 lanes, 32 KiB); workgroup g owns the
 // contiguous unit range [g N / grid, (g + 1) N / grid), so every workgroup
@@ -26,11 +26,12 @@
 //   at or above its k-th largest lane maximum (k = ceil(K / waves)); later
 //   the bar is the largest of that value, the wave's own K-th best key and
 //   the smallest of the four waves' published ceil(K / 4)-th best keys.
-//   Compaction sorts 64-key lists in registers.  At the end of a part the last wave to arrive merges
-//   the four waves' sorted best 32 into the part record (m, s, best 32 raw
-//   keys, and a cut bounding every key the part dropped).
+//   Compaction sorts 64-key lists in registers.  At the end of a part the
+//   last wave to arrive merges the four waves' sorted best 32 into the part
+//   record (m, s, best 32 raw keys, and a cut bounding every key the part
+//   dropped), staged in LDS and written when the range ends.
 //
-// merge_kernel: one workgroup per row merges the row's part records: L from
+// merge_kernel: one wave per row merges the row's part records: L from
 // the parts in part order, the chosen and selected gathers, and the natural
 // top K re-keyed by the reported value fl32(x - L), with an exactness guard
 // that rescans a part when the raw order it kept could differ from the final
