@@ -217,6 +217,13 @@ __device__ __forceinline__ float xlanef(float v, int lane) {
 __device__ __forceinline__ uint64_t reverse64(uint64_t v, int lane) {
   return xlane64<32>(xlane64<16>(xlane64<15>(v, lane), lane), lane);
 }
+// Value held by lane - 1 (0 in lane 0).
+__device__ __forceinline__ uint64_t wave_shr1_64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x138, 0xf, 0xf, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x138, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
@@ -287,6 +294,19 @@ __device__ __forceinline__ uint64_t bitonic_merge_desc(uint64_t k, int lane) {
   k = cx<1>(k, lane, (lane & 1) == 0);
   return k;
 }
+// Sort two lists held in lanes 0..31 and 32..63 descending.  Each list
+// comes from a part record sorted by raw key; re-keying by the reported
+// value keeps that order unless the subtraction ties distinct values, so
+// the halves are checked first and, when both are in order, merged by one
+// bitonic pass (the upper half mirrored to make the sequence bitonic).
+__device__ __forceinline__ uint64_t sort_halves_desc(uint64_t k, int lane) {
+  const uint64_t prev = wave_shr1_64(k);  // lane - 1
+  const bool out_of_order = (lane & 31) != 0 && prev < k;
+  if (__ballot(out_of_order) != 0ull) return sort64_desc(k, lane);
+  const uint64_t mirrored = xlane64<16>(xlane64<15>(k, lane), lane);  // lane 31 - l within 32
+  return bitonic_merge_desc(lane < 32 ? k : mirrored, lane);
+}
+
 // Lanes 0..31 of the result hold the best 32 of {top[0..32), list[0..64)}
 // sorted descending, given `top` sorted in lanes 0..31 and `list` sorted.
 __device__ __forceinline__ uint64_t merge_top32(uint64_t top, uint64_t list, int lane) {
@@ -323,13 +343,6 @@ struct Best32 {
   uint64_t bar;  // the rank-th best key once n >= rank, else 0 (wave-uniform)
 };
 
-// Value held by lane - 1 (0 in lane 0).
-__device__ __forceinline__ uint64_t wave_shr1_64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x138, 0xf, 0xf, false);
-  const uint32_t hi =
-      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x138, 0xf, 0xf, false);
-  return ((uint64_t)hi << 32) | lo;
-}
 
 // Insert the wave-uniform key k if it ranks among the best 32.
 __device__ __forceinline__ void best_insert(Best32& b, uint64_t k, int lane) {
@@ -599,9 +612,9 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // ---- kept candidates re-keyed by F, two parts (64 keys) per step
   const int K = p.K;
   const int Keff = K < V ? K : V;
-  uint64_t top = sort64_desc(raw0 != 0ull ? final_key(raw0, L) : 0ull, lane);
+  uint64_t top = sort_halves_desc(raw0 != 0ull ? final_key(raw0, L) : 0ull, lane);
   if (np > 2)
-    top = merge_top32(top, sort64_desc(raw1 != 0ull ? final_key(raw1, L) : 0ull, lane), lane);
+    top = merge_top32(top, sort_halves_desc(raw1 != 0ull ? final_key(raw1, L) : 0ull, lane), lane);
   for (int pb = 4; pb < np; pb += 2) {
     const int part = pb + (lane >> 5);
     uint64_t f = 0ull;
