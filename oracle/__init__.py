@@ -27,6 +27,7 @@ MAX_IDS = 128
 ROW_WORDS = 258
 MAX_K = 20
 NAN_BITS = 0x7FC00000
+PROMPT_WORDS = 43
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-Wall", "-Wextra"]
@@ -60,6 +61,12 @@ class Oracle:
                                           c.c_void_p, c.c_void_p, c.c_void_p,
                                           c.c_void_p, c.c_int32, c.c_void_p,
                                           c.c_void_p]
+        self.lib.oracle_prompt_row.restype = c.c_int
+        self.lib.oracle_prompt_row.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
+                                               c.c_void_p, c.c_void_p]
+        self.lib.oracle_prompt.restype = c.c_int64
+        self.lib.oracle_prompt.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
+                                           c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
 
     @staticmethod
     def _dtype_of(a: np.ndarray) -> int:
@@ -114,6 +121,35 @@ class Oracle:
                                   out.ctypes.data, lse.ctypes.data)
         if n < 0:
             raise ValueError("oracle_frame rejected its arguments")
+        return int(n), lse
+
+    def prompt_row(self, row: np.ndarray, target: int, V: int | None = None):
+        """One scored prompt row.  Returns (words[43] as int32, L)."""
+        row = np.ascontiguousarray(row)
+        V = row.shape[-1] if V is None else V
+        words = np.zeros(PROMPT_WORDS, dtype=np.int32)
+        L = ctypes.c_float(0.0)
+        rc = self.lib.oracle_prompt_row(row.ctypes.data, self._dtype_of(row), V, int(target),
+                                        words.ctypes.data, ctypes.byref(L))
+        if rc < 0:
+            raise ValueError("oracle_prompt_row rejected its arguments")
+        return words, float(L.value)
+
+    def prompt(self, logits: np.ndarray, rows: int, V: int, V_pad: int, targets,
+               out: np.ndarray):
+        """A scored chunk.  `out` is [rows, 43] int32, written in place.
+        Returns (valid rows, lse[rows])."""
+        logits = np.ascontiguousarray(logits)
+        assert logits.size >= rows * V_pad
+        tg = np.ascontiguousarray(targets, dtype=np.int32)
+        assert tg.size == rows
+        assert out.dtype == np.int32 and out.size == rows * PROMPT_WORDS
+        assert out.flags.c_contiguous
+        lse = np.full(rows, np.nan, dtype=np.float32)
+        n = self.lib.oracle_prompt(logits.ctypes.data, self._dtype_of(logits), rows, V, V_pad,
+                                   tg.ctypes.data, out.ctypes.data, lse.ctypes.data)
+        if n < 0:
+            raise ValueError("oracle_prompt rejected its arguments")
         return int(n), lse
 
 

@@ -28,6 +28,9 @@
  *     FP32 values (so equalities created by the subtraction are ties),
  *     signed zero is normalized, padded vocabulary lanes never take part,
  *     and selected IDs subtract the same normalization from their raw logit.
+ *   - GLP, prompt-logprobs paragraphs (scored prefill): one row per prompt
+ *     target with the target's logprob, its rank among strictly greater
+ *     reported values and twenty alternatives in the generation order.
  *   - MTP design page, section "A speculative round is a state transaction":
  *     a slot's verify rows are emitted as a prefix of length 1..k+1.
  *
@@ -58,6 +61,8 @@
 #define ORACLE_ROW_WORDS 258
 #define ORACLE_MAX_K 20
 #define ORACLE_NAN_BITS 0x7FC00000u
+#define ORACLE_PROMPT_WORDS 43
+#define ORACLE_PROMPT_ALTS 20
 
 /* One vocabulary entry with its reported value, for sorting. */
 typedef struct {
@@ -172,6 +177,77 @@ int oracle_row(const void* row, int dtype, int32_t V, int32_t token,
   }
   free(all);
   return 2 + 2 * K;
+}
+
+/*
+ * Prompt scoring (GLP, prompt-logprobs paragraphs): one scored row of a
+ * prefill chunk, written as 43 words
+ *     [target, bits(r_t), rank, id_0, bits_0, ..., id_19, bits_19]
+ * with r_i the reported value of lane i (same L and subtraction as above),
+ *     rank = 1 + #{ i in [0, V) : r_i > r_target }   (strictly greater:
+ * lanes whose reported value equals r_target, ties the subtraction creates
+ * included, do not count), and the twenty alternatives in the generation
+ * order (oracle_row's natural listing with K = 20).
+ * Readings: R11 a target outside [0, V) marks an invalid row, not only -1;
+ * R12 an invalid row reads nothing and writes target -1, NaN bits, rank 0
+ * and twenty (-1, 0x7FC00000) pairs (the page fixes the IDs, not the bits).
+ * Returns 43, or -1 when the arguments are unusable.  `L_out` (may be NULL)
+ * gets L, or NaN for an invalid row.
+ */
+int oracle_prompt_row(const void* row, int dtype, int32_t V, int32_t target,
+                      int32_t* words, float* L_out) {
+  if (!row || !words || V < 1) return -1;
+  if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16) return -1;
+  if (target < 0 || target >= V) { /* readings R11, R12 */
+    words[0] = -1;
+    words[1] = (int32_t)ORACLE_NAN_BITS;
+    words[2] = 0;
+    for (int j = 0; j < ORACLE_PROMPT_ALTS; ++j) {
+      words[3 + 2 * j] = -1;
+      words[4 + 2 * j] = (int32_t)ORACLE_NAN_BITS;
+    }
+    if (L_out) *L_out = NAN;
+    return ORACLE_PROMPT_WORDS;
+  }
+  int32_t listing[2 + 2 * ORACLE_MAX_K];
+  float L;
+  if (oracle_row(row, dtype, V, target, 0, NULL, ORACLE_PROMPT_ALTS, listing, &L) < 0)
+    return -1;
+  if (L_out) *L_out = L;
+  float rt = oracle_reported(row, dtype, target, L);
+  int32_t greater = 0;
+  for (int32_t i = 0; i < V; ++i)
+    if (oracle_reported(row, dtype, i, L) > rt) ++greater;
+  words[0] = listing[0];
+  words[1] = listing[1];
+  words[2] = 1 + greater;
+  memcpy(words + 3, listing + 2, sizeof(int32_t) * 2 * ORACLE_PROMPT_ALTS);
+  return ORACLE_PROMPT_WORDS;
+}
+
+/*
+ * A scored chunk: `rows` logit rows of stride V_pad and one target per row,
+ * written to out [rows, 43] (GLP, prompt-logprobs paragraphs; the page
+ * projects rows in blocks of at most 64, which changes nothing per row).
+ * `lse_out` (may be NULL) gets each row's L (NaN for invalid rows).
+ * Returns the number of valid rows, or -1 on unusable arguments.
+ */
+int64_t oracle_prompt(const void* logits, int dtype, int32_t rows, int32_t V,
+                      int32_t V_pad, const int32_t* targets, int32_t* out,
+                      float* lse_out) {
+  if (!logits || !targets || !out || rows < 1 || V < 1 || V_pad < V) return -1;
+  size_t esize = (dtype == ORACLE_DTYPE_BF16) ? 2 : 4;
+  int64_t valid = 0;
+  for (int32_t r = 0; r < rows; ++r) {
+    const char* row = (const char*)logits + (size_t)r * (size_t)V_pad * esize;
+    float L;
+    if (oracle_prompt_row(row, dtype, V, targets[r],
+                          out + (size_t)r * ORACLE_PROMPT_WORDS, &L) < 0)
+      return -1;
+    if (lse_out) lse_out[r] = L;
+    if (targets[r] >= 0 && targets[r] < V) ++valid;
+  }
+  return valid;
 }
 
 /*

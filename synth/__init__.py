@@ -11,7 +11,10 @@ mixed frame and a large batch).  Every random choice is a pure function of
 row can be regenerated alone.
 
 Stream tags: logits 1, chosen tokens 2, emitted counts 3, request flags 4,
-selected IDs 5, spike lane 6, one-hot rows 7.
+selected IDs 5, spike lane 6, one-hot rows 7, prompt targets 8.
+
+Prompt scoring (scored prefill) has its own chunk specs (``PROMPT_CONFIGS``):
+one logit row per prompt position and one target per row.
 """
 from __future__ import annotations
 
@@ -30,6 +33,8 @@ FP32, BF16 = 0, 1
 NORMAL, GUMBEL, GRID8 = 0, 1, 2
 PAD_ZERO, PAD_PINF, PAD_NAN = 0, 1, 2
 TAG_TOKENS, TAG_EMITTED, TAG_REQUESTED, TAG_IDS = 2, 3, 4, 5
+TAG_SPIKE, TAG_TARGETS = 6, 8
+PROMPT_WORDS = 43
 MAX_IDS = 128
 ROW_WORDS = 258
 POISON = np.int32(-559038737)  # 0xDEADBEEF
@@ -272,3 +277,78 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ------------------------------------------------------------ prompt scoring
+# A chunk spec reuses Spec with capacity = rows and T = 1 (the other gating
+# fields are unused).  Targets: the row's last position and a span of image
+# positions are -1; of the rest, half are the row's spike lane (the token the
+# model favours, rank 1) and half a uniform ID (a deep rank: most of the
+# vocabulary above it).
+PROMPT_CONFIGS = {
+    "P1": Spec("P1", 128, 1, 248320, 248320, BF16, GUMBEL, p1=10.0, seed=8,
+               description="scored prefill chunk: 128 rows x V=248,320 bf16 Gumbel + 10 peak; "
+                           "targets: 1/2 the peak lane, 1/2 uniform, an image span and the "
+                           "prompt end -1"),
+    "P2": Spec("P2", 512, 1, 151936, 152064, FP32, NORMAL, p0=4.0, p1=15.0, pad=PAD_PINF,
+               seed=9,
+               description="scored prefill chunk: 512 rows x V=151,936 (V_pad 152,064, +inf "
+                           "pads) FP32 ~ N(0,4) + 15 peak; targets as P1"),
+}
+
+
+@dataclasses.dataclass
+class PromptWorkload:
+    spec: Spec
+    logits: np.ndarray         # [rows, V_pad] float32, or uint16 bf16 bits
+    targets: np.ndarray        # int32 [rows]; -1 marks an invalid row
+
+    @property
+    def rows(self) -> int:
+        return self.spec.capacity
+
+    def valid_rows(self) -> int:
+        return int(((self.targets >= 0) & (self.targets < self.spec.V)).sum())
+
+    def algorithmic_bytes(self) -> int:
+        """Each valid row's V logits once plus its target; every row's target
+        and 43 output words."""
+        s = self.spec
+        b = 2 if s.dtype == BF16 else 4
+        return int(self.valid_rows() * s.V * b + self.rows * (4 + 4 * PROMPT_WORDS))
+
+    def poisoned_out(self) -> np.ndarray:
+        return np.full((self.rows, PROMPT_WORDS), POISON, dtype=np.int32)
+
+
+def prompt_targets(spec: Spec) -> np.ndarray:
+    """int32 [rows] targets for a chunk spec (recipe above)."""
+    s = spec
+    n = s.capacity
+    t = np.empty(n, dtype=np.int32)
+    for r in range(n):
+        h = hash64(s.seed, TAG_TARGETS, r)
+        if h & 1:
+            t[r] = hash64(s.seed, TAG_SPIKE, r) % s.V if s.p1 != 0.0 else hash64(s.seed, TAG_TARGETS, r, 1) % s.V
+        else:
+            t[r] = hash64(s.seed, TAG_TARGETS, r, 1) % s.V
+    if n >= 4:
+        span0 = int(hash64(s.seed, TAG_TARGETS, 1 << 40) % np.uint64(n // 2))
+        t[span0:span0 + max(1, n // 16)] = -1  # an image span
+    t[n - 1] = -1  # the prompt end
+    return t
+
+
+def make_prompt(spec: Spec | str, logits_out: np.ndarray | None = None,
+                **overrides) -> PromptWorkload:
+    if isinstance(spec, str):
+        spec = PROMPT_CONFIGS[spec]
+    if overrides:
+        spec = spec.with_(**overrides)
+    targets = prompt_targets(spec)
+    want = np.uint16 if spec.dtype == BF16 else np.float32
+    if logits_out is None:
+        logits_out = np.empty((spec.capacity, spec.V_pad), dtype=want)
+    garbage = (targets < 0).astype(np.uint8)  # invalid rows are never read
+    fill_logits(spec, logits_out, garbage)
+    return PromptWorkload(spec, logits_out, targets)

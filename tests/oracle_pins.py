@@ -342,8 +342,115 @@ def pin_frame_gating(o):
                 assert float(from_bits(cell[3])) > -1e-3
 
 
+# ------------------------------------------------------------ prompt scoring
+def _prompt_words_check(o, row, target, V=None):
+    """Check one scored row against facts derived without the oracle's rank
+    loop: the count of strictly greater reported values (numpy), the first
+    position of the target's value in a stable descending library sort, and
+    the generation listing of the same row (GLP, prompt-logprobs paragraphs)."""
+    V = row.shape[-1] if V is None else V
+    words, L = o.prompt_row(row, target, V=V)
+    xs = (synth.bf16_to_f32(row) if row.dtype == np.uint16 else row)[:V].astype(np.float32)
+    rep = (xs - f32(L)).astype(np.float32)
+    rep[rep == 0] = 0.0
+    rt = rep[target]
+    assert words[0] == target and words[1] == bits(rt), (words[:3], rt)
+    greater = int(np.count_nonzero(rep > rt))
+    assert words[2] == 1 + greater, (words[2], greater)
+    t = torch.sort(torch.from_numpy(rep), descending=True, stable=True)
+    first = int(np.nonzero(t.values.numpy() == rt)[0][0])
+    assert words[2] == 1 + first
+    gen, L2 = o.row(row, token=target, K=20, V=V)
+    assert L2 == L and np.array_equal(words[3:], gen[2:]), (words[3:9], gen[2:8])
+    return words
+
+
+def pin_prompt_rank_by_counting(o):
+    """Integer-valued logits (no subtraction can tie two of them): the rank is
+    one plus the number of larger raw logits; checked for the top, middle and
+    bottom targets, FP32 and bf16."""
+    rng = np.random.default_rng(21)
+    for V in (1, 5, 19, 20, 21, 1000, 30000):
+        row = rng.integers(-8, 9, size=V).astype(np.float32)
+        for target in {0, V // 2, V - 1, int(np.argmax(row)), int(np.argmin(row))}:
+            w = _prompt_words_check(o, row, target)
+            assert w[2] == 1 + int(np.count_nonzero(row > row[target]))
+            w16 = _prompt_words_check(o, synth.bf16_bits(row), target)
+            assert w16[2] == w[2]
+    # Ranks of all targets of a permutation row are 1..V.
+    V = 257
+    row = rng.permutation(V).astype(np.float32) - 100.0
+    ranks = sorted(int(o.prompt_row(row, t)[0][2]) for t in range(V))
+    assert ranks == list(range(1, V + 1))
+
+
+def pin_prompt_subtraction_tie(o):
+    """x0 = nextafter(1, 0), x1 = 1, x2 = 100, the rest -inf: L = 100 and both
+    x0 - L and x1 - L round to -99, so neither is strictly greater than the
+    other (rank 2 for both), x2 ranks 1 and a -inf lane ranks 4."""
+    V = 64
+    row = np.full(V, -np.inf, dtype=np.float32)
+    row[0] = np.nextafter(np.float32(1.0), np.float32(0.0))
+    row[1] = 1.0
+    row[2] = 100.0
+    for target, rank in ((0, 2), (1, 2), (2, 1), (3, 4), (63, 4)):
+        words, L = o.prompt_row(row, target)
+        assert L == f32(100.0) and words[2] == rank, (target, words[2], rank)
+        _prompt_words_check(o, row, target)
+    assert o.prompt_row(row, 0)[0][1] == bits(f32(-99.0))
+
+
+def pin_prompt_invalid_rows(o):
+    """Targets outside [0, V) (-1 at the prompt end and in image spans) give
+    ID -1, NaN bits, rank 0 and alternative IDs -1 (GLP, prompt-logprobs
+    paragraphs; the alternatives' NaN bits are reading R12)."""
+    row = np.arange(50, dtype=np.float32)
+    want = np.array([-1, NAN_BITS, 0] + [-1, NAN_BITS] * 20, dtype=np.int64).astype(np.int32)
+    for target in (-1, -7, 50, 51, 2**31 - 1):
+        words, L = o.prompt_row(row, target)
+        assert np.array_equal(words, want), (target, words[:5])
+        assert math.isnan(L)
+
+
+def pin_prompt_small_rows_exhaustive(o):
+    """Every row of length 1..4 over {-inf, -2, -1, -0, +0, 1, 2} and every
+    target: rank and listing against counting and a stable sort."""
+    values = np.array([-np.inf, -2.0, -1.0, -0.0, 0.0, 1.0, 2.0], dtype=np.float32)
+    for V in range(1, 5):
+        for combo in itertools.product(range(len(values)), repeat=V):
+            row = values[list(combo)]
+            if np.all(np.isneginf(row)):
+                continue
+            for target in range(V):
+                _prompt_words_check(o, row, target)
+
+
+def pin_prompt_chunk(o):
+    """A chunk of rows with V_pad > V (+inf pads that must not count), valid
+    and invalid targets: row r uses logits row r and target r, and the valid
+    count is returned."""
+    rows, V, V_pad = 9, 300, 320
+    rng = np.random.default_rng(22)
+    logits = np.full((rows, V_pad), np.inf, dtype=np.float32)
+    logits[:, :V] = (rng.standard_normal((rows, V)) * 3).astype(np.float32)
+    targets = np.array([5, -1, 299, 0, 300, 17, -1, 150, 2], dtype=np.int32)
+    out = np.full((rows, 43), -559038737, dtype=np.int32)
+    n, lse = o.prompt(logits, rows, V, V_pad, targets, out)
+    assert n == 6
+    for r in range(rows):
+        if 0 <= targets[r] < V:
+            xs = logits[r, :V]
+            assert out[r, 0] == targets[r]
+            assert out[r, 2] == 1 + int(np.count_nonzero(xs > xs[targets[r]]))
+            ref = float(torch.logsumexp(torch.from_numpy(xs.astype(np.float64)), 0))
+            assert abs(float(lse[r]) - ref) <= ulp32(ref)
+        else:
+            assert out[r, 0] == -1 and out[r, 2] == 0 and math.isnan(lse[r])
+
+
 ALL_PINS = [pin_uniform_row, pin_uniform_row_bf16, pin_two_level_row,
             pin_probabilities_sum_to_one, pin_one_hot, pin_library_logsumexp,
             pin_brute_force_order, pin_all_equal_row, pin_grid_row_by_counting,
             pin_subtraction_tie, pin_signed_zero, pin_v_below_k, pin_selected_ids,
-            pin_frame_gating]
+            pin_frame_gating, pin_prompt_rank_by_counting, pin_prompt_subtraction_tie,
+            pin_prompt_invalid_rows, pin_prompt_small_rows_exhaustive, pin_prompt_chunk]

@@ -42,6 +42,19 @@ MUTANTS = [
     ("no_count_clamp_to_zero", "if (n < 0) n = 0;\n    if (n > ORACLE_MAX_IDS)",
      "if (n < 0) n = 1;\n    if (n > ORACLE_MAX_IDS)"),
     ("invalid_id_zero_bits", "else\n    w[1] = (int32_t)ORACLE_NAN_BITS;", "else\n    w[1] = 0;"),
+    ("prompt_rank_counts_ties", "if (oracle_reported(row, dtype, i, L) > rt) ++greater;",
+     "if (oracle_reported(row, dtype, i, L) >= rt) ++greater;"),
+    ("prompt_rank_on_raw_logits", "if (oracle_reported(row, dtype, i, L) > rt) ++greater;",
+     "if (oracle_widen(row, dtype, i) > oracle_widen(row, dtype, target)) ++greater;"),
+    ("prompt_rank_zero_based", "words[2] = 1 + greater;", "words[2] = greater;"),
+    ("prompt_invalid_rank_one", "words[2] = 0;", "words[2] = 1;"),
+    ("prompt_invalid_alt_id_zero", "words[3 + 2 * j] = -1;", "words[3 + 2 * j] = 0;"),
+    ("prompt_padded_lanes_ranked", "if (oracle_prompt_row(row, dtype, V, targets[r],",
+     "if (oracle_prompt_row(row, dtype, V_pad, targets[r],"),
+    ("prompt_targets_reversed", "if (oracle_prompt_row(row, dtype, V, targets[r],",
+     "if (oracle_prompt_row(row, dtype, V, targets[rows - 1 - r],"),
+    ("prompt_last_alternative_dropped", "sizeof(int32_t) * 2 * ORACLE_PROMPT_ALTS);",
+     "sizeof(int32_t) * 2 * (ORACLE_PROMPT_ALTS - 1));"),
 ]
 
 
