@@ -9,10 +9,16 @@ shared library is missing the import of a binding function raises.
     ws = plan.workspace()
     plan.run(logits, tokens, emitted_counts, requested, id_counts, ids, out, ws)
 
+Prompt scoring (scored prefill rows: target logprob, rank, twenty
+alternatives) has its own plan:
+
+    pplan = PromptPlan(rows, V, V_pad, dtype=torch.bfloat16)
+    pplan.run(logits, targets, out, pplan.workspace())
+
 The functions ``flare_logprobs_plan``, ``flare_logprobs_run`` (and its two
-launches ``flare_logprobs_reduce`` and ``flare_logprobs_merge``),
-``flare_status_string`` and ``flare_logprobs_abi_version`` mirror the C entry
-points one to one.
+launches ``flare_logprobs_reduce`` and ``flare_logprobs_merge``), their
+``flare_prompt_logprobs_*`` counterparts, ``flare_status_string`` and
+``flare_logprobs_abi_version`` mirror the C entry points one to one.
 """
 from __future__ import annotations
 
@@ -24,11 +30,15 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libflare_logprobs.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_K = 20
 MAX_IDS = 128
 ROW_WORDS = 258
 NAN_BITS = 0x7FC00000
+PROMPT_ROW_WORDS = 43
+PROMPT_ALTERNATIVES = 20
+MODE_GENERATION = 0
+MODE_PROMPT = 1
 DTYPE_FP32 = 0
 DTYPE_BF16 = 1
 
@@ -45,7 +55,7 @@ class PlanStruct(ctypes.Structure):
                 ("unit_elems", ctypes.c_int32), ("units", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("vector_rows", ctypes.c_int32), ("cu_count", ctypes.c_int32),
-                ("ranges", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("ranges", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
                 ("lse_offset", ctypes.c_uint64), ("slots_offset", ctypes.c_uint64),
                 ("reserved_offset", ctypes.c_uint64), ("reserved", ctypes.c_uint32 * 6)]
@@ -78,6 +88,15 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
                           c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                           c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
+        L.flare_prompt_logprobs_plan.restype = c.c_int
+        L.flare_prompt_logprobs_plan.argtypes = [c.POINTER(PlanStruct), c.c_int32, c.c_int32,
+                                                 c.c_int32, c.c_int32, c.c_int32]
+        for name in ("flare_prompt_logprobs_run", "flare_prompt_logprobs_reduce",
+                     "flare_prompt_logprobs_merge"):
+            f = getattr(L, name)
+            f.restype = c.c_int
+            f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
+                          c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
         L.flare_status_string.restype = c.c_char_p
         L.flare_status_string.argtypes = [c.c_int]
         L.flare_logprobs_abi_version.restype = c.c_uint32
@@ -222,4 +241,90 @@ class Plan:
         _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
         fn(self.raw, logits, self.torch_dtype, rows, self.V, self.V_pad, requested, id_counts, ids,
            emitted_counts, tokens, self.K, out, workspace, stream)
+        return out
+
+
+# ------------------------------------------------------------ prompt scoring
+def flare_prompt_logprobs_plan(rows: int, V: int, V_pad: int, dtype, device: int) -> PlanStruct:
+    plan = PlanStruct()
+    rc = lib().flare_prompt_logprobs_plan(ctypes.byref(plan), rows, V, V_pad, dtype_code(dtype),
+                                          device)
+    if rc != 0:
+        raise FlareError(rc, "flare_prompt_logprobs_plan")
+    return plan
+
+
+def _prompt_call(name: str, plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                 targets, out, workspace, stream) -> None:
+    rc = getattr(lib(), name)(ctypes.byref(plan), _ptr(logits), dtype_code(dtype), rows, V,
+                              V_pad, _ptr(targets), _ptr(out), _ptr(workspace), _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, name)
+
+
+def flare_prompt_logprobs_run(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                              targets, out, workspace, stream=None) -> None:
+    """Score one prompt chunk on `stream` (default: torch's current stream)."""
+    _prompt_call("flare_prompt_logprobs_run", plan, logits, dtype, rows, V, V_pad, targets, out,
+                 workspace, stream)
+
+
+def flare_prompt_logprobs_reduce(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                                 targets, out, workspace, stream=None) -> None:
+    """The first launch of flare_prompt_logprobs_run (same arguments)."""
+    _prompt_call("flare_prompt_logprobs_reduce", plan, logits, dtype, rows, V, V_pad, targets,
+                 out, workspace, stream)
+
+
+def flare_prompt_logprobs_merge(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                                targets, out, workspace, stream=None) -> None:
+    """The second launch of flare_prompt_logprobs_run (same arguments, after reduce)."""
+    _prompt_call("flare_prompt_logprobs_merge", plan, logits, dtype, rows, V, V_pad, targets,
+                 out, workspace, stream)
+
+
+class PromptPlan:
+    """A validated prompt-scoring geometry plus the shapes its tensors must have."""
+
+    def __init__(self, rows: int, V: int, V_pad: int | None = None, dtype=torch.bfloat16,
+                 device: int | None = None):
+        if device is None:
+            device = torch.cuda.current_device()
+        self.torch_dtype = torch.bfloat16 if dtype_code(dtype) == DTYPE_BF16 else torch.float32
+        self.V_pad = V if V_pad is None else V_pad
+        self.raw = flare_prompt_logprobs_plan(rows, V, self.V_pad, dtype, device)
+        self.rows, self.V, self.device_index = rows, V, device
+
+    @property
+    def device(self) -> torch.device:
+        return torch.device("cuda", self.device_index)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.raw.workspace_bytes)
+
+    def workspace(self) -> torch.Tensor:
+        return torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+
+    def lse(self, workspace: torch.Tensor) -> torch.Tensor:
+        """Diagnostic view: the normalization L of every scored row (valid rows only)."""
+        off = int(self.raw.lse_offset)
+        return workspace[off:off + 4 * self.rows].view(torch.float32)
+
+    def new_out(self, fill: int = 0) -> torch.Tensor:
+        return torch.full((self.rows, PROMPT_ROW_WORDS), fill, dtype=torch.int32,
+                          device=self.device)
+
+    def run(self, logits, targets, out, workspace, stream=None,
+            phase: str = "all") -> torch.Tensor:
+        """Both launches (phase "all"), or only "reduce" or "merge"."""
+        fn = {"all": flare_prompt_logprobs_run, "reduce": flare_prompt_logprobs_reduce,
+              "merge": flare_prompt_logprobs_merge}[phase]
+        dev = self.device
+        _check(logits, "logits", self.torch_dtype, self.rows * self.V_pad, dev)
+        _check(targets, "targets", torch.int32, self.rows, dev)
+        _check(out, "out", torch.int32, self.rows * PROMPT_ROW_WORDS, dev)
+        _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
+        fn(self.raw, logits, self.torch_dtype, self.rows, self.V, self.V_pad, targets, out,
+           workspace, stream)
         return out

@@ -37,8 +37,12 @@ const char* flare_status_string(int status) {
   }
 }
 
-int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, int32_t V,
-                        int32_t V_pad, int32_t dtype, int32_t K, int32_t device) {
+}  // extern "C"
+
+// Both plans: a generation frame (mode 0) or a scored prompt chunk (mode 1,
+// capacity = rows, T = 1, K = 20).
+static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, int32_t V,
+                     int32_t V_pad, int32_t dtype, int32_t K, int32_t device, int32_t mode) {
   if (!plan) return FLARE_ERR_INVALID_ARGUMENT;
   memset(plan, 0, sizeof *plan);
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
@@ -65,7 +69,7 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess) return FLARE_ERR_DEVICE;
     if (prev != device && hipSetDevice(device) != hipSuccess) return FLARE_ERR_DEVICE;
-    per_cu = flp::reduce_occupancy(dtype, vec, capacity);
+    per_cu = flp::reduce_occupancy(dtype, vec, mode == FLARE_MODE_PROMPT, capacity);
     if (prev != device && hipSetDevice(prev) != hipSuccess) return FLARE_ERR_DEVICE;
     if (per_cu < 1) return FLARE_ERR_DEVICE;
   }
@@ -85,6 +89,17 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   plan->vector_rows = vec ? 1 : 0;
   plan->cu_count = cus;
   plan->ranges = plan->grid;
+  plan->mode = mode;
+  if (mode == FLARE_MODE_PROMPT) {
+    // A unit range holds at most ceil(N / grid) units, so it touches at most
+    // ceil((ceil(N / grid) - 1) / units) + 1 rows.
+    const int64_t n = rows * units;
+    const int64_t per = (n + plan->grid - 1) / plan->grid;
+    if ((per - 1 + units - 1) / units + 1 > flp::kMaxRangeRows) {
+      memset(plan, 0, sizeof *plan);
+      return FLARE_ERR_UNSUPPORTED_SIZE;
+    }
+  }
   uint64_t off = 0;
   plan->record_offset = off;
   off = align_up(off + (uint64_t)rows * units * sizeof(flp::PartRecord), kAlign);
@@ -95,6 +110,19 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
   plan->reserved_offset = 0;
   plan->workspace_bytes = off;
   return FLARE_OK;
+}
+
+extern "C" {
+
+int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, int32_t V,
+                        int32_t V_pad, int32_t dtype, int32_t K, int32_t device) {
+  return make_plan(plan, capacity, T, V, V_pad, dtype, K, device, FLARE_MODE_GENERATION);
+}
+
+int flare_prompt_logprobs_plan(flare_logprobs_plan_t* plan, int32_t rows, int32_t V,
+                               int32_t V_pad, int32_t dtype, int32_t device) {
+  return make_plan(plan, rows, 1, V, V_pad, dtype, FLARE_PROMPT_ALTERNATIVES, device,
+                   FLARE_MODE_PROMPT);
 }
 
 }  // extern "C"
@@ -109,6 +137,7 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
       !out || !workspace)
     return FLARE_ERR_INVALID_ARGUMENT;
   if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
+  if (plan->mode != FLARE_MODE_GENERATION) return FLARE_ERR_PLAN_MISMATCH;
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
   if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad || K != plan->K)
     return FLARE_ERR_PLAN_MISMATCH;
@@ -139,7 +168,53 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
   p.workers = plan->ranges;
 
   const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
-  const int e = flp::launch(p, dtype, vec, phases, hip_stream);
+  const int e = flp::launch(p, dtype, vec, false, phases, hip_stream);
+  return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
+}
+
+// The same for a scored prompt chunk.
+static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
+                         int64_t rows, int32_t V, int32_t V_pad, const int32_t* targets,
+                         int32_t* out, void* workspace, void* hip_stream, int phases) {
+  if (!plan || !logits || !targets || !out || !workspace) return FLARE_ERR_INVALID_ARGUMENT;
+  if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
+  if (plan->mode != FLARE_MODE_PROMPT) return FLARE_ERR_PLAN_MISMATCH;
+  if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
+  if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad) return FLARE_ERR_PLAN_MISMATCH;
+  if (rows != (int64_t)plan->capacity || plan->T != 1 || plan->K != FLARE_PROMPT_ALTERNATIVES)
+    return FLARE_ERR_PLAN_MISMATCH;
+  if (plan->grid < 1 || plan->units < 1 || plan->units > flp::kMaxUnits ||
+      plan->ranges != plan->grid || plan->block != flp::kBlock)
+    return FLARE_ERR_PLAN_MISMATCH;
+  {
+    const int64_t per = (rows * plan->units + plan->grid - 1) / plan->grid;
+    if ((per - 1 + plan->units - 1) / plan->units + 1 > flp::kMaxRangeRows)
+      return FLARE_ERR_PLAN_MISMATCH;
+  }
+  if (((uintptr_t)workspace & 15u) != 0) return FLARE_ERR_INVALID_ARGUMENT;
+
+  char* ws = (char*)workspace;
+  flp::Params p;
+  p.logits = logits;
+  p.requested = nullptr;
+  p.id_counts = nullptr;
+  p.ids = nullptr;
+  p.emitted = nullptr;
+  p.tokens = targets;
+  p.out = out;
+  p.records = (flp::PartRecord*)(ws + plan->record_offset);
+  p.lse = (float*)(ws + plan->lse_offset);
+  p.slot_rows = (int32_t*)(ws + plan->slots_offset);
+  p.V_pad = V_pad;
+  p.capacity = plan->capacity;
+  p.T = 1;
+  p.V = V;
+  p.K = FLARE_PROMPT_ALTERNATIVES;
+  p.units = plan->units;
+  p.workers = plan->ranges;
+
+  const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
+  const int e = flp::launch(p, dtype, vec, true, phases, hip_stream);
   return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
 }
 
@@ -171,6 +246,30 @@ int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits, 
                          int32_t* out, void* workspace, void* hip_stream) {
   return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
                     emitted_counts, tokens, K, out, workspace, hip_stream, flp::kPhaseMerge);
+}
+
+int flare_prompt_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
+                              int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                              const int32_t* targets, int32_t* out, void* workspace,
+                              void* hip_stream) {
+  return prompt_phases(plan, logits, dtype, rows, V, V_pad, targets, out, workspace, hip_stream,
+                       flp::kPhaseReduce | flp::kPhaseMerge);
+}
+
+int flare_prompt_logprobs_reduce(const flare_logprobs_plan_t* plan, const void* logits,
+                                 int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                 const int32_t* targets, int32_t* out, void* workspace,
+                                 void* hip_stream) {
+  return prompt_phases(plan, logits, dtype, rows, V, V_pad, targets, out, workspace, hip_stream,
+                       flp::kPhaseReduce);
+}
+
+int flare_prompt_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits,
+                                int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                const int32_t* targets, int32_t* out, void* workspace,
+                                void* hip_stream) {
+  return prompt_phases(plan, logits, dtype, rows, V, V_pad, targets, out, workspace, hip_stream,
+                       flp::kPhaseMerge);
 }
 
 }  // extern "C"

@@ -12,6 +12,9 @@ constexpr int kMergeBlock = 256;    // merge workgroup
 constexpr int kKeep = 32;           // raw keys a part keeps
 constexpr int kMaxUnits = 64;       // units per row (one merge lane per unit)
 constexpr int kMaxCapacity = 8192;  // slots whose active-row prefix fits in LDS
+constexpr int kPromptWords = 43;    // words of one scored prompt row
+constexpr int kPromptAlts = 20;     // alternatives of a scored prompt row
+constexpr int kMaxRangeRows = 64;   // rows one unit range may touch when scoring
 
 // Vocabulary lanes per 16-byte chunk, and per unit: the lanes one workgroup
 // holds in registers at a time (16,384 bf16 or 8,192 FP32 lanes, 32 KiB).
@@ -23,13 +26,15 @@ constexpr int elem_bytes(int dtype) { return dtype == 1 ? 2 : 4; }
 // of one row that one workgroup reduced.  m is the part's max, s the sum of
 // exp(x - m) over its lanes, keys its best raw keys (value, then smaller ID)
 // sorted descending, cut a bound on every key it dropped: each lane it did
-// not keep has a raw key <= cut (0: the part kept every lane).  Stored at
-// records[row * units + first unit of part].
+// not keep has a raw key <= cut (0: the part kept every lane).  When a
+// prompt row is scored, `above` counts the part's lanes whose raw logit
+// exceeds the target's and `next_above` is the smallest such logit (+inf
+// if none).  Stored at records[row * units + first unit of part].
 struct PartRecord {
   float m;
   float s;
-  int32_t n;      // keys held (kKeep unless the part has fewer lanes)
-  int32_t flags;  // reserved (0)
+  int32_t above;     // scoring only (0 otherwise)
+  float next_above;  // scoring only
   uint64_t cut;
   uint64_t keys[kKeep];
 };
@@ -59,9 +64,11 @@ struct Params {
 constexpr int kPhaseReduce = 1;
 constexpr int kPhaseMerge = 2;
 // Launcher implemented in flp_kernels.hip; returns a hipError_t as int.
-int launch(const Params& p, int dtype, bool vector_rows, int phases, void* stream);
+// `score` selects prompt scoring: one row per slot (T = 1), a row is active
+// when its target (tokens[s]) is a vocabulary ID, K = 20, kPromptWords per row.
+int launch(const Params& p, int dtype, bool vector_rows, bool score, int phases, void* stream);
 // Resident reduction workgroups per CU (0 on error).
-int reduce_occupancy(int dtype, bool vector_rows, int capacity);
+int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity);
 size_t prefix_lds_bytes(int capacity);
 
 }  // namespace flp

@@ -251,6 +251,16 @@ __device__ __forceinline__ float wave_sum(float v, int lane) {
   return v;
 }
 
+__device__ __forceinline__ int wave_sum_i32(int v, int lane) {
+  v += (int)xlane<32>((uint32_t)v, lane);
+  v += (int)xlane<16>((uint32_t)v, lane);
+  v += (int)xlane<8>((uint32_t)v, lane);
+  v += (int)xlane<4>((uint32_t)v, lane);
+  v += (int)xlane<2>((uint32_t)v, lane);
+  v += (int)xlane<1>((uint32_t)v, lane);
+  return v;
+}
+
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -405,7 +415,13 @@ __device__ __forceinline__ void cand_append(CandBuf& cb, Best32& b, uint64_t k, 
 constexpr int kSelBit = (int)0x80000000u;
 constexpr int kRowsMask = 0x7FFFFFFF;
 
+// A scored prompt row (one per slot) is active when its target is an ID.
+template <bool SCORE>
 __device__ __forceinline__ int slot_word(const Params& p, int s) {
+  if (SCORE) {
+    const int tk = p.tokens[s];
+    return (tk >= 0 && tk < p.V) ? 1 : 0;
+  }
   // The three words are loaded together (one round trip).
   const int r = p.requested[s], e = p.emitted[s], n = p.id_counts[s];
   const int rows = r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
@@ -415,7 +431,7 @@ __device__ __forceinline__ int slot_word(const Params& p, int s) {
 // prefix[s] = active rows of slots before s (with slot s's selection bit);
 // prefix[capacity] = total.  All NW waves of the workgroup take part; `scan`
 // is NW ints of LDS.
-template <int NW>
+template <int NW, bool SCORE>
 __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
   constexpr int NT = NW * 64;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -425,7 +441,7 @@ __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
   const int s1 = s0 + per < cap ? s0 + per : cap;
   int local = 0;
   for (int s = s0; s < s1; ++s) {
-    const int c = slot_word(p, s);
+    const int c = slot_word<SCORE>(p, s);
     prefix[s] = c;
     local += c & kRowsMask;
   }
@@ -527,7 +543,37 @@ __device__ __forceinline__ void rescan_lanes(uint64_t& top, uint64_t& thr, const
   }
 }
 
+// Lanes [lo, hi) of a row whose reported value exceeds rt, summed over the
+// wave (every lane gets the total).  One 16-byte chunk per lane per step.
 template <int DT, bool VEC>
+__device__ __forceinline__ int count_above(const char* rowp, int lo, int hi, float L, float rt,
+                                           int lane) {
+  using E = Elem<DT>;
+  constexpr int kPer = E::kPer;
+  int n = 0;
+  for (int b = lo; b < hi; b += 64 * kPer) {
+    const int first = b + lane * kPer;
+    if (first < hi) {
+      const u32x4 r = load_chunk<DT, VEC>(rowp, first, hi);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) n += reported(E::get(r, j), L) > rt ? 1 : 0;
+    }
+  }
+  return wave_sum_i32(n, lane);
+}
+
+// With SCORE the rows are the scored rows of a prompt chunk (T = 1): a row
+// whose target is not an ID gets its fixed invalid record, the others the
+// target's pair, its rank (one plus the count of lanes whose reported value
+// exceeds the target's) and the top twenty, kPromptWords words in all.
+//
+// Rank.  The reduction counted, per part, the lanes whose raw logit exceeds
+// the target's, x_t, and kept the smallest of them, x_n.  r(x) = fl32(x - L)
+// is monotone, so no lane at or below x_t can report more than r(x_t), and a
+// lane above x_t reports at least r(x_n) >= r(x_t); the raw count is exact
+// unless r(x_n) == r(x_t) (the subtraction tied them), and such a part is
+// counted again lane by lane with reported values.
+template <int DT, bool VEC, bool SCORE>
 __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kUnitElems = kUnitThreads * kChunks * E::kPer;
@@ -539,16 +585,23 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int s = row / p.T, t = row - s * p.T;
   // Every input word this row needs, loaded at once (the row counts are
   // only meaningful for an active row).
-  const int req = p.requested[s], emi = p.emitted[s], cnt = p.id_counts[s];
+  const int req = SCORE ? 1 : p.requested[s], emi = SCORE ? 1 : p.emitted[s];
+  const int cnt = SCORE ? 0 : p.id_counts[s];
   const int before = p.slot_rows[s], total = p.slot_rows[p.capacity];
   const int tok = p.tokens[row];
+  const int V = p.V, U = p.units;
+  int32_t* out = p.out + (int64_t)row * (SCORE ? kPromptWords : kRowWords);
+  if (SCORE && !(tok >= 0 && tok < V)) {
+    // [-1, NaN, rank 0, then (-1, NaN) twenty times]
+    if (lane < kPromptWords)
+      out[lane] = lane == 2 ? 0 : ((lane == 0 || (lane >= 3 && (lane & 1))) ? -1 : (int32_t)kNanBits);
+    return;
+  }
   if (req == 0 || t >= (emi < 0 ? 0 : (emi > p.T ? p.T : emi))) return;
   const int n_sel = cnt < 0 ? 0 : (cnt > 128 ? 128 : cnt);
   const bool natural = p.K > 0 && n_sel == 0;
-  const int V = p.V, U = p.units;
   const PartRecord* rec = p.records + (int64_t)row * U;
   const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * E::kBytes;
-  int32_t* out = p.out + (int64_t)row * kRowWords;
   int16_t* part_u0 = part_u0_all[wv];
 
   // ---- the row's parts (one lane per unit): a part starts at the row's
@@ -568,10 +621,16 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // first four parts' kept keys and each part's guard words
   float pm = kNegInf, ps = 0.0f;
   uint64_t c_key = 0ull;
+  int p_above = 0;
+  float p_next = __builtin_huge_valf();
   if (lane < np) {
     pm = rec[u0].m;
     ps = rec[u0].s;
     c_key = rec[u0].cut;
+    if (SCORE) {
+      p_above = rec[u0].above;
+      p_next = rec[u0].next_above;
+    }
   }
   const uint64_t raw0 = (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
   const uint64_t raw1 = 2 + (lane >> 5) < np ? rec[part_u0[2 + (lane >> 5)]].keys[lane & 31] : 0ull;
@@ -598,10 +657,25 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
     out[0] = tok;
     out[1] = (int32_t)(tok >= 0 && tok < V ? __float_as_uint(reported(x_tok, L)) : kNanBits);
   }
+  if (SCORE) {
+    const float rt = reported(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x_tok), 0)), L);
+    uint64_t ties = __ballot(lane < np && p_next < __builtin_huge_valf() && reported(p_next, L) == rt);
+    while (ties != 0ull) {
+      const int part = __builtin_ctzll(ties);
+      ties &= ties - 1ull;
+      const int lo = part_u0[part] * kUnitElems;
+      int hi = part_u0[part + 1] * kUnitElems;
+      hi = hi < V ? hi : V;
+      const int exact = count_above<DT, VEC>(rowp, lo, hi, L, rt, lane);
+      if (lane == part) p_above = exact;
+    }
+    const int greater = wave_sum_i32(lane < np ? p_above : 0, lane);
+    if (lane == 0) out[2] = 1 + greater;
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int j = lane + 64 * h;
-    if (j < n_sel) {
+    if (!SCORE && j < n_sel) {
       const uint32_t bits = sel_id[h] >= 0 && sel_id[h] < V ? __float_as_uint(reported(x_sel[h], L))
                                                             : kNanBits;
       *(int2*)(out + 2 + 2 * j) = make_int2(sel_id[h], (int32_t)bits);
@@ -663,7 +737,12 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       id = (int32_t)key_id(top);
       bits = __float_as_uint(unkey32((uint32_t)(top >> 32)));
     }
-    *(int2*)(out + 2 + 2 * lane) = make_int2(id, (int32_t)bits);
+    if (SCORE) {  // after the rank word: pairs start at an odd word
+      out[3 + 2 * lane] = id;
+      out[4 + 2 * lane] = (int32_t)bits;
+    } else {
+      *(int2*)(out + 2 + 2 * lane) = make_int2(id, (int32_t)bits);
+    }
   }
 }
 
@@ -690,6 +769,8 @@ struct ReduceSmem {
   uint64_t flush_cut[2][kWaves];         // a part's per-wave cut, by part parity
   float wm[2][kWaves];                   // a part's per-wave max and scaled sum
   float ws[2][kWaves];
+  int wabove[2][kWaves];                 // scoring: a part's per-wave count above the target
+  float wnext[2][kWaves];                // and smallest logit above it
   int arrive[2];                         // waves that flushed the part of this parity
   int merged;                            // parts of the range merged into records
   int n_staged;                          // records staged in `staged`
@@ -879,13 +960,16 @@ struct PassOut {
 // the chunks that reach the threshold.  The first sweep waits for the whole
 // unit, which only delays that unit's refills.  `ht`, `stage` and `o.tau`
 // return the threshold and its test.
-template <int DT, bool VEC>
+// With SCORE, a chunk whose maximum exceeds xa (the target's logit) also
+// adds its lanes above xa to `above` and their minimum to `next_above`.
+template <int DT, bool VEC, bool SCORE>
 __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[kChunks],
                                              float m_l, bool tail, int wave_base,
                                              __amdgpu_buffer_rsrc_t next_rsrc,
                                              const char* next_rowp, int next_base, bool has_next,
                                              int V, int lane, bool& stage, HotTest& ht, Stage& st,
-                                             bool first, int kq) {
+                                             bool first, int kq, float xa, int& above,
+                                             float& next_above) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   PassOut o;
@@ -931,6 +1015,15 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
       o.acc += __builtin_amdgcn_exp2f(__builtin_fmaf(xv, kLog2e, o.nb));
     }
     cm[c] = mc;
+    if (SCORE && __ballot(mc > xa) != 0ull) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const float xv = E::get(raw[c], j);
+        const bool gt = xv > xa;
+        above += gt ? 1 : 0;
+        next_above = gt ? fminf(next_above, xv) : next_above;
+      }
+    }
     if (stage) stage_chunk(st, raw[c], mc > ht.above, c, lane);
     {
       int lane_dep = lane;
@@ -1031,7 +1124,7 @@ __device__ __forceinline__ void lds_store64(uint64_t* a, uint64_t v) {
 }
 
 // Four waves per workgroup, five workgroups per CU: at most 96 VGPRs per lane.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool SCORE>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) void reduce_kernel(
     Params p) {
   using E = Elem<DT>;
@@ -1048,7 +1141,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   if (tid < 2) sh.arrive[tid] = 0;
   if (tid == 0) sh.merged = 0;
   if (tid == 0) sh.n_staged = 0;
-  const int total = build_prefix<kWaves>(p, prefix, sh.scan);
+  const int total = build_prefix<kWaves, SCORE>(p, prefix, sh.scan);
   // The slots' active-row counts before them, and the total, for the merge.
   if (blockIdx.x == 0)
     for (int s = tid; s <= p.capacity; s += kBlock) p.slot_rows[s] = prefix[s] & kRowsMask;
@@ -1067,6 +1160,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     refill_chunk<DT, VEC>(raw[c], row_rsrc(cur.rowp, row_bytes), cur.rowp,
                           cur.u * kUnitElems + w * kWaveElems, c, lane_id, V, true);
   bool natural = p.K > 0 && (prefix[cur.s] & kSelBit) == 0;
+
+  // Scoring: lane i holds the target logit of the range's i-th row (the
+  // host keeps a range within kMaxRangeRows rows); each lane counts its
+  // part's lanes above it.
+  const int a_first = x0 / U;
+  float xa_lane = 0.0f;
+  if (SCORE) {
+    const int a = a_first + lane_id;
+    if (lane_id < kMaxRangeRows && (int64_t)a * U < x1) {
+      const int s = slot_of(prefix, p.capacity, a);
+      xa_lane = load_elem<DT>((const char*)p.logits + (int64_t)s * p.V_pad * E::kBytes, p.tokens[s]);
+    }
+  }
+  int above = 0;
+  float next_above = __builtin_huge_valf();
 
   // Per lane: running max m_l and the sum, relative to m_l, of exp over the
   // lane's values except one occurrence of m_l (whose term is exactly 1 and
@@ -1147,10 +1255,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
 
     st.n = 0;
     float cm[kChunks];
-    const PassOut po =
-        unit_pass<DT, VEC>(raw, cm, m_l, tail, wave_base, row_rsrc(nxt.rowp, has_next ? row_bytes : 0),
-                           nxt.rowp, next_base, has_next, V, lane, stage, ht, st,
-                           natural && part_starts, kfirst);
+    const float xa =
+        SCORE ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(xa_lane), cur.a - a_first))
+              : 0.0f;
+    const PassOut po = unit_pass<DT, VEC, SCORE>(
+        raw, cm, m_l, tail, wave_base, row_rsrc(nxt.rowp, has_next ? row_bytes : 0), nxt.rowp,
+        next_base, has_next, V, lane, stage, ht, st, natural && part_starts, kfirst, xa, above,
+        next_above);
     const float lm = po.lm;
 
     // ---- fold the unit into the lane's running (max, sum)
@@ -1233,6 +1344,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
           sh.wm[b][w] = M;
           sh.ws[b][w] = S;
         }
+        if (SCORE) {
+          const int na = wave_sum_i32(above, lane);
+          float nx = next_above;
+          nx = fminf(nx, xlanef<32>(nx, lane));
+          nx = fminf(nx, xlanef<16>(nx, lane));
+          nx = fminf(nx, xlanef<8>(nx, lane));
+          nx = fminf(nx, xlanef<4>(nx, lane));
+          nx = fminf(nx, xlanef<2>(nx, lane));
+          nx = fminf(nx, xlanef<1>(nx, lane));
+          if (lane == 0) {
+            sh.wabove[b][w] = na;
+            sh.wnext[b][w] = nx;
+          }
+        }
       }
       if (natural && lane < kKeep) sh.flush_keys[b][w][lane] = best.top;
       if (lane == 0) sh.flush_cut[b][w] = natural ? cut : 0ull;
@@ -1267,10 +1392,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
               if (sh.wm[b][i] != kNegInf)
                 S += sh.ws[b][i] * __builtin_amdgcn_exp2f((sh.wm[b][i] - M) * kLog2e);
           for (int i = 0; i < kWaves; ++i) pcut = sh.flush_cut[b][i] > pcut ? sh.flush_cut[b][i] : pcut;
+          int na = 0;
+          float nx = __builtin_huge_valf();
+          if (SCORE)
+            for (int i = 0; i < kWaves; ++i) {
+              na += sh.wabove[b][i];
+              nx = fminf(nx, sh.wnext[b][i]);
+            }
           rec->m = M;
           rec->s = S;
-          rec->n = held;
-          rec->flags = 0;
+          rec->above = na;
+          rec->next_above = nx;
           rec->cut = pcut;
           sr->dst = cur.row * U + part_u0;
           sr->natural = natural;
@@ -1303,6 +1435,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         published = 0ull;
         first_bar = 0ull;
         cut = 0ull;
+        above = 0;
+        next_above = __builtin_huge_valf();
         part_u0 = nxt.u;
         natural = p.K > 0 && (prefix[nxt.s] & kSelBit) == 0;
       }
@@ -1311,18 +1445,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   }
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool SCORE>
 hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
   if (phases & kPhaseReduce) {
     const size_t lds = prefix_lds_bytes(p.capacity);
-    hipLaunchKernelGGL((reduce_kernel<DT, VEC>), dim3((uint32_t)p.workers), dim3(kBlock), lds,
+    hipLaunchKernelGGL((reduce_kernel<DT, VEC, SCORE>), dim3((uint32_t)p.workers), dim3(kBlock), lds,
                        st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(phases & kPhaseMerge)) return hipSuccess;
   const int64_t rows = (int64_t)p.capacity * p.T;
-  hipLaunchKernelGGL((merge_kernel<DT, VEC>), dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)),
+  hipLaunchKernelGGL((merge_kernel<DT, VEC, SCORE>), dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)),
                      dim3(kMergeBlock), 0, st, p);
   return hipGetLastError();
 }
@@ -1331,30 +1465,38 @@ hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
 
 size_t prefix_lds_bytes(int capacity) { return (size_t)(capacity + 1) * sizeof(int); }
 
-int reduce_occupancy(int dtype, bool vector_rows, int capacity) {
+template <int DT, bool VEC, bool SCORE>
+int occupancy_typed(size_t lds) {
   int n = 0;
-  const size_t lds = prefix_lds_bytes(capacity);
-  hipError_t e;
-  if (dtype == 1)
-    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<1, true>,
-                                                                   kBlock, lds)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<1, false>,
-                                                                   kBlock, lds);
-  else
-    e = vector_rows ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<0, true>,
-                                                                   kBlock, lds)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<0, false>,
-                                                                   kBlock, lds);
+  const hipError_t e =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_kernel<DT, VEC, SCORE>, kBlock, lds);
   return e == hipSuccess ? n : 0;
 }
 
-int launch(const Params& p, int dtype, bool vector_rows, int phases, void* stream) {
+int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity) {
+  const size_t lds = prefix_lds_bytes(capacity);
+  if (dtype == 1) {
+    if (score) return vector_rows ? occupancy_typed<1, true, true>(lds) : occupancy_typed<1, false, true>(lds);
+    return vector_rows ? occupancy_typed<1, true, false>(lds) : occupancy_typed<1, false, false>(lds);
+  }
+  if (score) return vector_rows ? occupancy_typed<0, true, true>(lds) : occupancy_typed<0, false, true>(lds);
+  return vector_rows ? occupancy_typed<0, true, false>(lds) : occupancy_typed<0, false, false>(lds);
+}
+
+int launch(const Params& p, int dtype, bool vector_rows, bool score, int phases, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (dtype == 1)
-    e = vector_rows ? launch_typed<1, true>(p, phases, st) : launch_typed<1, false>(p, phases, st);
-  else
-    e = vector_rows ? launch_typed<0, true>(p, phases, st) : launch_typed<0, false>(p, phases, st);
+  if (dtype == 1) {
+    if (score)
+      e = vector_rows ? launch_typed<1, true, true>(p, phases, st) : launch_typed<1, false, true>(p, phases, st);
+    else
+      e = vector_rows ? launch_typed<1, true, false>(p, phases, st) : launch_typed<1, false, false>(p, phases, st);
+  } else {
+    if (score)
+      e = vector_rows ? launch_typed<0, true, true>(p, phases, st) : launch_typed<0, false, true>(p, phases, st);
+    else
+      e = vector_rows ? launch_typed<0, true, false>(p, phases, st) : launch_typed<0, false, false>(p, phases, st);
+  }
   return (int)e;
 }
 

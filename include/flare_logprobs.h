@@ -45,11 +45,18 @@
 extern "C" {
 #endif
 
-#define FLARE_LOGPROBS_ABI_VERSION 2u
+#define FLARE_LOGPROBS_ABI_VERSION 3u
 #define FLARE_LOGPROBS_MAX_K 20
 #define FLARE_LOGPROBS_MAX_IDS 128
 #define FLARE_LOGPROBS_ROW_WORDS 258 /* 2 + 2 * 128 */
 #define FLARE_LOGPROBS_NAN_BITS 0x7FC00000u
+#define FLARE_PROMPT_ROW_WORDS 43     /* 3 + 2 * 20 */
+#define FLARE_PROMPT_ALTERNATIVES 20
+
+enum flare_mode {
+  FLARE_MODE_GENERATION = 0, /* flare_logprobs_plan: emitted verify positions */
+  FLARE_MODE_PROMPT = 1      /* flare_prompt_logprobs_plan: scored prompt rows */
+};
 
 enum flare_dtype {
   FLARE_DTYPE_FP32 = 0, /* IEEE binary32 logits */
@@ -88,7 +95,7 @@ typedef struct flare_logprobs_plan {
   int32_t vector_rows;   /* 1 if V_pad * element size is a multiple of 16 */
   int32_t cu_count;      /* compute units of `device` (256 if host-only) */
   int32_t ranges;        /* contiguous unit ranges of the launch (== grid) */
-  int32_t reserved0;
+  int32_t mode;          /* enum flare_mode: which run entry points accept it */
   uint64_t workspace_bytes; /* bytes of device workspace the caller provides */
   uint64_t record_offset;   /* per-(row, unit) part records */
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
@@ -159,6 +166,49 @@ int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits,
                          const int32_t* ids, const int32_t* emitted_counts,
                          const int32_t* tokens, int32_t K, int32_t* out,
                          void* workspace, void* hip_stream);
+
+/*
+ * Prompt scoring (Flare generation-logprobs design page, prompt-logprobs
+ * paragraphs: scored prefill).  For each of `rows` prompt positions, with
+ * x the raw logit row and t = targets[r] the prompt token that follows it:
+ *     out[r] = [t, bits(lp(t)), rank, id_0, bits_0, ..., id_19, bits_19]
+ * where lp is the same fl32(x - L) as above, rank = 1 + the number of lanes
+ * in [0, V) whose lp is strictly greater than lp(t) (equal values, ties the
+ * subtraction creates included, do not count), and the twenty alternatives
+ * follow the generation order (decreasing lp, then increasing ID; when V < 20
+ * the unused pairs are (-1, 0x7FC00000)).  A row whose target is outside
+ * [0, V) (-1 at the prompt end and inside image spans) reads no logits and is
+ * written as [-1, 0x7FC00000, 0, then (-1, 0x7FC00000) twenty times].
+ *
+ * flare_prompt_logprobs_plan validates 1 <= rows <= 8192 and the other
+ * geometry as flare_logprobs_plan does (its plan has capacity = rows, T = 1,
+ * K = 20 and mode FLARE_MODE_PROMPT; FLARE_ERR_UNSUPPORTED_SIZE also when a
+ * launch range would touch more than 64 rows, which needs far more rows than
+ * a GPU's workgroups) and sizes its workspace.
+ *   logits     device, [rows, V_pad] of `dtype`, row-major, read only
+ *   rows, dtype, V, V_pad   must equal the plan's (FLARE_ERR_PLAN_MISMATCH)
+ *   targets    device int32 [rows]
+ *   out        device int32 [rows, 43]; every row is written
+ *   workspace  device, plan->workspace_bytes, 16-byte aligned, no initialisation
+ * Ownership, errors, streams and graph capture are as for flare_logprobs_run;
+ * a plan of one mode is rejected by the other mode's entry points.  _reduce
+ * and _merge are the two launches of _run, with the same contract as
+ * flare_logprobs_reduce and flare_logprobs_merge.
+ */
+int flare_prompt_logprobs_plan(flare_logprobs_plan_t* plan, int32_t rows, int32_t V,
+                               int32_t V_pad, int32_t dtype, int32_t device);
+int flare_prompt_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
+                              int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                              const int32_t* targets, int32_t* out, void* workspace,
+                              void* hip_stream);
+int flare_prompt_logprobs_reduce(const flare_logprobs_plan_t* plan, const void* logits,
+                                 int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                 const int32_t* targets, int32_t* out, void* workspace,
+                                 void* hip_stream);
+int flare_prompt_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits,
+                                int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                const int32_t* targets, int32_t* out, void* workspace,
+                                void* hip_stream);
 
 /* Human-readable name of a flare_status value (static storage). */
 const char* flare_status_string(int status);

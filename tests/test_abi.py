@@ -34,7 +34,9 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert {"flare_logprobs_plan", "flare_logprobs_run", "flare_logprobs_reduce",
             "flare_logprobs_merge", "flare_status_string",
-            "flare_logprobs_abi_version"} <= set(names)
+            "flare_logprobs_abi_version", "flare_prompt_logprobs_plan",
+            "flare_prompt_logprobs_run", "flare_prompt_logprobs_reduce",
+            "flare_prompt_logprobs_merge"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(flp):
@@ -65,7 +67,8 @@ def test_plan_host_only_geometry(flp):
     rc, p = host_plan(flp)
     assert rc == 0
     assert p.units == 16 and p.unit_elems == 16384 and p.block == 256 and p.vector_rows == 1
-    assert p.cu_count == 256 and p.abi_version == 2 and p.grid == 1024 and p.ranges == 1024
+    assert p.cu_count == 256 and p.abi_version == flp.ABI_VERSION and p.grid == 1024
+    assert p.ranges == 1024 and p.mode == flp.MODE_GENERATION
     rows = 128 * 8
     assert p.lse_offset >= rows * 16 * 280 and p.slots_offset >= p.lse_offset + 4 * rows
     assert p.slots_offset % 16 == 0 and p.reserved_offset == 0
@@ -157,6 +160,72 @@ def test_run_rejects_corrupt_plan(flp, entry):
 def test_run_rejects_misaligned_workspace(flp, entry):
     rc, plan = host_plan(flp)
     assert run_status(flp, plan, workspace=FAKE + 4) == 1
+
+
+# ------------------------------------------------------------ prompt scoring
+def prompt_plan(flp, rows=128, V=248320, V_pad=248320, dtype=1):
+    plan = flp.PlanStruct()
+    rc = flp.lib().flare_prompt_logprobs_plan(ctypes.byref(plan), rows, V, V_pad, dtype, -1)
+    return rc, plan
+
+
+def prompt_status(flp, plan, entry="flare_prompt_logprobs_run", **over):
+    args = dict(logits=FAKE, dtype=plan.dtype, rows=plan.capacity, V=plan.V, V_pad=plan.V_pad,
+                targets=FAKE, out=FAKE, workspace=FAKE, stream=None)
+    args.update(over)
+    return getattr(flp.lib(), entry)(ctypes.byref(plan), args["logits"], args["dtype"],
+                                     args["rows"], args["V"], args["V_pad"], args["targets"],
+                                     args["out"], args["workspace"], args["stream"])
+
+
+def test_prompt_plan_geometry(flp):
+    rc, p = prompt_plan(flp)
+    assert rc == 0 and p.mode == flp.MODE_PROMPT and p.T == 1 and p.K == 20
+    assert p.capacity == 128 and p.units == 16 and p.grid == 1024
+    assert p.lse_offset >= 128 * 16 * 280 and p.slots_offset >= p.lse_offset + 4 * 128
+    assert p.workspace_bytes >= p.slots_offset + 4 * 129
+    rc, p = prompt_plan(flp, rows=8192, V=151936, V_pad=152064, dtype=0)
+    assert rc == 0 and p.units == 19 and p.vector_rows == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=0), 1), (dict(rows=8193), 1), (dict(V=0), 1), (dict(V_pad=5, V=6), 1),
+    (dict(dtype=3), 2), (dict(V=16384 * 64 + 1, V_pad=16384 * 64 + 1), 6),
+])
+def test_prompt_plan_rejects(flp, kw, status):
+    rc, p = prompt_plan(flp, **kw)
+    assert rc == status and p.abi_version == 0
+    assert flp.lib().flare_prompt_logprobs_plan(None, 1, 1, 1, 0, -1) == 1
+
+
+@pytest.mark.parametrize("pentry", ["flare_prompt_logprobs_run", "flare_prompt_logprobs_reduce",
+                                    "flare_prompt_logprobs_merge"])
+def test_prompt_run_rejects(flp, pentry):
+    rc, plan = prompt_plan(flp)
+    assert rc == 0
+    for field in ("logits", "targets", "out", "workspace"):
+        assert prompt_status(flp, plan, pentry, **{field: None}) == 1
+    for over in (dict(dtype=0), dict(V=1000), dict(V_pad=248328), dict(rows=127)):
+        assert prompt_status(flp, plan, pentry, **over) == 3
+    assert prompt_status(flp, plan, pentry, dtype=9) == 2
+    assert prompt_status(flp, plan, pentry, workspace=FAKE + 8) == 1
+    bad = flp.PlanStruct.from_buffer_copy(plan)
+    bad.T = 2
+    assert prompt_status(flp, bad, pentry) == 3
+    bad = flp.PlanStruct.from_buffer_copy(plan)
+    bad.abi_version = 2
+    assert prompt_status(flp, bad, pentry) == 3
+
+
+def test_plans_are_not_interchangeable(flp):
+    """A generation plan is rejected by the prompt entry points and a prompt
+    plan by the generation ones."""
+    rc, gplan = host_plan(flp, capacity=128, T=1, K=20)
+    assert rc == 0
+    assert prompt_status(flp, gplan) == 3
+    rc, pplan = prompt_plan(flp)
+    assert rc == 0
+    assert run_status(flp, pplan) == 3
 
 
 def test_binding_names_mirror_the_abi(flp):
