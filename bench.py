@@ -14,6 +14,10 @@ that launch on the launch stream), and the CPU oracle timed on a bounded sample
 of the same rows.  The HBM traffic of the reduction launch comes from the
 rocprofv3 counter summary under profiles/, and only while the kernel source is
 the one those counters were taken on.
+
+`--prompt P1` (or P2) measures prompt scoring instead: one step scores one
+prefill chunk (P1: 128 rows x V=248,320 bf16, each row's target logprob, rank
+and twenty alternatives), reported the same way in its own JSON line.
 """
 from __future__ import annotations
 
@@ -31,7 +35,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = ("full_vocab_logprob_amd/csrc/flp_kernels.hip",
                   "full_vocab_logprob_amd/csrc/flp_internal.h")
-TRAFFIC_SUMMARY = "profiles/reduce_kernel_speculative_verify_bf16_K20.txt"
+TRAFFIC_SUMMARIES = {"C3": "profiles/reduce_kernel_speculative_verify_bf16_K20.txt",
+                     "P1": "profiles/reduce_kernel_prompt_scoring_bf16.txt"}
 
 
 def kernel_source_hash() -> str:
@@ -46,7 +51,9 @@ def measured_traffic(config: str):
     """HBM bytes per reduction launch from the committed counter summary, or
     None when the summary is missing, covers another workload, or was taken
     on a different kernel source."""
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if config not in TRAFFIC_SUMMARIES:
+        return None
+    path = os.path.join(ROOT, TRAFFIC_SUMMARIES[config])
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -79,7 +86,173 @@ def parse():
                          "three times (scales HBM byte counters; 0 disables it)")
     ap.add_argument("--graph", type=int, default=1,
                     help="also time the calls replayed from one captured HIP graph (0: skip)")
+    ap.add_argument("--prompt", default=None,
+                    help="measure prompt scoring on this chunk (P1 or P2) instead")
     return ap.parse_args()
+
+
+def copy_kernel(dev, mib):
+    """A kernel of known traffic (reads and writes `mib` MiB each) so that
+    profiler byte counters can be converted into bytes."""
+    import torch
+    src = torch.ones(mib * (1 << 18), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def bench_prompt(args):
+    """Prompt scoring: the same three timed regions as the generation bench."""
+    import numpy as np
+    import torch
+
+    import __graft_entry__
+    __graft_entry__._ensure_built()
+    import full_vocab_logprob_amd as flp
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    spec = synth.PROMPT_CONFIGS[args.prompt]
+    bf16 = spec.dtype == synth.BF16
+    print(f"[bench] generating {spec.name}: {spec.description}", file=sys.stderr, flush=True)
+    w = synth.make_prompt(spec)
+    valid = w.valid_rows()
+    algo_bytes = w.algorithmic_bytes()
+    lg = torch.from_numpy(w.logits.view(np.int16) if bf16 else w.logits).to(dev)
+    lg = (lg.view(torch.bfloat16) if bf16 else lg).reshape(-1)
+    copies = [lg] + [lg.clone() for _ in range(1, args.copies)]
+    targets = torch.from_numpy(np.ascontiguousarray(w.targets, np.int32)).to(dev)
+    plan = flp.PromptPlan(w.rows, spec.V, spec.V_pad,
+                          dtype=torch.bfloat16 if bf16 else torch.float32, device=0)
+    ws = plan.workspace()
+    out = plan.new_out(int(synth.POISON))
+    stream = torch.cuda.current_stream()
+
+    def step(i, phase="all"):
+        plan.run(copies[i % len(copies)], targets, out, ws, phase=phase)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    checked = 0
+    vrows = np.nonzero((w.targets >= 0) & (w.targets < spec.V))[0]
+    if args.check_rows > 0:
+        import oracle
+        o = oracle.get()
+        for r in vrows[:: max(1, len(vrows) // args.check_rows)][: args.check_rows]:
+            words, _ = o.prompt_row(w.logits[r], int(w.targets[r]), V=spec.V)
+            g_ = got[r]
+            assert g_[0] == words[0] and g_[2] == words[2], f"bench check: row {r}"
+            assert np.array_equal(g_[3::2], words[3::2]), f"bench check: ids differ on row {r}"
+            gv = np.concatenate([g_[1:2], g_[4::2]]).view(np.float32).astype(np.float64)
+            rv = np.concatenate([words[1:2], words[4::2]]).view(np.float32).astype(np.float64)
+            assert np.all(np.abs(gv - rv) <= 2e-5), f"values differ on row {r}"
+            checked += 1
+
+    K = args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(K):
+        step(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / K
+
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record(stream)
+        step(args.warmup + i, "reduce")
+        ev[i][1].record(stream)
+        step(args.warmup + i, "merge")
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    reduce_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    merge_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    mean_reduce_ms = sum(reduce_ms) / K
+
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(gr, stream=side):
+                for c in range(len(copies)):
+                    plan.run(copies[c], targets, out, ws)
+        torch.cuda.synchronize()
+        reps = max(1, K // len(copies))
+        for _ in range(2):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        per_call = g0.elapsed_time(g1) / (reps * len(copies))
+        graph = {"ms_per_call": per_call, "rows_per_s": w.rows / (per_call / 1e3),
+                 "calls": reps * len(copies)}
+        del gr
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        o = oracle.get()
+        n = 0
+        c0 = time.perf_counter()
+        while n < w.rows and time.perf_counter() - c0 < args.cpu_seconds:
+            o.prompt_row(w.logits[n], int(w.targets[n]), V=spec.V)
+            n += 1
+        dt = time.perf_counter() - c0
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} rows of {spec.name} (of {w.rows}, {valid} valid), "
+                         f"single-threaded oracle, {dt:.1f} s"}
+    if args.copy_mib > 0:
+        copy_kernel(dev, args.copy_mib)
+
+    achieved = algo_bytes / (mean_reduce_ms / 1e3) / 1e9
+    res = {
+        "metric": f"scored prompt rows/s and achieved HBM GB/s (% of peak) at V={spec.V}, "
+                  f"{w.rows}-row chunk",
+        "value": w.rows / (ms_per_step / 1e3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "fp32",
+        "data": "synthetic (seeded logits + peak; targets: half the peak lane, half uniform, "
+                "an image span and the prompt end invalid)",
+        "config": {"workload": f"{spec.name}: {w.rows} rows x V={spec.V} "
+                               f"{'bf16' if bf16 else 'fp32'}, prompt scoring",
+                   "rows": w.rows, "valid_rows": valid, "V": spec.V, "copies": len(copies),
+                   "oracle_rows_checked": checked},
+        "roofline": {"bound": "hbm", "kernel": "reduce_kernel (scoring)", "achieved": achieved,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": measured_traffic(spec.name)},
+        "reduce_ms": {"mean": mean_reduce_ms, "median": reduce_ms[K // 2],
+                      "p10": reduce_ms[K // 10], "p90": reduce_ms[(9 * K) // 10]},
+        "merge_ms": {"mean": sum(merge_ms) / K, "median": merge_ms[K // 2]},
+        "graph_replay": graph,
+        "algorithmic_bytes_per_launch": algo_bytes,
+        "wall_s": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
 
 
 def main():
@@ -89,6 +262,9 @@ def main():
               "exchange, so N GPUs run N independent copies; multi-GPU runs are not "
               "part of this build (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.prompt:
+        bench_prompt(args)
+        return
 
     import numpy as np
     import torch
@@ -236,14 +412,7 @@ def main():
                          f"single-threaded oracle, {dt:.1f} s"}
 
     if args.copy_mib > 0:
-        # A kernel of known traffic (reads and writes copy_mib MiB each) so that
-        # profiler byte counters can be converted into bytes.
-        src = torch.ones(args.copy_mib * (1 << 18), dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_kernel(dev, args.copy_mib)
 
     res = {
         "metric": "logprob rows/s and achieved HBM GB/s (% of peak) at V=248,320, T=8, 128 slots",

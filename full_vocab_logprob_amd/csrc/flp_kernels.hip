@@ -12,7 +12,8 @@
 // reduce_kernel: a persistent launch of `grid` 256-thread workgroups (five
 // per CU).  The work is the concatenation, over active rows, of each row's
 // units (16,384 bf16 or 8,192 FP32 lanes, 32 KiB); workgroup g owns the
-// contiguous unit range [g N / grid, (g + 1) N / grid), so every workgroup
+// contiguous unit range [g N / R, (g + 1) N / R), R = grid once N >= 2 grid
+// (fewer units: one or two per range, see range_count), so every workgroup
 // streams the same number of bytes and a range may cross rows.  The units of
 // one row inside one range form a part.
 //   Per unit, each thread holds 8 x 16-byte chunks (coalesced dwordx4 loads)
@@ -498,6 +499,7 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
 // either test is rescanned lane by lane with final keys; F_K over a subset
 // never exceeds the true K-th key, so the test stays sound.
 constexpr int kMergeWaves = kMergeBlock / 64;
+constexpr int kLdsPairs = 14;  // part pairs after the first two staged in LDS (rows up to 32 parts)
 
 // Whether unit x begins one of the `grid` ranges [floor(g n / grid),
 // floor((g + 1) n / grid)) of n units: with g the smallest index whose range
@@ -505,6 +507,16 @@ constexpr int kMergeWaves = kMergeBlock / 64;
 // Every product is below 2^53 and every quotient that is not an integer is
 // at least 1/n (resp. 1/grid) away from one, so the double divisions round
 // to the exact ceiling and floor.
+// Unit ranges of a launch over n units with `grid` workgroups: one unit each
+// up to grid units, then two units each (fewer, equally loaded workgroups
+// rather than a mix of one- and two-unit ranges), then `grid` ranges.  The
+// reduction and the merge derive it from the same n.
+__device__ __forceinline__ int range_count(int64_t n, int grid) {
+  if (n >= 2 * (int64_t)grid) return grid;
+  if (n > grid) return (int)((n + 1) >> 1);
+  return n < 1 ? 1 : (int)n;
+}
+
 __device__ __forceinline__ bool is_range_start(int x, int n, int grid) {
   const double g = __builtin_ceil((double)x * (double)grid / (double)n);
   return __builtin_floor(g * (double)n / (double)grid) == (double)x;
@@ -512,52 +524,66 @@ __device__ __forceinline__ bool is_range_start(int x, int n, int grid) {
 
 // Every lane [lo, hi) of a row whose final key reaches thr, merged into the
 // sorted best 32 in `top`; thr rises to the K-th kept key as it fills.  One
-// 16-byte chunk per lane per step, the next one in flight.
+// 16-byte chunk per lane per step, eight steps' chunks loaded at once.
 template <int DT, bool VEC>
 __device__ __forceinline__ void rescan_lanes(uint64_t& top, uint64_t& thr, const char* rowp, int lo,
                                              int hi, float L, int Keff, int lane) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   constexpr int kStep = 64 * kPer;
-  u32x4 nx = lo + lane * kPer < hi ? load_chunk<DT, VEC>(rowp, lo + lane * kPer, hi)
-                                   : u32x4{0u, 0u, 0u, 0u};
-  for (int b = lo; b < hi; b += kStep) {
-    const u32x4 cur = nx;
-    const int nf = b + kStep + lane * kPer;
-    if (b + kStep < hi) nx = nf < hi ? load_chunk<DT, VEC>(rowp, nf, hi) : u32x4{0u, 0u, 0u, 0u};
+  constexpr int kBatch = 8;  // chunks per lane in flight at once
+  for (int b = lo; b < hi; b += kBatch * kStep) {
+    u32x4 cur[kBatch];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = b + lane * kPer + j;
-      uint64_t f = 0ull;
-      if (i < hi) {
-        f = make_key(reported(E::get(cur, j), L), (uint32_t)i);
-        if (f < thr) f = 0ull;
+    for (int c = 0; c < kBatch; ++c) {
+      const int first = b + c * kStep + lane * kPer;
+      cur[c] = first < hi ? load_chunk<DT, VEC>(rowp, first, hi) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int steps = (hi - b + kStep - 1) / kStep < kBatch ? (hi - b + kStep - 1) / kStep : kBatch;
+#pragma nounroll
+    for (int c = 0; c < steps; ++c) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = b + c * kStep + lane * kPer + j;
+        uint64_t f = 0ull;
+        if (i < hi) {
+          f = make_key(reported(E::get(cur[0], j), L), (uint32_t)i);
+          if (f < thr) f = 0ull;
+        }
+        if (__ballot(f != 0ull) != 0ull) {
+          top = merge_top32(top, sort64_desc(f, lane), lane);
+          // The list only improves: its K-th key is a floor for the rest.
+          const uint64_t kth = readlane64(top, Keff - 1);
+          thr = kth > thr ? kth : thr;
+        }
       }
-      if (__ballot(f != 0ull) != 0ull) {
-        top = merge_top32(top, sort64_desc(f, lane), lane);
-        // The list only improves: its K-th key is a floor for the rest.
-        const uint64_t kth = readlane64(top, Keff - 1);
-        thr = kth > thr ? kth : thr;
-      }
+#pragma unroll
+      for (int c2 = 0; c2 + 1 < kBatch; ++c2) cur[c2] = cur[c2 + 1];
     }
   }
 }
 
 // Lanes [lo, hi) of a row whose reported value exceeds rt, summed over the
-// wave (every lane gets the total).  One 16-byte chunk per lane per step.
+// wave (every lane gets the total); eight 16-byte chunks per lane in flight.
 template <int DT, bool VEC>
 __device__ __forceinline__ int count_above(const char* rowp, int lo, int hi, float L, float rt,
                                            int lane) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
+  constexpr int kBatch = 8;  // chunks per lane in flight at once
+  constexpr uint32_t w = E::kNegInfWord;
   int n = 0;
-  for (int b = lo; b < hi; b += 64 * kPer) {
-    const int first = b + lane * kPer;
-    if (first < hi) {
-      const u32x4 r = load_chunk<DT, VEC>(rowp, first, hi);
+  for (int b = lo; b < hi; b += kBatch * 64 * kPer) {
+    u32x4 r[kBatch];
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) n += reported(E::get(r, j), L) > rt ? 1 : 0;
+    for (int c = 0; c < kBatch; ++c) {
+      const int first = b + (c * 64 + lane) * kPer;
+      r[c] = first < hi ? load_chunk<DT, VEC>(rowp, first, hi) : u32x4{w, w, w, w};
     }
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c)
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) n += reported(E::get(r[c], j), L) > rt ? 1 : 0;
   }
   return wave_sum_i32(n, lane);
 }
@@ -578,6 +604,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kUnitElems = kUnitThreads * kChunks * E::kPer;
   __shared__ int16_t part_u0_all[kMergeWaves][kMaxUnits + 1];
+  __shared__ uint64_t pair_keys[kMergeWaves][kLdsPairs][64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int row = (int)blockIdx.x * kMergeWaves + wv;
@@ -606,10 +633,11 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
 
   // ---- the row's parts (one lane per unit): a part starts at the row's
   // first unit and wherever a workgroup's unit range starts, at
-  // floor(g N / grid) of the N units of the active rows (the reduction's
+  // floor(g N / R) of the N units of the active rows (the reduction's
   // partition, recomputed exactly in double precision).
   const int a = before + t;
-  const bool start = lane < U && (lane == 0 || is_range_start(a * U + lane, total * U, p.workers));
+  const int ranges = range_count((int64_t)total * U, p.workers);
+  const bool start = lane < U && (lane == 0 || is_range_start(a * U + lane, total * U, ranges));
   const uint64_t starts = __ballot(start);
   const int np = __popcll(starts);
   if (start) part_u0[lanes_below(starts)] = (int16_t)lane;
@@ -618,7 +646,8 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int u0 = lane < np ? part_u0[lane] : 0;
 
   // ---- record and logit loads, issued together: the part statistics, the
-  // first four parts' kept keys and each part's guard words
+  // first four parts' kept keys in registers, those of the next 2 kLdsPairs
+  // parts (rows of many parts) staged in LDS, and each part's guard words
   float pm = kNegInf, ps = 0.0f;
   uint64_t c_key = 0ull;
   int p_above = 0;
@@ -634,6 +663,18 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   }
   const uint64_t raw0 = (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
   const uint64_t raw1 = 2 + (lane >> 5) < np ? rec[part_u0[2 + (lane >> 5)]].keys[lane & 31] : 0ull;
+  if (natural && np > 4) {
+    // All loads in flight at once: a row of many parts pays one round trip.
+    uint64_t pre[kLdsPairs];
+#pragma unroll
+    for (int i = 0; i < kLdsPairs; ++i) {
+      const int part = 4 + 2 * i + (lane >> 5);
+      pre[i] = part < np ? rec[part_u0[part]].keys[lane & 31] : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < kLdsPairs; ++i) pair_keys[wv][i][lane] = pre[i];
+    wave_sync();
+  }
   float x_tok = 0.0f;
   if (lane == 0 && tok >= 0 && tok < V) x_tok = load_elem<DT>(rowp, tok);
   int sel_id[2] = {0, 0};
@@ -691,12 +732,10 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
     top = merge_top32(top, sort_halves_desc(raw1 != 0ull ? final_key(raw1, L) : 0ull, lane), lane);
   for (int pb = 4; pb < np; pb += 2) {
     const int part = pb + (lane >> 5);
-    uint64_t f = 0ull;
-    if (part < np) {
-      const uint64_t raw = rec[part_u0[part]].keys[lane & 31];
-      if (raw != 0ull) f = final_key(raw, L);
-    }
-    top = merge_top32(top, sort64_desc(f, lane), lane);
+    uint64_t raw = 0ull;
+    if (pb < 4 + 2 * kLdsPairs) raw = pair_keys[wv][(pb - 4) >> 1][lane];
+    else if (part < np) raw = rec[part_u0[part]].keys[lane & 31];
+    top = merge_top32(top, sort_halves_desc(raw != 0ull ? final_key(raw, L) : 0ull, lane), lane);
   }
   // ---- guard, one lane per part
   const uint64_t FK = readlane64(top, Keff - 1);
@@ -1147,8 +1186,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     for (int s = tid; s <= p.capacity; s += kBlock) p.slot_rows[s] = prefix[s] & kRowsMask;
   // This workgroup's range of the N < 2^31 units (the host checks N).
   const int64_t N = (int64_t)total * U;
-  const int x0 = (int)((int64_t)blockIdx.x * N / p.workers);
-  const int x1 = (int)(((int64_t)blockIdx.x + 1) * N / p.workers);
+  const int ranges = range_count(N, p.workers);
+  if ((int)blockIdx.x >= ranges) return;
+  const int x0 = (int)((int64_t)blockIdx.x * N / ranges);
+  const int x1 = (int)(((int64_t)blockIdx.x + 1) * N / ranges);
   if (x0 >= x1) return;
 
   UnitPos cur = locate<DT>(p, prefix, x0);
