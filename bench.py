@@ -88,6 +88,9 @@ def parse():
                     help="also time the calls replayed from one captured HIP graph (0: skip)")
     ap.add_argument("--prompt", default=None,
                     help="measure prompt scoring on this chunk (P1 or P2) instead")
+    ap.add_argument("--packed", type=int, default=0,
+                    help="1: the frame's committed rows packed into P physical rows "
+                         "(shuffled slot order) and read through row offsets")
     return ap.parse_args()
 
 
@@ -291,21 +294,37 @@ def main():
         t = torch.from_numpy(a.view(np.int16) if bf16 else a).to(dev)
         return t.view(torch.bfloat16).reshape(-1) if bf16 else t.reshape(-1)
 
-    copies = [upload(w.logits)]
+    g = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa
+    packed_rows, offsets = None, None
+    if args.packed:
+        # Slot order shuffled, each slot's committed rows directly after another's.
+        e = np.where(w.requested != 0, np.clip(w.emitted, 0, spec.T), 0)
+        off = np.zeros(spec.capacity, dtype=np.int32)
+        P = 0
+        for sl in np.random.default_rng(spec.seed).permutation(spec.capacity):
+            off[sl] = P
+            P += int(e[sl])
+        packed = np.empty((P, spec.V_pad), dtype=w.logits.dtype)
+        for sl in range(spec.capacity):
+            packed[off[sl]:off[sl] + e[sl]] = w.logits[sl * spec.T:sl * spec.T + e[sl]]
+        copies = [upload(packed)]
+        packed_rows, offsets = P, g(off)
+    else:
+        copies = [upload(w.logits)]
     for _ in range(1, args.copies):
         copies.append(copies[0].clone())
-    g = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa
     tokens, emitted, requested = g(w.tokens), g(w.emitted), g(w.requested)
     id_counts, ids = g(w.id_counts), g(w.ids)
     plan = flp.Plan(spec.capacity, spec.T, spec.V, spec.V_pad,
-                    dtype=torch.bfloat16 if bf16 else torch.float32, K=spec.K, device=0)
+                    dtype=torch.bfloat16 if bf16 else torch.float32, K=spec.K, device=0,
+                    packed_rows=packed_rows)
     ws = plan.workspace()
     out = plan.new_out(int(synth.POISON))
     stream = torch.cuda.current_stream()
 
     def step(i, phase="all"):
         plan.run(copies[i % len(copies)], tokens, emitted, requested, id_counts, ids, out, ws,
-                 phase=phase)
+                 phase=phase, row_offsets=offsets)
 
     for i in range(args.warmup):
         step(i)
@@ -374,7 +393,8 @@ def main():
         with torch.cuda.stream(side):
             with torch.cuda.graph(gr, stream=side):
                 for c in range(len(copies)):
-                    plan.run(copies[c], tokens, emitted, requested, id_counts, ids, out, ws)
+                    plan.run(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
+                             row_offsets=offsets)
         torch.cuda.synchronize()
         reps = max(1, K // len(copies))
         for _ in range(2):
@@ -392,7 +412,7 @@ def main():
                  "calls": reps * len(copies)}
         del gr
     achieved_gbps = algo_bytes / (mean_reduce_ms / 1e3) / 1e9
-    traffic = measured_traffic(spec.name)
+    traffic = None if packed_rows else measured_traffic(spec.name)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -428,7 +448,8 @@ def main():
         "dtype": "bf16" if bf16 else "fp32",
         "data": "synthetic (seeded Gumbel logits + 10 peak; garbage rows past each prefix)",
         "config": {"workload": f"{spec.name}: {spec.capacity} slots x T={spec.T} x V={spec.V} "
-                               f"{'bf16' if bf16 else 'fp32'}, emitted 1..{spec.T}, K={spec.K}",
+                               f"{'bf16' if bf16 else 'fp32'}, emitted 1..{spec.T}, K={spec.K}"
+                               + (f", packed into {packed_rows} rows" if packed_rows else ""),
                    "active_rows": active, "capacity": spec.capacity, "T": spec.T, "V": spec.V,
                    "K": spec.K, "copies": len(copies), "oracle_rows_checked": checked},
         "roofline": {"bound": "hbm", "kernel": "reduce_kernel", "achieved": achieved_gbps,

@@ -30,7 +30,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libflare_logprobs.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_K = 20
 MAX_IDS = 128
 ROW_WORDS = 258
@@ -58,7 +58,8 @@ class PlanStruct(ctypes.Structure):
                 ("ranges", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
                 ("lse_offset", ctypes.c_uint64), ("slots_offset", ctypes.c_uint64),
-                ("reserved_offset", ctypes.c_uint64), ("reserved", ctypes.c_uint32 * 6)]
+                ("reserved_offset", ctypes.c_uint64), ("packed_rows", ctypes.c_int32),
+                ("reserved", ctypes.c_uint32 * 5)]
 
 
 class FlareError(RuntimeError):
@@ -87,6 +88,15 @@ def lib() -> ctypes.CDLL:
             f.restype = c.c_int
             f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
                           c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                          c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
+        L.flare_logprobs_plan_packed.restype = c.c_int
+        L.flare_logprobs_plan_packed.argtypes = [c.POINTER(PlanStruct)] + [c.c_int32] * 8
+        for name in ("flare_logprobs_run_packed", "flare_logprobs_reduce_packed",
+                     "flare_logprobs_merge_packed"):
+            f = getattr(L, name)
+            f.restype = c.c_int
+            f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
+                          c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                           c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
         L.flare_prompt_logprobs_plan.restype = c.c_int
         L.flare_prompt_logprobs_plan.argtypes = [c.POINTER(PlanStruct), c.c_int32, c.c_int32,
@@ -131,6 +141,16 @@ def flare_logprobs_plan(capacity: int, T: int, V: int, V_pad: int, dtype, K: int
     return plan
 
 
+def flare_logprobs_plan_packed(capacity: int, T: int, packed_rows: int, V: int, V_pad: int,
+                               dtype, K: int, device: int) -> PlanStruct:
+    plan = PlanStruct()
+    rc = lib().flare_logprobs_plan_packed(ctypes.byref(plan), capacity, T, packed_rows, V, V_pad,
+                                          dtype_code(dtype), K, device)
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_plan_packed")
+    return plan
+
+
 def _ptr(t) -> int | None:
     if t is None:
         return None
@@ -166,6 +186,41 @@ def flare_logprobs_run(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad
           emitted_counts, tokens, K, out, workspace, stream)
 
 
+def _packed_call(name: str, plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                 requested, id_counts, ids, emitted_counts, tokens, row_offsets, K: int, out,
+                 workspace, stream) -> None:
+    rc = getattr(lib(), name)(ctypes.byref(plan), _ptr(logits), dtype_code(dtype), rows, V,
+                              V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids),
+                              _ptr(emitted_counts), _ptr(tokens), _ptr(row_offsets), K,
+                              _ptr(out), _ptr(workspace), _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, name)
+
+
+def flare_logprobs_run_packed(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                              requested, id_counts, ids, emitted_counts, tokens, row_offsets,
+                              K: int, out, workspace, stream=None) -> None:
+    """One frame over packed target rows (rows = P, row_offsets int32 [capacity])."""
+    _packed_call("flare_logprobs_run_packed", plan, logits, dtype, rows, V, V_pad, requested,
+                 id_counts, ids, emitted_counts, tokens, row_offsets, K, out, workspace, stream)
+
+
+def flare_logprobs_reduce_packed(plan: PlanStruct, logits, dtype, rows: int, V: int,
+                                 V_pad: int, requested, id_counts, ids, emitted_counts, tokens,
+                                 row_offsets, K: int, out, workspace, stream=None) -> None:
+    """The first launch of flare_logprobs_run_packed (same arguments)."""
+    _packed_call("flare_logprobs_reduce_packed", plan, logits, dtype, rows, V, V_pad, requested,
+                 id_counts, ids, emitted_counts, tokens, row_offsets, K, out, workspace, stream)
+
+
+def flare_logprobs_merge_packed(plan: PlanStruct, logits, dtype, rows: int, V: int,
+                                V_pad: int, requested, id_counts, ids, emitted_counts, tokens,
+                                row_offsets, K: int, out, workspace, stream=None) -> None:
+    """The second launch of flare_logprobs_run_packed (same arguments, after reduce)."""
+    _packed_call("flare_logprobs_merge_packed", plan, logits, dtype, rows, V, V_pad, requested,
+                 id_counts, ids, emitted_counts, tokens, row_offsets, K, out, workspace, stream)
+
+
 def flare_logprobs_reduce(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
                           requested, id_counts, ids, emitted_counts, tokens, K: int, out,
                           workspace, stream=None) -> None:
@@ -194,12 +249,20 @@ class Plan:
     """A validated geometry plus the shapes its tensors must have."""
 
     def __init__(self, capacity: int, T: int, V: int, V_pad: int | None = None,
-                 dtype=torch.bfloat16, K: int = 20, device: int | None = None):
+                 dtype=torch.bfloat16, K: int = 20, device: int | None = None,
+                 packed_rows: int | None = None):
+        """`packed_rows` = P selects packed target rows (logits [P, V_pad], slot s's
+        row t at row_offsets[s] + t); None keeps the rectangular [capacity*T, V_pad]."""
         if device is None:
             device = torch.cuda.current_device()
         self.torch_dtype = torch.bfloat16 if dtype_code(dtype) == DTYPE_BF16 else torch.float32
         self.V_pad = V if V_pad is None else V_pad
-        self.raw = flare_logprobs_plan(capacity, T, V, self.V_pad, dtype, K, device)
+        if packed_rows is None:
+            self.raw = flare_logprobs_plan(capacity, T, V, self.V_pad, dtype, K, device)
+        else:
+            self.raw = flare_logprobs_plan_packed(capacity, T, packed_rows, V, self.V_pad, dtype,
+                                                  K, device)
+        self.packed_rows = packed_rows
         self.capacity, self.T, self.V, self.K, self.device_index = capacity, T, V, K, device
 
     @property
@@ -224,13 +287,31 @@ class Plan:
                           device=self.device)
 
     def run(self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
-            stream=None, phase: str = "all") -> torch.Tensor:
+            stream=None, phase: str = "all", row_offsets=None) -> torch.Tensor:
         """One call: both launches (phase "all"), or only the first ("reduce")
-        or the second ("merge") of them."""
-        fn = {"all": flare_logprobs_run, "reduce": flare_logprobs_reduce,
-              "merge": flare_logprobs_merge}[phase]
+        or the second ("merge") of them.  A packed plan takes `row_offsets`
+        (int32 [capacity]) and the same phases."""
         dev = self.device
         rows = self.capacity * self.T
+        if self.packed_rows is not None:
+            if row_offsets is None:
+                raise ValueError("a packed plan needs row_offsets")
+            _check(logits, "logits", self.torch_dtype, self.packed_rows * self.V_pad, dev)
+            _check(row_offsets, "row_offsets", torch.int32, self.capacity, dev)
+            _check(tokens, "tokens", torch.int32, rows, dev)
+            _check(emitted_counts, "emitted_counts", torch.int32, self.capacity, dev)
+            _check(requested, "requested", torch.int32, self.capacity, dev)
+            _check(id_counts, "id_counts", torch.int32, self.capacity, dev)
+            _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
+            _check(out, "out", torch.int32, rows * ROW_WORDS, dev)
+            _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
+            fn = {"all": flare_logprobs_run_packed, "reduce": flare_logprobs_reduce_packed,
+                  "merge": flare_logprobs_merge_packed}[phase]
+            fn(self.raw, logits, self.torch_dtype, self.packed_rows, self.V, self.V_pad, requested,
+               id_counts, ids, emitted_counts, tokens, row_offsets, self.K, out, workspace, stream)
+            return out
+        fn = {"all": flare_logprobs_run, "reduce": flare_logprobs_reduce,
+              "merge": flare_logprobs_merge}[phase]
         _check(logits, "logits", self.torch_dtype, rows * self.V_pad, dev)
         _check(tokens, "tokens", torch.int32, rows, dev)
         _check(emitted_counts, "emitted_counts", torch.int32, self.capacity, dev)

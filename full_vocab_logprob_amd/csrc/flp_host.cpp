@@ -42,7 +42,8 @@ const char* flare_status_string(int status) {
 // Both plans: a generation frame (mode 0) or a scored prompt chunk (mode 1,
 // capacity = rows, T = 1, K = 20).
 static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, int32_t V,
-                     int32_t V_pad, int32_t dtype, int32_t K, int32_t device, int32_t mode) {
+                     int32_t V_pad, int32_t dtype, int32_t K, int32_t device, int32_t mode,
+                     int32_t packed_rows) {
   if (!plan) return FLARE_ERR_INVALID_ARGUMENT;
   memset(plan, 0, sizeof *plan);
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
@@ -50,6 +51,7 @@ static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, i
   if (capacity > flp::kMaxCapacity) return FLARE_ERR_INVALID_ARGUMENT;
   const int64_t rows = (int64_t)capacity * T;
   if (rows > (int64_t)1 << 30) return FLARE_ERR_INVALID_ARGUMENT;
+  if (packed_rows < 0 || packed_rows > (1 << 30)) return FLARE_ERR_INVALID_ARGUMENT;
   const int unit = flp::unit_elems(dtype);
   const int64_t units = ((int64_t)V + unit - 1) / unit;
   if (units > flp::kMaxUnits) return FLARE_ERR_UNSUPPORTED_SIZE;
@@ -69,7 +71,7 @@ static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, i
     int prev = 0;
     if (hipGetDevice(&prev) != hipSuccess) return FLARE_ERR_DEVICE;
     if (prev != device && hipSetDevice(device) != hipSuccess) return FLARE_ERR_DEVICE;
-    per_cu = flp::reduce_occupancy(dtype, vec, mode == FLARE_MODE_PROMPT, capacity);
+    per_cu = flp::reduce_occupancy(dtype, vec, mode == FLARE_MODE_PROMPT, capacity, packed_rows > 0);
     if (prev != device && hipSetDevice(prev) != hipSuccess) return FLARE_ERR_DEVICE;
     if (per_cu < 1) return FLARE_ERR_DEVICE;
   }
@@ -90,6 +92,7 @@ static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, i
   plan->cu_count = cus;
   plan->ranges = plan->grid;
   plan->mode = mode;
+  plan->packed_rows = packed_rows;
   if (mode == FLARE_MODE_PROMPT) {
     // A unit range holds at most ceil(N / grid) units, so it touches at most
     // ceil((ceil(N / grid) - 1) / units) + 1 rows.
@@ -116,13 +119,24 @@ extern "C" {
 
 int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, int32_t V,
                         int32_t V_pad, int32_t dtype, int32_t K, int32_t device) {
-  return make_plan(plan, capacity, T, V, V_pad, dtype, K, device, FLARE_MODE_GENERATION);
+  return make_plan(plan, capacity, T, V, V_pad, dtype, K, device, FLARE_MODE_GENERATION, 0);
+}
+
+int flare_logprobs_plan_packed(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T,
+                               int32_t packed_rows, int32_t V, int32_t V_pad, int32_t dtype,
+                               int32_t K, int32_t device) {
+  if (packed_rows < 1) {
+    if (plan) memset(plan, 0, sizeof *plan);
+    return FLARE_ERR_INVALID_ARGUMENT;
+  }
+  return make_plan(plan, capacity, T, V, V_pad, dtype, K, device, FLARE_MODE_GENERATION,
+                   packed_rows);
 }
 
 int flare_prompt_logprobs_plan(flare_logprobs_plan_t* plan, int32_t rows, int32_t V,
                                int32_t V_pad, int32_t dtype, int32_t device) {
   return make_plan(plan, rows, 1, V, V_pad, dtype, FLARE_PROMPT_ALTERNATIVES, device,
-                   FLARE_MODE_PROMPT);
+                   FLARE_MODE_PROMPT, 0);
 }
 
 }  // extern "C"
@@ -131,25 +145,32 @@ int flare_prompt_logprobs_plan(flare_logprobs_plan_t* plan, int32_t rows, int32_
 static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
                       int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
                       const int32_t* id_counts, const int32_t* ids,
-                      const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
-                      int32_t* out, void* workspace, void* hip_stream, int phases) {
+                      const int32_t* emitted_counts, const int32_t* tokens,
+                      const int32_t* row_offsets, int32_t K, int32_t* out, void* workspace,
+                      void* hip_stream, int phases) {
   if (!plan || !logits || !requested || !id_counts || !ids || !emitted_counts || !tokens ||
       !out || !workspace)
     return FLARE_ERR_INVALID_ARGUMENT;
+  // A packed plan takes its row offsets and P logit rows; a rectangular one neither.
+  if ((plan->packed_rows > 0) != (row_offsets != nullptr)) return FLARE_ERR_PLAN_MISMATCH;
   if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
   if (plan->mode != FLARE_MODE_GENERATION) return FLARE_ERR_PLAN_MISMATCH;
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
   if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad || K != plan->K)
     return FLARE_ERR_PLAN_MISMATCH;
-  if (rows != (int64_t)plan->capacity * plan->T) return FLARE_ERR_PLAN_MISMATCH;
+  if (rows != (plan->packed_rows > 0 ? (int64_t)plan->packed_rows
+                                      : (int64_t)plan->capacity * plan->T))
+    return FLARE_ERR_PLAN_MISMATCH;
   if (plan->grid < 1 || plan->units < 1 || plan->units > flp::kMaxUnits ||
-      plan->ranges != plan->grid || plan->block != flp::kBlock)
+      plan->ranges != plan->grid || plan->block != flp::kBlock || plan->packed_rows < 0)
     return FLARE_ERR_PLAN_MISMATCH;
   if (((uintptr_t)workspace & 15u) != 0) return FLARE_ERR_INVALID_ARGUMENT;
 
   char* ws = (char*)workspace;
   flp::Params p;
   p.logits = logits;
+  p.row_offsets = plan->packed_rows > 0 ? row_offsets : nullptr;
+  p.packed_rows = plan->packed_rows;
   p.requested = requested;
   p.id_counts = id_counts;
   p.ids = ids;
@@ -181,7 +202,8 @@ static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, 
   if (plan->mode != FLARE_MODE_PROMPT) return FLARE_ERR_PLAN_MISMATCH;
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
   if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad) return FLARE_ERR_PLAN_MISMATCH;
-  if (rows != (int64_t)plan->capacity || plan->T != 1 || plan->K != FLARE_PROMPT_ALTERNATIVES)
+  if (rows != (int64_t)plan->capacity || plan->T != 1 || plan->K != FLARE_PROMPT_ALTERNATIVES ||
+      plan->packed_rows != 0)
     return FLARE_ERR_PLAN_MISMATCH;
   if (plan->grid < 1 || plan->units < 1 || plan->units > flp::kMaxUnits ||
       plan->ranges != plan->grid || plan->block != flp::kBlock)
@@ -196,6 +218,8 @@ static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, 
   char* ws = (char*)workspace;
   flp::Params p;
   p.logits = logits;
+  p.row_offsets = nullptr;
+  p.packed_rows = 0;
   p.requested = nullptr;
   p.id_counts = nullptr;
   p.ids = nullptr;
@@ -226,8 +250,44 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits, in
                        const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
                        int32_t* out, void* workspace, void* hip_stream) {
   return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
-                    emitted_counts, tokens, K, out, workspace, hip_stream,
+                    emitted_counts, tokens, nullptr, K, out, workspace, hip_stream,
                     flp::kPhaseReduce | flp::kPhaseMerge);
+}
+
+int flare_logprobs_run_packed(const flare_logprobs_plan_t* plan, const void* logits,
+                              int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                              const int32_t* requested, const int32_t* id_counts,
+                              const int32_t* ids, const int32_t* emitted_counts,
+                              const int32_t* tokens, const int32_t* row_offsets, int32_t K,
+                              int32_t* out, void* workspace, void* hip_stream) {
+  if (!row_offsets) return FLARE_ERR_INVALID_ARGUMENT;
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, row_offsets, K, out, workspace, hip_stream,
+                    flp::kPhaseReduce | flp::kPhaseMerge);
+}
+
+int flare_logprobs_reduce_packed(const flare_logprobs_plan_t* plan, const void* logits,
+                                 int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                 const int32_t* requested, const int32_t* id_counts,
+                                 const int32_t* ids, const int32_t* emitted_counts,
+                                 const int32_t* tokens, const int32_t* row_offsets, int32_t K,
+                                 int32_t* out, void* workspace, void* hip_stream) {
+  if (!row_offsets) return FLARE_ERR_INVALID_ARGUMENT;
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, row_offsets, K, out, workspace, hip_stream,
+                    flp::kPhaseReduce);
+}
+
+int flare_logprobs_merge_packed(const flare_logprobs_plan_t* plan, const void* logits,
+                                int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                const int32_t* requested, const int32_t* id_counts,
+                                const int32_t* ids, const int32_t* emitted_counts,
+                                const int32_t* tokens, const int32_t* row_offsets, int32_t K,
+                                int32_t* out, void* workspace, void* hip_stream) {
+  if (!row_offsets) return FLARE_ERR_INVALID_ARGUMENT;
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, row_offsets, K, out, workspace, hip_stream,
+                    flp::kPhaseMerge);
 }
 
 int flare_logprobs_reduce(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
@@ -236,7 +296,7 @@ int flare_logprobs_reduce(const flare_logprobs_plan_t* plan, const void* logits,
                           const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
                           int32_t* out, void* workspace, void* hip_stream) {
   return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
-                    emitted_counts, tokens, K, out, workspace, hip_stream, flp::kPhaseReduce);
+                    emitted_counts, tokens, nullptr, K, out, workspace, hip_stream, flp::kPhaseReduce);
 }
 
 int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
@@ -245,7 +305,7 @@ int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits, 
                          const int32_t* emitted_counts, const int32_t* tokens, int32_t K,
                          int32_t* out, void* workspace, void* hip_stream) {
   return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
-                    emitted_counts, tokens, K, out, workspace, hip_stream, flp::kPhaseMerge);
+                    emitted_counts, tokens, nullptr, K, out, workspace, hip_stream, flp::kPhaseMerge);
 }
 
 int flare_prompt_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,

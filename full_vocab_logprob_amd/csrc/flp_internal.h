@@ -51,6 +51,8 @@ struct Params {
   PartRecord* records;
   float* lse;
   int32_t* slot_rows;   // [capacity + 1]: active rows before each slot, then their total
+  const int32_t* row_offsets;  // packed target rows: logit row of (s, t) is row_offsets[s] + t
+  int32_t packed_rows;         // rows of a packed logits buffer (0: rectangular, row s T + t)
   int64_t V_pad;
   int32_t capacity;
   int32_t T;
@@ -68,7 +70,8 @@ constexpr int kPhaseMerge = 2;
 // when its target (tokens[s]) is a vocabulary ID, K = 20, kPromptWords per row.
 int launch(const Params& p, int dtype, bool vector_rows, bool score, int phases, void* stream);
 // Resident reduction workgroups per CU (0 on error).
-int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity);
-size_t prefix_lds_bytes(int capacity);
+int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity, bool packed);
+// Dynamic LDS of the reduction: the slot table, and each slot's packed row offset.
+size_t prefix_lds_bytes(int capacity, bool packed);
 
 }  // namespace flp

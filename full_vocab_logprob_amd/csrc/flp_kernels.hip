@@ -416,6 +416,13 @@ __device__ __forceinline__ void cand_append(CandBuf& cb, Best32& b, uint64_t k, 
 constexpr int kSelBit = (int)0x80000000u;
 constexpr int kRowsMask = 0x7FFFFFFF;
 
+// Packed target rows: a slot whose committed rows [off, off + rows) would
+// leave the P physical rows reads and writes nothing.
+__device__ __forceinline__ int packed_rows_of(const Params& p, int s, int rows) {
+  const int off = p.row_offsets[s];
+  return rows > 0 && (off < 0 || (int64_t)off + rows > p.packed_rows) ? 0 : rows;
+}
+
 // A scored prompt row (one per slot) is active when its target is an ID.
 template <bool SCORE>
 __device__ __forceinline__ int slot_word(const Params& p, int s) {
@@ -423,9 +430,10 @@ __device__ __forceinline__ int slot_word(const Params& p, int s) {
     const int tk = p.tokens[s];
     return (tk >= 0 && tk < p.V) ? 1 : 0;
   }
-  // The three words are loaded together (one round trip).
+  // The words are loaded together (one round trip).
   const int r = p.requested[s], e = p.emitted[s], n = p.id_counts[s];
-  const int rows = r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
+  int rows = r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
+  if (p.row_offsets) rows = packed_rows_of(p, s, rows);
   return rows | (n > 0 ? kSelBit : 0);
 }
 
@@ -441,9 +449,11 @@ __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
   const int s0 = tid * per;
   const int s1 = s0 + per < cap ? s0 + per : cap;
   int local = 0;
+  int* phys = prefix + cap + 1;  // packed row offsets (packed launches only)
   for (int s = s0; s < s1; ++s) {
     const int c = slot_word<SCORE>(p, s);
     prefix[s] = c;
+    if (!SCORE && p.row_offsets) phys[s] = p.row_offsets[s];
     local += c & kRowsMask;
   }
   // exclusive scan of `local` over the block
@@ -614,6 +624,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // only meaningful for an active row).
   const int req = SCORE ? 1 : p.requested[s], emi = SCORE ? 1 : p.emitted[s];
   const int cnt = SCORE ? 0 : p.id_counts[s];
+  const int off = !SCORE && p.row_offsets ? p.row_offsets[s] : 0;
   const int before = p.slot_rows[s], total = p.slot_rows[p.capacity];
   const int tok = p.tokens[row];
   const int V = p.V, U = p.units;
@@ -624,11 +635,15 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       out[lane] = lane == 2 ? 0 : ((lane == 0 || (lane >= 3 && (lane & 1))) ? -1 : (int32_t)kNanBits);
     return;
   }
-  if (req == 0 || t >= (emi < 0 ? 0 : (emi > p.T ? p.T : emi))) return;
+  int rows_s = req == 0 ? 0 : (emi < 0 ? 0 : (emi > p.T ? p.T : emi));
+  if (!SCORE && p.row_offsets && rows_s > 0 && (off < 0 || (int64_t)off + rows_s > p.packed_rows))
+    rows_s = 0;  // as packed_rows_of, with the offset already loaded
+  if (t >= rows_s) return;
   const int n_sel = cnt < 0 ? 0 : (cnt > 128 ? 128 : cnt);
   const bool natural = p.K > 0 && n_sel == 0;
   const PartRecord* rec = p.records + (int64_t)row * U;
-  const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * E::kBytes;
+  const int lrow = !SCORE && p.row_offsets ? off + t : row;
+  const char* rowp = (const char*)p.logits + (int64_t)lrow * p.V_pad * E::kBytes;
   int16_t* part_u0 = part_u0_all[wv];
 
   // ---- the row's parts (one lane per unit): a part starts at the row's
@@ -830,7 +845,8 @@ __device__ __forceinline__ uint64_t pub_read(uint64_t pub, int part) {
   return (pub & 0xFFFFFFFF00000000ull) | (uint64_t)(~(uint32_t)(pub & 0xFFFFFu));
 }
 
-// Where a unit sits: active row a, unit u of that row, slot s, logit row.
+// Where a unit sits: active row a, unit u of that row, slot s, frame
+// position row = s T + t, and the logit row's address (packed or not).
 struct UnitPos {
   int a, u, s, row;
   const char* rowp;
@@ -842,8 +858,11 @@ __device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, in
   q.a = x / p.units;
   q.u = x - q.a * p.units;
   q.s = __builtin_amdgcn_readfirstlane(slot_of(prefix, p.capacity, q.a));
-  q.row = __builtin_amdgcn_readfirstlane(q.s * p.T + (q.a - (prefix[q.s] & kRowsMask)));
-  q.rowp = (const char*)p.logits + (int64_t)q.row * p.V_pad * Elem<DT>::kBytes;
+  const int t = q.a - (prefix[q.s] & kRowsMask);
+  q.row = __builtin_amdgcn_readfirstlane(q.s * p.T + t);
+  const int lrow =
+      p.row_offsets ? __builtin_amdgcn_readfirstlane(prefix[p.capacity + 1 + q.s] + t) : q.row;
+  q.rowp = (const char*)p.logits + (int64_t)lrow * p.V_pad * Elem<DT>::kBytes;
   return q;
 }
 
@@ -1489,7 +1508,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
 template <int DT, bool VEC, bool SCORE>
 hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
   if (phases & kPhaseReduce) {
-    const size_t lds = prefix_lds_bytes(p.capacity);
+    const size_t lds = prefix_lds_bytes(p.capacity, p.row_offsets != nullptr);
     hipLaunchKernelGGL((reduce_kernel<DT, VEC, SCORE>), dim3((uint32_t)p.workers), dim3(kBlock), lds,
                        st, p);
     const hipError_t e = hipGetLastError();
@@ -1504,7 +1523,9 @@ hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
 
 }  // namespace
 
-size_t prefix_lds_bytes(int capacity) { return (size_t)(capacity + 1) * sizeof(int); }
+size_t prefix_lds_bytes(int capacity, bool packed) {
+  return (size_t)(capacity + 1 + (packed ? capacity : 0)) * sizeof(int);
+}
 
 template <int DT, bool VEC, bool SCORE>
 int occupancy_typed(size_t lds) {
@@ -1514,8 +1535,8 @@ int occupancy_typed(size_t lds) {
   return e == hipSuccess ? n : 0;
 }
 
-int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity) {
-  const size_t lds = prefix_lds_bytes(capacity);
+int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity, bool packed) {
+  const size_t lds = prefix_lds_bytes(capacity, packed);
   if (dtype == 1) {
     if (score) return vector_rows ? occupancy_typed<1, true, true>(lds) : occupancy_typed<1, false, true>(lds);
     return vector_rows ? occupancy_typed<1, true, false>(lds) : occupancy_typed<1, false, false>(lds);

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FLARE_LOGPROBS_ABI_VERSION 3u
+#define FLARE_LOGPROBS_ABI_VERSION 4u
 #define FLARE_LOGPROBS_MAX_K 20
 #define FLARE_LOGPROBS_MAX_IDS 128
 #define FLARE_LOGPROBS_ROW_WORDS 258 /* 2 + 2 * 128 */
@@ -101,7 +101,8 @@ typedef struct flare_logprobs_plan {
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
   uint64_t slots_offset;    /* int32[capacity + 1]: active rows before each slot, then all */
   uint64_t reserved_offset; /* 0 */
-  uint32_t reserved[6];
+  int32_t packed_rows;      /* P of flare_logprobs_plan_packed; 0 for the rectangular layout */
+  uint32_t reserved[5];
 } flare_logprobs_plan_t;
 
 /*
@@ -141,6 +142,48 @@ int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
                        const int32_t* ids, const int32_t* emitted_counts,
                        const int32_t* tokens, int32_t K, int32_t* out,
                        void* workspace, void* hip_stream);
+
+/*
+ * Packed target rows (MTP design page, graph catalog paragraph: a verify
+ * descriptor's physical target capacity P may be below B x W; generation
+ * design page, gating paragraph: a packed request's columns past its
+ * committed prefix may hold another request's rows and are never read).
+ * The logits hold P rows; slot s's verify row t is logit row
+ * row_offsets[s] + t.  Everything else (gating, the [capacity, T, 258]
+ * output frame indexed by slot and position, tokens, IDs) is as for
+ * flare_logprobs_run.
+ *   flare_logprobs_plan_packed: as flare_logprobs_plan, plus 1 <= packed_rows
+ *     <= 2^30 (else FLARE_ERR_INVALID_ARGUMENT); the plan records P.
+ *   flare_logprobs_run_packed: run's arguments with rows == P and
+ *     row_offsets a device int32 [capacity] (NULL: FLARE_ERR_INVALID_ARGUMENT).
+ *     A slot whose committed rows [row_offsets[s], row_offsets[s] + e) leave
+ *     [0, P) reads and writes nothing (e the clamped emitted count).
+ * A packed plan is rejected by flare_logprobs_run (and its two launches) and
+ * a rectangular plan by the _packed entry points (FLARE_ERR_PLAN_MISMATCH).
+ * flare_logprobs_reduce_packed and flare_logprobs_merge_packed are the two
+ * launches of flare_logprobs_run_packed, as for the rectangular layout.
+ */
+int flare_logprobs_plan_packed(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T,
+                               int32_t packed_rows, int32_t V, int32_t V_pad, int32_t dtype,
+                               int32_t K, int32_t device);
+int flare_logprobs_run_packed(const flare_logprobs_plan_t* plan, const void* logits,
+                              int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                              const int32_t* requested, const int32_t* id_counts,
+                              const int32_t* ids, const int32_t* emitted_counts,
+                              const int32_t* tokens, const int32_t* row_offsets, int32_t K,
+                              int32_t* out, void* workspace, void* hip_stream);
+int flare_logprobs_reduce_packed(const flare_logprobs_plan_t* plan, const void* logits,
+                                 int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                 const int32_t* requested, const int32_t* id_counts,
+                                 const int32_t* ids, const int32_t* emitted_counts,
+                                 const int32_t* tokens, const int32_t* row_offsets, int32_t K,
+                                 int32_t* out, void* workspace, void* hip_stream);
+int flare_logprobs_merge_packed(const flare_logprobs_plan_t* plan, const void* logits,
+                                int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                                const int32_t* requested, const int32_t* id_counts,
+                                const int32_t* ids, const int32_t* emitted_counts,
+                                const int32_t* tokens, const int32_t* row_offsets, int32_t K,
+                                int32_t* out, void* workspace, void* hip_stream);
 
 /*
  * The two launches of flare_logprobs_run, for callers that want to order

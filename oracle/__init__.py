@@ -61,6 +61,12 @@ class Oracle:
                                           c.c_void_p, c.c_void_p, c.c_void_p,
                                           c.c_void_p, c.c_int32, c.c_void_p,
                                           c.c_void_p]
+        self.lib.oracle_frame_packed.restype = c.c_int64
+        self.lib.oracle_frame_packed.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
+                                                 c.c_int32, c.c_int32, c.c_int32, c.c_void_p,
+                                                 c.c_void_p, c.c_void_p, c.c_void_p,
+                                                 c.c_void_p, c.c_void_p, c.c_int32,
+                                                 c.c_void_p, c.c_void_p]
         self.lib.oracle_prompt_row.restype = c.c_int
         self.lib.oracle_prompt_row.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
                                                c.c_void_p, c.c_void_p]
@@ -121,6 +127,30 @@ class Oracle:
                                   out.ctypes.data, lse.ctypes.data)
         if n < 0:
             raise ValueError("oracle_frame rejected its arguments")
+        return int(n), lse
+
+    def frame_packed(self, logits: np.ndarray, capacity: int, T: int, P: int, V: int,
+                     V_pad: int, requested, id_counts, ids, emitted, tokens, row_offsets,
+                     K: int, out: np.ndarray):
+        """One frame over P packed logit rows (slot s's row t at row_offsets[s] + t).
+        `out` is [capacity, T, 258], written in place.  Returns (active rows, lse)."""
+        logits = np.ascontiguousarray(logits)
+        assert logits.size >= P * V_pad
+        a = lambda x: np.ascontiguousarray(x, dtype=np.int32)  # noqa: E731
+        req, cnt, idv, emi, tok, off = (a(requested), a(id_counts), a(ids), a(emitted),
+                                        a(tokens), a(row_offsets))
+        assert req.size == capacity and cnt.size == capacity and emi.size == capacity
+        assert off.size == capacity and idv.size == capacity * MAX_IDS
+        assert tok.size == capacity * T
+        assert out.dtype == np.int32 and out.size == capacity * T * ROW_WORDS
+        assert out.flags.c_contiguous
+        lse = np.full(capacity * T, np.nan, dtype=np.float32)
+        n = self.lib.oracle_frame_packed(logits.ctypes.data, self._dtype_of(logits), capacity,
+                                         T, P, V, V_pad, req.ctypes.data, cnt.ctypes.data,
+                                         idv.ctypes.data, emi.ctypes.data, tok.ctypes.data,
+                                         off.ctypes.data, K, out.ctypes.data, lse.ctypes.data)
+        if n < 0:
+            raise ValueError("oracle_frame_packed rejected its arguments")
         return int(n), lse
 
     def prompt_row(self, row: np.ndarray, target: int, V: int | None = None):

@@ -45,6 +45,9 @@
  *       value bits 0x7FC00000 and is never dereferenced.
  *   R10 emitted counts are clamped to [0, T], ID counts to [0, 128]; a zero
  *       request flag wins over a nonzero ID count.
+ *   R13 packed target rows: slot s's verify row t is logit row
+ *       row_offsets[s] + t of P rows; a slot whose committed rows would leave
+ *       [0, P) is treated as not emitting (nothing read or written).
  *
  * Parity pins: every function here is pinned by tests that do not reuse its
  * arithmetic (closed forms, brute-force ranks, designed tie rows, a library
@@ -289,6 +292,51 @@ int64_t oracle_frame(const void* logits, int dtype, int32_t capacity,
                           out + (size_t)r * ORACLE_ROW_WORDS, &L);
       if (rc < 0) return -1;
       if (lse_out) lse_out[r] = L;
+      ++active;
+    }
+  }
+  return active;
+}
+
+/*
+ * One frame over packed target rows (MTP design page, graph catalog
+ * paragraph: P physical target rows, possibly fewer than capacity * T; GLP
+ * gating paragraph: a packed request's columns past its committed prefix are
+ * never read).  As oracle_frame, except that position (s, t) reads logit row
+ * row_offsets[s] + t of the P rows at `logits` (reading R13).  Output and
+ * `lse_out` stay indexed by frame position s * T + t.
+ */
+int64_t oracle_frame_packed(const void* logits, int dtype, int32_t capacity,
+                            int32_t T, int32_t P, int32_t V, int32_t V_pad,
+                            const int32_t* requested, const int32_t* id_counts,
+                            const int32_t* ids, const int32_t* emitted,
+                            const int32_t* tokens, const int32_t* row_offsets,
+                            int32_t K, int32_t* out, float* lse_out) {
+  if (!logits || !requested || !id_counts || !ids || !emitted || !tokens ||
+      !row_offsets || !out)
+    return -1;
+  if (capacity < 1 || T < 1 || P < 1 || V < 1 || V_pad < V || K < 0 ||
+      K > ORACLE_MAX_K)
+    return -1;
+  size_t esize = (dtype == ORACLE_DTYPE_BF16) ? 2 : 4;
+  int64_t active = 0;
+  for (int32_t s = 0; s < capacity; ++s) {
+    if (!requested[s]) continue;
+    int32_t e = emitted[s] < 0 ? 0 : (emitted[s] > T ? T : emitted[s]);
+    int64_t first = row_offsets[s];
+    if (e > 0 && (first < 0 || first + e > P)) continue; /* reading R13 */
+    int32_t n = id_counts[s] < 0 ? 0 : id_counts[s];
+    if (n > ORACLE_MAX_IDS) n = ORACLE_MAX_IDS;
+    for (int32_t t = 0; t < e; ++t) {
+      int64_t pos = (int64_t)s * T + t; /* frame position */
+      const char* row =
+          (const char*)logits + (size_t)(first + t) * (size_t)V_pad * esize;
+      float L;
+      if (oracle_row(row, dtype, V, tokens[pos], n,
+                     ids + (size_t)s * ORACLE_MAX_IDS, K,
+                     out + (size_t)pos * ORACLE_ROW_WORDS, &L) < 0)
+        return -1;
+      if (lse_out) lse_out[pos] = L;
       ++active;
     }
   }

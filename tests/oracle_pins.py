@@ -342,6 +342,67 @@ def pin_frame_gating(o):
                 assert float(from_bits(cell[3])) > -1e-3
 
 
+# ------------------------------------------------------------ packed target rows
+def packed_case(dtype=np.float32, seed=19):
+    """A rectangular frame and the same rows packed into P < capacity * T
+    physical rows in a shuffled slot order, each slot's committed rows
+    followed directly by another slot's (MTP design page, graph catalog
+    paragraph).  The packed buffer has capacity * T rows, those past P and
+    the uncommitted ones NaN, so a reader of the wrong row sees NaN."""
+    cap, T, V, V_pad = 7, 4, 90, 96
+    rng = np.random.default_rng(seed)
+    rect = np.full((cap * T, V_pad), np.nan, dtype=np.float32)
+    rect[:, :V] = (rng.standard_normal((cap * T, V)) * 3).astype(np.float32)
+    requested = np.array([1, 1, 0, 1, 1, 1, 1], dtype=np.int32)
+    emitted = np.array([2, 4, 3, 0, 1, 3, 9], dtype=np.int32)  # slot 6 clamps to T
+    id_counts = np.array([0, 5, 0, 0, 0, 0, 0], dtype=np.int32)
+    ids = np.full(cap * 128, -2, dtype=np.int32)
+    ids[128:133] = [3, 80, 3, 0, 89]
+    tokens = (np.arange(cap * T, dtype=np.int32) * 7) % V
+    order = rng.permutation(cap)
+    offsets = np.zeros(cap, dtype=np.int32)
+    P = 0
+    for s in order:
+        e = 0 if requested[s] == 0 else min(max(int(emitted[s]), 0), T)
+        offsets[s] = P
+        P += e
+    packed = np.full((cap * T, V_pad), np.nan, dtype=np.float32)
+    for s in range(cap):
+        e = 0 if requested[s] == 0 else min(max(int(emitted[s]), 0), T)
+        packed[offsets[s]:offsets[s] + e] = rect[s * T:s * T + e]
+    if dtype == np.uint16:
+        rect, packed = synth.bf16_bits(rect), synth.bf16_bits(packed)
+    return dict(cap=cap, T=T, V=V, V_pad=V_pad, P=P, rect=rect, packed=packed,
+                requested=requested, emitted=emitted, id_counts=id_counts, ids=ids,
+                tokens=tokens, offsets=offsets)
+
+
+def pin_packed_rows_equal_rectangular(o):
+    """Packing the committed rows (any slot order, P < capacity * T) changes
+    no output word; a slot whose committed rows would pass P writes nothing."""
+    for dt in (np.float32, np.uint16):
+        c = packed_case(dt)
+        assert c["P"] < c["cap"] * c["T"]
+        args = (c["requested"], c["id_counts"], c["ids"], c["emitted"], c["tokens"])
+        ref = np.full((c["cap"], c["T"], 258), -559038737, dtype=np.int32)
+        n_ref, lse_ref = o.frame(c["rect"], c["cap"], c["T"], c["V"], c["V_pad"], *args, 20, ref)
+        got = np.full_like(ref, -559038737)
+        n, lse = o.frame_packed(c["packed"], c["cap"], c["T"], c["P"], c["V"], c["V_pad"],
+                                *args, c["offsets"], 20, got)
+        assert n == n_ref and np.array_equal(got, ref)
+        assert np.array_equal(np.isnan(lse), np.isnan(lse_ref))
+        # slot 1's rows pushed past P: slot 1 becomes inactive, nothing else changes
+        off = c["offsets"].copy()
+        off[1] = c["P"] - 2  # 4 committed rows from P - 2
+        got = np.full_like(ref, -559038737)
+        n, _ = o.frame_packed(c["packed"], c["cap"], c["T"], c["P"], c["V"], c["V_pad"],
+                              *args, off, 20, got)
+        assert n == n_ref - 4
+        assert np.all(got[1] == -559038737)
+        keep = [s for s in range(c["cap"]) if s != 1]
+        assert np.array_equal(got[keep], ref[keep])
+
+
 # ------------------------------------------------------------ prompt scoring
 def _prompt_words_check(o, row, target, V=None):
     """Check one scored row against facts derived without the oracle's rank
@@ -453,4 +514,5 @@ ALL_PINS = [pin_uniform_row, pin_uniform_row_bf16, pin_two_level_row,
             pin_brute_force_order, pin_all_equal_row, pin_grid_row_by_counting,
             pin_subtraction_tie, pin_signed_zero, pin_v_below_k, pin_selected_ids,
             pin_frame_gating, pin_prompt_rank_by_counting, pin_prompt_subtraction_tie,
-            pin_prompt_invalid_rows, pin_prompt_small_rows_exhaustive, pin_prompt_chunk]
+            pin_prompt_invalid_rows, pin_prompt_small_rows_exhaustive, pin_prompt_chunk,
+            pin_packed_rows_equal_rectangular]

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
             "flare_logprobs_merge", "flare_status_string",
             "flare_logprobs_abi_version", "flare_prompt_logprobs_plan",
             "flare_prompt_logprobs_run", "flare_prompt_logprobs_reduce",
-            "flare_prompt_logprobs_merge"} <= set(names)
+            "flare_prompt_logprobs_merge", "flare_logprobs_plan_packed",
+            "flare_logprobs_run_packed"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(flp):
@@ -53,7 +54,7 @@ def test_abi_version_and_status_strings(flp):
 
 
 def test_plan_struct_layout_matches_header(flp):
-    # 16 int32-sized fields, 5 uint64, 6 reserved uint32
+    # 16 int32-sized fields, 5 uint64, packed_rows, 5 reserved uint32
     assert ctypes.sizeof(flp.PlanStruct) == 16 * 4 + 5 * 8 + 6 * 4
 
 
@@ -226,6 +227,50 @@ def test_plans_are_not_interchangeable(flp):
     rc, pplan = prompt_plan(flp)
     assert rc == 0
     assert run_status(flp, pplan) == 3
+
+
+# ------------------------------------------------------------ packed target rows
+def packed_plan(flp, capacity=128, T=8, P=600, V=248320, V_pad=248320, dtype=1, K=20):
+    plan = flp.PlanStruct()
+    rc = flp.lib().flare_logprobs_plan_packed(ctypes.byref(plan), capacity, T, P, V, V_pad, dtype,
+                                              K, -1)
+    return rc, plan
+
+
+def packed_status(flp, plan, **over):
+    args = dict(logits=FAKE, dtype=plan.dtype, rows=plan.packed_rows, V=plan.V, V_pad=plan.V_pad,
+                requested=FAKE, id_counts=FAKE, ids=FAKE, emitted=FAKE, tokens=FAKE,
+                offsets=FAKE, K=plan.K, out=FAKE, workspace=FAKE, stream=None)
+    args.update(over)
+    return flp.lib().flare_logprobs_run_packed(
+        ctypes.byref(plan), args["logits"], args["dtype"], args["rows"], args["V"], args["V_pad"],
+        args["requested"], args["id_counts"], args["ids"], args["emitted"], args["tokens"],
+        args["offsets"], args["K"], args["out"], args["workspace"], args["stream"])
+
+
+def test_packed_plan(flp):
+    rc, p = packed_plan(flp)
+    assert rc == 0 and p.packed_rows == 600 and p.mode == flp.MODE_GENERATION
+    rc0, p0 = host_plan(flp)
+    assert p.workspace_bytes == p0.workspace_bytes and p0.packed_rows == 0
+    for P in (0, -3, (1 << 30) + 1):
+        rc, p = packed_plan(flp, P=P)
+        assert rc == 1 and p.abi_version == 0
+
+
+def test_packed_run_rejects(flp):
+    rc, plan = packed_plan(flp)
+    assert rc == 0
+    for field in ("logits", "requested", "id_counts", "ids", "emitted", "tokens", "offsets",
+                  "out", "workspace"):
+        assert packed_status(flp, plan, **{field: None}) == 1, field
+    for over in (dict(rows=1024), dict(rows=599), dict(V=1000), dict(K=3), dict(dtype=0)):
+        assert packed_status(flp, plan, **over) == 3, over
+    # plans of the other layout
+    rc, rect = host_plan(flp)
+    assert packed_status(flp, rect, rows=1024) == 3
+    assert run_status(flp, plan, rows=600) == 3
+    assert run_status(flp, plan, rows=1024) == 3
 
 
 def test_binding_names_mirror_the_abi(flp):

@@ -53,6 +53,10 @@ MUTANTS = [
      "if (oracle_prompt_row(row, dtype, V_pad, targets[r],"),
     ("prompt_targets_reversed", "if (oracle_prompt_row(row, dtype, V, targets[r],",
      "if (oracle_prompt_row(row, dtype, V, targets[rows - 1 - r],"),
+    ("packed_rows_read_rectangular",
+     "(const char*)logits + (size_t)(first + t) * (size_t)V_pad * esize;",
+     "(const char*)logits + (size_t)pos * (size_t)V_pad * esize;"),
+    ("packed_range_unchecked", "if (e > 0 && (first < 0 || first + e > P)) continue;", ""),
     ("prompt_last_alternative_dropped", "sizeof(int32_t) * 2 * ORACLE_PROMPT_ALTS);",
      "sizeof(int32_t) * 2 * (ORACLE_PROMPT_ALTS - 1));"),
 ]
