@@ -286,33 +286,23 @@ class Plan:
         return torch.full((self.capacity, self.T, ROW_WORDS), fill, dtype=torch.int32,
                           device=self.device)
 
-    def run(self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
-            stream=None, phase: str = "all", row_offsets=None) -> torch.Tensor:
-        """One call: both launches (phase "all"), or only the first ("reduce")
-        or the second ("merge") of them.  A packed plan takes `row_offsets`
-        (int32 [capacity]) and the same phases."""
+    def bind(self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
+             phase: str = "all", row_offsets=None) -> "BoundCall":
+        """Validate one call's tensors once and marshal its C arguments: the
+        returned BoundCall launches with a single C call each time (for
+        serving loops and timing, where per-call Python checks would hold up
+        the GPU).  It keeps the tensors alive."""
         dev = self.device
         rows = self.capacity * self.T
-        if self.packed_rows is not None:
-            if row_offsets is None:
-                raise ValueError("a packed plan needs row_offsets")
-            _check(logits, "logits", self.torch_dtype, self.packed_rows * self.V_pad, dev)
+        packed = self.packed_rows is not None
+        if packed and row_offsets is None:
+            raise ValueError("a packed plan needs row_offsets")
+        if not packed and row_offsets is not None:
+            raise ValueError("row_offsets needs a packed plan")
+        _check(logits, "logits", self.torch_dtype,
+               (self.packed_rows if packed else rows) * self.V_pad, dev)
+        if packed:
             _check(row_offsets, "row_offsets", torch.int32, self.capacity, dev)
-            _check(tokens, "tokens", torch.int32, rows, dev)
-            _check(emitted_counts, "emitted_counts", torch.int32, self.capacity, dev)
-            _check(requested, "requested", torch.int32, self.capacity, dev)
-            _check(id_counts, "id_counts", torch.int32, self.capacity, dev)
-            _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
-            _check(out, "out", torch.int32, rows * ROW_WORDS, dev)
-            _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
-            fn = {"all": flare_logprobs_run_packed, "reduce": flare_logprobs_reduce_packed,
-                  "merge": flare_logprobs_merge_packed}[phase]
-            fn(self.raw, logits, self.torch_dtype, self.packed_rows, self.V, self.V_pad, requested,
-               id_counts, ids, emitted_counts, tokens, row_offsets, self.K, out, workspace, stream)
-            return out
-        fn = {"all": flare_logprobs_run, "reduce": flare_logprobs_reduce,
-              "merge": flare_logprobs_merge}[phase]
-        _check(logits, "logits", self.torch_dtype, rows * self.V_pad, dev)
         _check(tokens, "tokens", torch.int32, rows, dev)
         _check(emitted_counts, "emitted_counts", torch.int32, self.capacity, dev)
         _check(requested, "requested", torch.int32, self.capacity, dev)
@@ -320,9 +310,42 @@ class Plan:
         _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
         _check(out, "out", torch.int32, rows * ROW_WORDS, dev)
         _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
-        fn(self.raw, logits, self.torch_dtype, rows, self.V, self.V_pad, requested, id_counts, ids,
-           emitted_counts, tokens, self.K, out, workspace, stream)
+        name = {"all": "flare_logprobs_run", "reduce": "flare_logprobs_reduce",
+                "merge": "flare_logprobs_merge"}[phase] + ("_packed" if packed else "")
+        head = (ctypes.byref(self.raw), _ptr(logits), DTYPE_BF16 if self.torch_dtype ==
+                torch.bfloat16 else DTYPE_FP32, self.packed_rows if packed else rows, self.V,
+                self.V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids), _ptr(emitted_counts),
+                _ptr(tokens))
+        args = head + ((_ptr(row_offsets),) if packed else ()) + (self.K, _ptr(out),
+                                                                  _ptr(workspace))
+        keep = (self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
+                row_offsets)
+        return BoundCall(name, args, keep)
+
+    def run(self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
+            stream=None, phase: str = "all", row_offsets=None) -> torch.Tensor:
+        """One call: both launches (phase "all"), or only the first ("reduce")
+        or the second ("merge") of them.  A packed plan takes `row_offsets`
+        (int32 [capacity]) and the same phases."""
+        self.bind(logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
+                  phase=phase, row_offsets=row_offsets)(stream)
         return out
+
+
+class BoundCall:
+    """One validated call of a C entry point with its arguments marshalled;
+    calling it launches on `stream` (default: torch's current stream)."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.name = name
+        self._fn = getattr(lib(), name)
+        self._args = args
+        self._keep = keep  # the tensors whose pointers `args` holds
+
+    def __call__(self, stream=None) -> None:
+        rc = self._fn(*self._args, _stream(stream))
+        if rc != 0:
+            raise FlareError(rc, self.name)
 
 
 # ------------------------------------------------------------ prompt scoring
@@ -396,16 +419,21 @@ class PromptPlan:
         return torch.full((self.rows, PROMPT_ROW_WORDS), fill, dtype=torch.int32,
                           device=self.device)
 
-    def run(self, logits, targets, out, workspace, stream=None,
-            phase: str = "all") -> torch.Tensor:
-        """Both launches (phase "all"), or only "reduce" or "merge"."""
-        fn = {"all": flare_prompt_logprobs_run, "reduce": flare_prompt_logprobs_reduce,
-              "merge": flare_prompt_logprobs_merge}[phase]
+    def bind(self, logits, targets, out, workspace, phase: str = "all") -> BoundCall:
+        """Validate once and marshal the C arguments (see Plan.bind)."""
         dev = self.device
         _check(logits, "logits", self.torch_dtype, self.rows * self.V_pad, dev)
         _check(targets, "targets", torch.int32, self.rows, dev)
         _check(out, "out", torch.int32, self.rows * PROMPT_ROW_WORDS, dev)
         _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
-        fn(self.raw, logits, self.torch_dtype, self.rows, self.V, self.V_pad, targets, out,
-           workspace, stream)
+        name = {"all": "flare_prompt_logprobs_run", "reduce": "flare_prompt_logprobs_reduce",
+                "merge": "flare_prompt_logprobs_merge"}[phase]
+        args = (ctypes.byref(self.raw), _ptr(logits), dtype_code(self.torch_dtype), self.rows,
+                self.V, self.V_pad, _ptr(targets), _ptr(out), _ptr(workspace))
+        return BoundCall(name, args, (self, logits, targets, out, workspace))
+
+    def run(self, logits, targets, out, workspace, stream=None,
+            phase: str = "all") -> torch.Tensor:
+        """Both launches (phase "all"), or only "reduce" or "merge"."""
+        self.bind(logits, targets, out, workspace, phase=phase)(stream)
         return out

@@ -360,3 +360,28 @@ def test_hip_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager), f"replay {i}"
         del junk
+
+
+def test_bound_call_matches_run(oracle_handle):
+    """A prepared call (Plan.bind) launches the same work as Plan.run."""
+    import full_vocab_logprob_amd as flp
+    spec = synth.CONFIGS["C3"].with_(capacity=6, T=4, V=50000, V_pad=50000)
+    announce("bound call vs run")
+    w = synth.make(spec)
+    d = H.to_device(w)
+    a, _ = H.run_gpu(w, dev_inputs=d)
+    plan = H.make_plan(spec)
+    ws = plan.workspace()
+    out = plan.new_out(H.POISON)
+    call = plan.bind(d["logits"], d["tokens"], d["emitted"], d["requested"], d["id_counts"],
+                     d["ids"], out, ws)
+    call()
+    call(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), a)
+    with pytest.raises(ValueError):
+        plan.bind(d["logits"][:-1], d["tokens"], d["emitted"], d["requested"], d["id_counts"],
+                  d["ids"], out, ws)
+    with pytest.raises(flp.FlareError):
+        bad = flp.BoundCall(call.name, (call._args[0], 0) + call._args[2:], ())
+        bad()
