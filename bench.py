@@ -91,6 +91,8 @@ def parse():
                     help="also time the calls replayed from one captured HIP graph (0: skip)")
     ap.add_argument("--prompt", default=None,
                     help="measure prompt scoring on this chunk (P1 or P2) instead")
+    ap.add_argument("--records", type=int, default=0,
+                    help="1: emitted counts and tokens read from int64 completion records")
     ap.add_argument("--packed", type=int, default=0,
                     help="1: the frame's committed rows packed into P physical rows "
                          "(shuffled slot order) and read through row offsets")
@@ -338,6 +340,16 @@ def main():
     bound = {(c, ph): plan.bind(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
                                 phase=ph, row_offsets=offsets)
              for c in range(len(copies)) for ph in ("all", "reduce", "merge")}
+    if args.records:
+        # Timed calls read the counts and tokens from completion records
+        # (emitted count in field 3); the split launches keep the int32 inputs.
+        rec = np.zeros((spec.capacity, 16 + spec.T), dtype=np.int64)
+        rec[:, 3] = w.emitted
+        rec[:, 16:] = w.tokens.reshape(spec.capacity, spec.T)
+        rec_t = torch.from_numpy(rec).to(dev)
+        for c in range(len(copies)):
+            bound[(c, "all")] = plan.bind_records(copies[c], rec_t, requested, out, ws, 3,
+                                                  id_counts=id_counts, ids=ids)
 
     def step(i, phase="all"):
         bound[(i % len(copies), phase)](sh)
@@ -466,7 +478,9 @@ def main():
         "data": "synthetic (seeded Gumbel logits + 10 peak; garbage rows past each prefix)",
         "config": {"workload": f"{spec.name}: {spec.capacity} slots x T={spec.T} x V={spec.V} "
                                f"{'bf16' if bf16 else 'fp32'}, emitted 1..{spec.T}, K={spec.K}"
-                               + (f", packed into {packed_rows} rows" if packed_rows else ""),
+                               + (f", packed into {packed_rows} rows" if packed_rows else "")
+                               + (", counts and tokens from completion records"
+                                  if args.records else ""),
                    "active_rows": active, "capacity": spec.capacity, "T": spec.T, "V": spec.V,
                    "K": spec.K, "copies": len(copies), "oracle_rows_checked": checked},
         "roofline": {"bound": "hbm", "kernel": "reduce_kernel", "achieved": achieved_gbps,

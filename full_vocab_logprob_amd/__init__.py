@@ -30,7 +30,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libflare_logprobs.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_K = 20
 MAX_IDS = 128
 ROW_WORDS = 258
@@ -98,6 +98,12 @@ def lib() -> ctypes.CDLL:
             f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
                           c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
                           c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
+        L.flare_logprobs_run_records.restype = c.c_int
+        L.flare_logprobs_run_records.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32,
+                                                 c.c_int64, c.c_int32, c.c_int32, c.c_void_p,
+                                                 c.c_void_p, c.c_void_p, c.c_void_p, c.c_int32,
+                                                 c.c_int32, c.c_void_p, c.c_int32, c.c_void_p,
+                                                 c.c_void_p]
         L.flare_prompt_logprobs_plan.restype = c.c_int
         L.flare_prompt_logprobs_plan.argtypes = [c.POINTER(PlanStruct), c.c_int32, c.c_int32,
                                                  c.c_int32, c.c_int32, c.c_int32]
@@ -221,6 +227,20 @@ def flare_logprobs_merge_packed(plan: PlanStruct, logits, dtype, rows: int, V: i
                  id_counts, ids, emitted_counts, tokens, row_offsets, K, out, workspace, stream)
 
 
+def flare_logprobs_run_records(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                               requested, id_counts, ids, records, emitted_field: int, K: int,
+                               out, out_row_words: int, workspace, stream=None) -> None:
+    """One frame reading emitted counts and tokens from int64 completion
+    records [capacity, 16 + T]; id_counts/ids may both be None (natural only,
+    rows of 2 + 2K words)."""
+    rc = lib().flare_logprobs_run_records(ctypes.byref(plan), _ptr(logits), dtype_code(dtype),
+                                          rows, V, V_pad, _ptr(requested), _ptr(id_counts),
+                                          _ptr(ids), _ptr(records), emitted_field, K, _ptr(out),
+                                          out_row_words, _ptr(workspace), _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_run_records")
+
+
 def flare_logprobs_reduce(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
                           requested, id_counts, ids, emitted_counts, tokens, K: int, out,
                           workspace, stream=None) -> None:
@@ -330,6 +350,44 @@ class Plan:
         self.bind(logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
                   phase=phase, row_offsets=row_offsets)(stream)
         return out
+
+
+def _plan_bind_records(self, logits, records, requested, out, workspace, emitted_field: int,
+                       id_counts=None, ids=None) -> "BoundCall":
+    """Plan method: a prepared frame whose emitted counts and tokens come from
+    the int64 completion records [capacity, 16 + T] (emitted count at
+    `emitted_field`).  Without ID inputs (both None) `out` holds 2 + 2K words
+    per position, else 258."""
+    if self.packed_rows is not None:
+        raise ValueError("completion records take a rectangular plan")
+    dev = self.device
+    rows = self.capacity * self.T
+    words = ROW_WORDS if id_counts is not None else 2 + 2 * self.K
+    _check(logits, "logits", self.torch_dtype, rows * self.V_pad, dev)
+    _check(records, "records", torch.int64, self.capacity * (16 + self.T), dev)
+    _check(requested, "requested", torch.int32, self.capacity, dev)
+    if id_counts is not None or ids is not None:
+        _check(id_counts, "id_counts", torch.int32, self.capacity, dev)
+        _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
+    _check(out, "out", torch.int32, rows * words, dev)
+    _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
+    args = (ctypes.byref(self.raw), _ptr(logits), dtype_code(self.torch_dtype), rows, self.V,
+            self.V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids), _ptr(records),
+            emitted_field, self.K, _ptr(out), words, _ptr(workspace))
+    return BoundCall("flare_logprobs_run_records", args,
+                     (self, logits, records, requested, out, workspace, id_counts, ids))
+
+
+def _plan_run_records(self, logits, records, requested, out, workspace, emitted_field: int,
+                      id_counts=None, ids=None, stream=None) -> torch.Tensor:
+    """Plan method: bind_records, then launch on `stream`."""
+    self.bind_records(logits, records, requested, out, workspace, emitted_field, id_counts,
+                      ids)(stream)
+    return out
+
+
+Plan.bind_records = _plan_bind_records
+Plan.run_records = _plan_run_records
 
 
 class BoundCall:

@@ -147,10 +147,19 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
                       const int32_t* id_counts, const int32_t* ids,
                       const int32_t* emitted_counts, const int32_t* tokens,
                       const int32_t* row_offsets, int32_t K, int32_t* out, void* workspace,
-                      void* hip_stream, int phases) {
-  if (!plan || !logits || !requested || !id_counts || !ids || !emitted_counts || !tokens ||
-      !out || !workspace)
-    return FLARE_ERR_INVALID_ARGUMENT;
+                      void* hip_stream, int phases, const int64_t* records = nullptr,
+                      int32_t emitted_field = 0, int32_t row_words = FLARE_LOGPROBS_ROW_WORDS) {
+  // Completion records replace emitted_counts and tokens; a frame without ID
+  // inputs (both null) is natural-only with rows of 2 + 2K words.
+  const bool rec = records != nullptr;
+  if (!plan || !logits || !requested || !out || !workspace) return FLARE_ERR_INVALID_ARGUMENT;
+  if (!rec && (!emitted_counts || !tokens || !id_counts || !ids)) return FLARE_ERR_INVALID_ARGUMENT;
+  if ((id_counts == nullptr) != (ids == nullptr)) return FLARE_ERR_INVALID_ARGUMENT;
+  if (rec && (emitted_field < 0 || emitted_field >= flp::kRecordMeta)) return FLARE_ERR_INVALID_ARGUMENT;
+  if (row_words != FLARE_LOGPROBS_ROW_WORDS) {
+    // The compact extent: only without ID inputs, 2 + 2K words, 1 <= K <= 20.
+    if (id_counts || K < 1 || row_words != 2 + 2 * K) return FLARE_ERR_INVALID_ARGUMENT;
+  }
   // A packed plan takes its row offsets and P logit rows; a rectangular one neither.
   if ((plan->packed_rows > 0) != (row_offsets != nullptr)) return FLARE_ERR_PLAN_MISMATCH;
   if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
@@ -169,6 +178,9 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
   char* ws = (char*)workspace;
   flp::Params p;
   p.logits = logits;
+  p.crecords = records;
+  p.emitted_field = emitted_field;
+  p.row_words = row_words;
   p.row_offsets = plan->packed_rows > 0 ? row_offsets : nullptr;
   p.packed_rows = plan->packed_rows;
   p.requested = requested;
@@ -218,6 +230,9 @@ static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, 
   char* ws = (char*)workspace;
   flp::Params p;
   p.logits = logits;
+  p.crecords = nullptr;
+  p.emitted_field = 0;
+  p.row_words = FLARE_PROMPT_ROW_WORDS;
   p.row_offsets = nullptr;
   p.packed_rows = 0;
   p.requested = nullptr;
@@ -264,6 +279,19 @@ int flare_logprobs_run_packed(const flare_logprobs_plan_t* plan, const void* log
   return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
                     emitted_counts, tokens, row_offsets, K, out, workspace, hip_stream,
                     flp::kPhaseReduce | flp::kPhaseMerge);
+}
+
+int flare_logprobs_run_records(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int64_t* records, int32_t emitted_field,
+                               int32_t K, int32_t* out, int32_t out_row_words, void* workspace,
+                               void* hip_stream) {
+  if (!records) return FLARE_ERR_INVALID_ARGUMENT;
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids, nullptr,
+                    nullptr, nullptr, K, out, workspace, hip_stream,
+                    flp::kPhaseReduce | flp::kPhaseMerge, records, emitted_field,
+                    out_row_words);
 }
 
 int flare_logprobs_reduce_packed(const flare_logprobs_plan_t* plan, const void* logits,

@@ -15,6 +15,7 @@ constexpr int kMaxCapacity = 8192;  // slots whose active-row prefix fits in LDS
 constexpr int kPromptWords = 43;    // words of one scored prompt row
 constexpr int kPromptAlts = 20;     // alternatives of a scored prompt row
 constexpr int kMaxRangeRows = 64;   // rows one unit range may touch when scoring
+constexpr int kRecordMeta = 16;     // metadata fields before a completion record's tokens
 
 // Vocabulary lanes per 16-byte chunk, and per unit: the lanes one workgroup
 // holds in registers at a time (16,384 bf16 or 8,192 FP32 lanes, 32 KiB).
@@ -51,6 +52,10 @@ struct Params {
   PartRecord* records;
   float* lse;
   int32_t* slot_rows;   // [capacity + 1]: active rows before each slot, then their total
+  const int64_t* crecords;     // completion records [capacity, 16 + T] (or null): emitted
+                               // count at field emitted_field, tokens at fields 16 + t
+  int32_t emitted_field;
+  int32_t row_words;           // output words per position: 258, or 2 + 2K without ID inputs
   const int32_t* row_offsets;  // packed target rows: logit row of (s, t) is row_offsets[s] + t
   int32_t packed_rows;         // rows of a packed logits buffer (0: rectangular, row s T + t)
   int64_t V_pad;

@@ -53,7 +53,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kNanBits = 0x7FC00000u;
-constexpr int kRowWords = 258;
 
 // ------------------------------------------------------------------ keys
 // Order-preserving map of an FP32 value (with -0 read as +0) to uint32.
@@ -423,6 +422,20 @@ __device__ __forceinline__ int packed_rows_of(const Params& p, int s, int rows) 
   return rows > 0 && (off < 0 || (int64_t)off + rows > p.packed_rows) ? 0 : rows;
 }
 
+// A slot's emitted count and a position's chosen token, from the int32
+// inputs or from the slot's int64 completion record (values outside the
+// int32 range: a count reads as 0, a token as -1).
+__device__ __forceinline__ int emitted_of(const Params& p, int s) {
+  if (!p.crecords) return p.emitted[s];
+  const int64_t v = p.crecords[(int64_t)s * (kRecordMeta + p.T) + p.emitted_field];
+  return v < 0 || v > 0x7FFFFFFF ? 0 : (int)v;
+}
+__device__ __forceinline__ int token_of(const Params& p, int s, int t) {
+  if (!p.crecords) return p.tokens[s * p.T + t];
+  const int64_t v = p.crecords[(int64_t)s * (kRecordMeta + p.T) + kRecordMeta + t];
+  return v < -0x80000000ll || v > 0x7FFFFFFF ? -1 : (int)v;
+}
+
 // A scored prompt row (one per slot) is active when its target is an ID.
 template <bool SCORE>
 __device__ __forceinline__ int slot_word(const Params& p, int s) {
@@ -431,7 +444,7 @@ __device__ __forceinline__ int slot_word(const Params& p, int s) {
     return (tk >= 0 && tk < p.V) ? 1 : 0;
   }
   // The words are loaded together (one round trip).
-  const int r = p.requested[s], e = p.emitted[s], n = p.id_counts[s];
+  const int r = p.requested[s], e = emitted_of(p, s), n = p.id_counts ? p.id_counts[s] : 0;
   int rows = r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
   if (p.row_offsets) rows = packed_rows_of(p, s, rows);
   return rows | (n > 0 ? kSelBit : 0);
@@ -622,13 +635,13 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int s = row / p.T, t = row - s * p.T;
   // Every input word this row needs, loaded at once (the row counts are
   // only meaningful for an active row).
-  const int req = SCORE ? 1 : p.requested[s], emi = SCORE ? 1 : p.emitted[s];
-  const int cnt = SCORE ? 0 : p.id_counts[s];
+  const int req = SCORE ? 1 : p.requested[s], emi = SCORE ? 1 : emitted_of(p, s);
+  const int cnt = SCORE || !p.id_counts ? 0 : p.id_counts[s];
   const int off = !SCORE && p.row_offsets ? p.row_offsets[s] : 0;
   const int before = p.slot_rows[s], total = p.slot_rows[p.capacity];
-  const int tok = p.tokens[row];
+  const int tok = SCORE ? p.tokens[row] : token_of(p, s, t);
   const int V = p.V, U = p.units;
-  int32_t* out = p.out + (int64_t)row * (SCORE ? kPromptWords : kRowWords);
+  int32_t* out = p.out + (int64_t)row * (SCORE ? kPromptWords : p.row_words);
   if (SCORE && !(tok >= 0 && tok < V)) {
     // [-1, NaN, rank 0, then (-1, NaN) twenty times]
     if (lane < kPromptWords)

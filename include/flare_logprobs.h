@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FLARE_LOGPROBS_ABI_VERSION 4u
+#define FLARE_LOGPROBS_ABI_VERSION 5u
 #define FLARE_LOGPROBS_MAX_K 20
 #define FLARE_LOGPROBS_MAX_IDS 128
 #define FLARE_LOGPROBS_ROW_WORDS 258 /* 2 + 2 * 128 */
@@ -184,6 +184,34 @@ int flare_logprobs_merge_packed(const flare_logprobs_plan_t* plan, const void* l
                                 const int32_t* ids, const int32_t* emitted_counts,
                                 const int32_t* tokens, const int32_t* row_offsets, int32_t K,
                                 int32_t* out, void* workspace, void* hip_stream);
+
+/*
+ * Adapter for the completion records and for cores without ID inputs
+ * (generation design page, buffer table: completion_records int64
+ * [2, capacity, 16 + T], one record per slot with 16 metadata fields, the
+ * emitted count among them, then T token IDs; declaration paragraph: a core
+ * without the ID inputs has rows of 2 + 2K words, 1 <= K <= 20, and serves
+ * natural alternatives only; MTP design page, catalog paragraph).
+ *   records        device int64 [capacity, 16 + T]: one frame of records.
+ *                  Slot s's emitted count is field emitted_field (0..15; the
+ *                  pages do not fix its index), its verify token t is field
+ *                  16 + t.  A count outside [0, 2^31) reads as 0, a token
+ *                  outside the int32 range as -1 (then written with NaN bits).
+ *   id_counts, ids both NULL (no ID inputs: every slot natural) or both given.
+ *   out_row_words  258, or 2 + 2K (only without ID inputs): out is
+ *                  int32 [capacity, T, out_row_words].
+ * Everything else is as for flare_logprobs_run (rectangular plans only; a
+ * packed plan is FLARE_ERR_PLAN_MISMATCH).  Host-checkable errors
+ * (FLARE_ERR_INVALID_ARGUMENT): records NULL, emitted_field outside [0, 16),
+ * one ID input NULL and not the other, an extent other than 258 or 2 + 2K, or
+ * 2 + 2K with ID inputs or K = 0.
+ */
+int flare_logprobs_run_records(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int64_t* records, int32_t emitted_field,
+                               int32_t K, int32_t* out, int32_t out_row_words, void* workspace,
+                               void* hip_stream);
 
 /*
  * The two launches of flare_logprobs_run, for callers that want to order

@@ -67,6 +67,11 @@ class Oracle:
                                                  c.c_void_p, c.c_void_p, c.c_void_p,
                                                  c.c_void_p, c.c_void_p, c.c_int32,
                                                  c.c_void_p, c.c_void_p]
+        self.lib.oracle_frame_records.restype = c.c_int64
+        self.lib.oracle_frame_records.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
+                                                  c.c_int32, c.c_int32, c.c_void_p, c.c_void_p,
+                                                  c.c_void_p, c.c_void_p, c.c_int32, c.c_int32,
+                                                  c.c_int32, c.c_void_p, c.c_void_p]
         self.lib.oracle_prompt_row.restype = c.c_int
         self.lib.oracle_prompt_row.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
                                                c.c_void_p, c.c_void_p]
@@ -151,6 +156,35 @@ class Oracle:
                                          off.ctypes.data, K, out.ctypes.data, lse.ctypes.data)
         if n < 0:
             raise ValueError("oracle_frame_packed rejected its arguments")
+        return int(n), lse
+
+    def frame_records(self, logits: np.ndarray, capacity: int, T: int, V: int, V_pad: int,
+                      requested, id_counts, ids, records, emitted_field: int, K: int,
+                      out: np.ndarray):
+        """One frame reading counts and tokens from int64 records [capacity, 16 + T].
+        id_counts/ids None: natural only, `out` [capacity, T, 2 + 2K]; else 258."""
+        logits = np.ascontiguousarray(logits)
+        req = np.ascontiguousarray(requested, dtype=np.int32)
+        rec = np.ascontiguousarray(records, dtype=np.int64)
+        assert rec.size == capacity * (16 + T) and req.size == capacity
+        if id_counts is None:
+            cnt = idv = None
+            words = 2 + 2 * K
+        else:
+            cnt = np.ascontiguousarray(id_counts, dtype=np.int32)
+            idv = np.ascontiguousarray(ids, dtype=np.int32)
+            words = ROW_WORDS
+        assert out.dtype == np.int32 and out.size == capacity * T * words
+        assert out.flags.c_contiguous
+        lse = np.full(capacity * T, np.nan, dtype=np.float32)
+        n = self.lib.oracle_frame_records(logits.ctypes.data, self._dtype_of(logits), capacity, T,
+                                          V, V_pad, req.ctypes.data,
+                                          None if cnt is None else cnt.ctypes.data,
+                                          None if idv is None else idv.ctypes.data,
+                                          rec.ctypes.data, emitted_field, K, words,
+                                          out.ctypes.data, lse.ctypes.data)
+        if n < 0:
+            raise ValueError("oracle_frame_records rejected its arguments")
         return int(n), lse
 
     def prompt_row(self, row: np.ndarray, target: int, V: int | None = None):

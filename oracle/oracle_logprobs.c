@@ -45,6 +45,12 @@
  *       value bits 0x7FC00000 and is never dereferenced.
  *   R10 emitted counts are clamped to [0, T], ID counts to [0, 128]; a zero
  *       request flag wins over a nonzero ID count.
+ *   R14 completion records: slot s's record is int64 [16 + T]; its emitted
+ *       count is the field the caller names (the pages list the fields
+ *       without their indices) and verify token t is field 16 + t.  A
+ *       count outside [0, 2^31) reads as 0, a token outside the int32
+ *       range as -1.  Without ID inputs every slot is natural and each
+ *       position holds 2 + 2K words.
  *   R13 packed target rows: slot s's verify row t is logit row
  *       row_offsets[s] + t of P rows; a slot whose committed rows would leave
  *       [0, P) is treated as not emitting (nothing read or written).
@@ -342,3 +348,53 @@ int64_t oracle_frame_packed(const void* logits, int dtype, int32_t capacity,
   }
   return active;
 }
+
+/*
+ * One frame whose emitted counts and chosen tokens are read from the int64
+ * completion records [capacity, 16 + T] (GLP buffer table; MTP design page,
+ * catalog paragraph; reading R14).  `id_counts` and `ids` may both be NULL
+ * (a core without ID inputs, GLP declaration paragraph): then every slot is
+ * natural and position (s, t) occupies `row_words` = 2 + 2K words of `out`;
+ * otherwise row_words is 258.  Returns the active row count, or -1.
+ */
+int64_t oracle_frame_records(const void* logits, int dtype, int32_t capacity,
+                             int32_t T, int32_t V, int32_t V_pad,
+                             const int32_t* requested, const int32_t* id_counts,
+                             const int32_t* ids, const int64_t* records,
+                             int32_t emitted_field, int32_t K, int32_t row_words,
+                             int32_t* out, float* lse_out) {
+  if (!logits || !requested || !records || !out) return -1;
+  if ((id_counts == NULL) != (ids == NULL)) return -1;
+  if (emitted_field < 0 || emitted_field >= 16) return -1;
+  if (capacity < 1 || T < 1 || V < 1 || V_pad < V || K < 0 || K > ORACLE_MAX_K)
+    return -1;
+  if (id_counts ? row_words != ORACLE_ROW_WORDS : (K < 1 || row_words != 2 + 2 * K))
+    return -1;
+  size_t esize = (dtype == ORACLE_DTYPE_BF16) ? 2 : 4;
+  int32_t words[ORACLE_ROW_WORDS];
+  int64_t active = 0;
+  for (int32_t s = 0; s < capacity; ++s) {
+    const int64_t* record = records + (size_t)s * (16 + (size_t)T);
+    if (!requested[s]) continue;
+    int64_t count = record[emitted_field];
+    int32_t e = (count < 0 || count > 2147483647LL) ? 0 : (int32_t)count;
+    if (e > T) e = T;
+    int32_t n = 0;
+    if (id_counts) n = id_counts[s] < 0 ? 0 : (id_counts[s] > ORACLE_MAX_IDS ? ORACLE_MAX_IDS : id_counts[s]);
+    for (int32_t t = 0; t < e; ++t) {
+      int64_t tok64 = record[16 + t];
+      int32_t tok = (tok64 < -2147483648LL || tok64 > 2147483647LL) ? -1 : (int32_t)tok64;
+      int64_t at = (int64_t)s * T + t;
+      const char* row = (const char*)logits + (size_t)at * (size_t)V_pad * esize;
+      float L;
+      int used = oracle_row(row, dtype, V, tok, n, ids ? ids + (size_t)s * ORACLE_MAX_IDS : NULL,
+                            K, words, &L);
+      if (used < 0 || used > row_words) return -1;
+      memcpy(out + (size_t)at * (size_t)row_words, words, sizeof(int32_t) * (size_t)used);
+      if (lse_out) lse_out[at] = L;
+      ++active;
+    }
+  }
+  return active;
+}
+

@@ -403,6 +403,44 @@ def pin_packed_rows_equal_rectangular(o):
         assert np.array_equal(got[keep], ref[keep])
 
 
+# ------------------------------------------------------------ completion records
+def pin_records_equal_int32_inputs(o):
+    """Reading the emitted count from a record field and the tokens from
+    fields 16 + t (GLP buffer table) gives the frame of the same values
+    passed as int32 arrays; an out-of-range count reads as 0 and an
+    out-of-range token as -1 (reading R14).  Without ID inputs each position
+    holds exactly 2 + 2K words: the natural words of the 258-word frame."""
+    cap, T, V = 6, 3, 50
+    rng = np.random.default_rng(23)
+    logits = (rng.standard_normal((cap * T, V)) * 3).astype(np.float32)
+    requested = np.array([1, 1, 0, 1, 1, 1], dtype=np.int32)
+    field = 5
+    rec = rng.integers(-2**40, 2**40, size=(cap, 16 + T)).astype(np.int64)  # metadata noise
+    counts = np.array([2, 3, 1, 2**40 + 2, -4, 7], dtype=np.int64)  # 2^40 + 2 would truncate to 2
+    rec[:, field] = counts
+    toks = rng.integers(0, V, size=(cap, T)).astype(np.int64)
+    toks[1, 1] = 2**33  # outside int32: -1
+    toks[5, 0] = -7
+    rec[:, 16:] = toks
+    emitted = np.array([2, 3, 1, 0, 0, 3], dtype=np.int32)  # R14 read by hand, clamped to T
+    tokens = np.where((toks < -2**31) | (toks >= 2**31), -1, toks).astype(np.int32).reshape(-1)
+    id_counts = np.array([0, 4, 0, 0, 0, 0], dtype=np.int32)
+    ids = np.full(cap * 128, -2, dtype=np.int32)
+    ids[128:132] = [7, 49, 0, 7]
+    ref = np.full((cap, T, 258), -559038737, dtype=np.int32)
+    n_ref, _ = o.frame(logits, cap, T, V, V, requested, id_counts, ids, emitted, tokens, 20, ref)
+    got = np.full_like(ref, -559038737)
+    n, _ = o.frame_records(logits, cap, T, V, V, requested, id_counts, ids, rec, field, 20, got)
+    assert n == n_ref == 8 and np.array_equal(got, ref)
+    assert ref[1, 1, 0] == -1 and ref[1, 1, 1] == NAN_BITS
+    # no ID inputs: natural everywhere, 2 + 2K words per position
+    ref0 = np.full((cap, T, 258), -559038737, dtype=np.int32)
+    o.frame(logits, cap, T, V, V, requested, np.zeros(cap, np.int32), ids, emitted, tokens, 7, ref0)
+    got0 = np.full((cap, T, 16), -559038737, dtype=np.int32)
+    o.frame_records(logits, cap, T, V, V, requested, None, None, rec, field, 7, got0)
+    assert np.array_equal(got0, ref0[:, :, :16])
+
+
 # ------------------------------------------------------------ prompt scoring
 def _prompt_words_check(o, row, target, V=None):
     """Check one scored row against facts derived without the oracle's rank
@@ -515,4 +553,4 @@ ALL_PINS = [pin_uniform_row, pin_uniform_row_bf16, pin_two_level_row,
             pin_subtraction_tie, pin_signed_zero, pin_v_below_k, pin_selected_ids,
             pin_frame_gating, pin_prompt_rank_by_counting, pin_prompt_subtraction_tie,
             pin_prompt_invalid_rows, pin_prompt_small_rows_exhaustive, pin_prompt_chunk,
-            pin_packed_rows_equal_rectangular]
+            pin_packed_rows_equal_rectangular, pin_records_equal_int32_inputs]

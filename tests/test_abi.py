@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
             "flare_logprobs_abi_version", "flare_prompt_logprobs_plan",
             "flare_prompt_logprobs_run", "flare_prompt_logprobs_reduce",
             "flare_prompt_logprobs_merge", "flare_logprobs_plan_packed",
-            "flare_logprobs_run_packed"} <= set(names)
+            "flare_logprobs_run_packed", "flare_logprobs_run_records"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(flp):
@@ -271,6 +271,35 @@ def test_packed_run_rejects(flp):
     assert packed_status(flp, rect, rows=1024) == 3
     assert run_status(flp, plan, rows=600) == 3
     assert run_status(flp, plan, rows=1024) == 3
+
+
+# ------------------------------------------------------------ completion records
+def records_status(flp, plan, **over):
+    args = dict(logits=FAKE, dtype=plan.dtype, rows=plan.capacity * plan.T, V=plan.V,
+                V_pad=plan.V_pad, requested=FAKE, id_counts=FAKE, ids=FAKE, records=FAKE,
+                field=3, K=plan.K, out=FAKE, words=258, workspace=FAKE, stream=None)
+    args.update(over)
+    return flp.lib().flare_logprobs_run_records(
+        ctypes.byref(plan), args["logits"], args["dtype"], args["rows"], args["V"], args["V_pad"],
+        args["requested"], args["id_counts"], args["ids"], args["records"], args["field"],
+        args["K"], args["out"], args["words"], args["workspace"], args["stream"])
+
+
+def test_records_run_rejects(flp):
+    rc, plan = host_plan(flp)
+    assert rc == 0
+    for field in ("logits", "requested", "records", "out", "workspace"):
+        assert records_status(flp, plan, **{field: None}) == 1, field
+    assert records_status(flp, plan, id_counts=None) == 1  # one ID input without the other
+    assert records_status(flp, plan, ids=None) == 1
+    assert records_status(flp, plan, field=-1) == 1 and records_status(flp, plan, field=16) == 1
+    assert records_status(flp, plan, words=42) == 1            # 2 + 2K needs no ID inputs
+    assert records_status(flp, plan, id_counts=None, ids=None, words=41) == 1
+    assert records_status(flp, plan, K=5) == 3                 # K differs from the plan
+    rc, p0 = host_plan(flp, K=0)
+    assert records_status(flp, p0, id_counts=None, ids=None, words=2) == 1  # K = 0
+    rc, pk = packed_plan(flp)
+    assert records_status(flp, pk, rows=600) == 3
 
 
 def test_binding_names_mirror_the_abi(flp):

@@ -57,6 +57,14 @@ MUTANTS = [
      "(const char*)logits + (size_t)(first + t) * (size_t)V_pad * esize;",
      "(const char*)logits + (size_t)pos * (size_t)V_pad * esize;"),
     ("packed_range_unchecked", "if (e > 0 && (first < 0 || first + e > P)) continue;", ""),
+    ("records_token_field_off_by_one", "int64_t tok64 = record[16 + t];",
+     "int64_t tok64 = record[15 + t];"),
+    ("records_stride_short", "records + (size_t)s * (16 + (size_t)T);",
+     "records + (size_t)s * (15 + (size_t)T);"),
+    ("records_count_unchecked", "int32_t e = (count < 0 || count > 2147483647LL) ? 0 : (int32_t)count;",
+     "int32_t e = (int32_t)count;"),
+    ("records_compact_stride", "memcpy(out + (size_t)at * (size_t)row_words,",
+     "memcpy(out + (size_t)at * (size_t)(row_words - 2),"),
     ("prompt_last_alternative_dropped", "sizeof(int32_t) * 2 * ORACLE_PROMPT_ALTS);",
      "sizeof(int32_t) * 2 * (ORACLE_PROMPT_ALTS - 1));"),
 ]
