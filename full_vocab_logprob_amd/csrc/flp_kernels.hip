@@ -41,6 +41,17 @@
 // The pages' own scheme ranks normalized values in a second pass over the
 // vocabulary; ranking raw values and re-keying only the survivors is what
 // lets this path read the logits once.
+//
+// The same two kernels serve three variants of the input and output:
+//   - prompt scoring (SCORE): one row per scored prompt position, active when
+//     its target is an ID; the stream also counts, per part, the lanes above
+//     the target's logit, and the merge turns the counts into the rank
+//     (recounting a part only where the subtraction tied a larger logit with
+//     the target) and writes 43-word rows;
+//   - packed target rows: slot s's row t is logit row row_offsets[s] + t of P
+//     rows, the offsets kept in the slot table in LDS;
+//   - completion records: emitted counts and tokens read from int64 records,
+//     with optional ID inputs and rows of 2 + 2K words.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
