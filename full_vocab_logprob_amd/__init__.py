@@ -342,6 +342,39 @@ class Plan:
                 row_offsets)
         return BoundCall(name, args, keep)
 
+    def bind_records(self, logits, records, requested, out, workspace, emitted_field: int,
+                     id_counts=None, ids=None) -> "BoundCall":
+        """A prepared frame whose emitted counts and tokens come from
+        the int64 completion records [capacity, 16 + T] (emitted count at
+        `emitted_field`).  Without ID inputs (both None) `out` holds 2 + 2K words
+        per position, else 258."""
+        if self.packed_rows is not None:
+            raise ValueError("completion records take a rectangular plan")
+        dev = self.device
+        rows = self.capacity * self.T
+        words = ROW_WORDS if id_counts is not None else 2 + 2 * self.K
+        _check(logits, "logits", self.torch_dtype, rows * self.V_pad, dev)
+        _check(records, "records", torch.int64, self.capacity * (16 + self.T), dev)
+        _check(requested, "requested", torch.int32, self.capacity, dev)
+        if id_counts is not None or ids is not None:
+            _check(id_counts, "id_counts", torch.int32, self.capacity, dev)
+            _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
+        _check(out, "out", torch.int32, rows * words, dev)
+        _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
+        args = (ctypes.byref(self.raw), _ptr(logits), dtype_code(self.torch_dtype), rows, self.V,
+                self.V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids), _ptr(records),
+                emitted_field, self.K, _ptr(out), words, _ptr(workspace))
+        return BoundCall("flare_logprobs_run_records", args,
+                         (self, logits, records, requested, out, workspace, id_counts, ids))
+
+
+    def run_records(self, logits, records, requested, out, workspace, emitted_field: int,
+                    id_counts=None, ids=None, stream=None) -> torch.Tensor:
+        """bind_records, then launch on `stream`."""
+        self.bind_records(logits, records, requested, out, workspace, emitted_field, id_counts,
+                          ids)(stream)
+        return out
+
     def run(self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
             stream=None, phase: str = "all", row_offsets=None) -> torch.Tensor:
         """One call: both launches (phase "all"), or only the first ("reduce")
@@ -352,42 +385,6 @@ class Plan:
         return out
 
 
-def _plan_bind_records(self, logits, records, requested, out, workspace, emitted_field: int,
-                       id_counts=None, ids=None) -> "BoundCall":
-    """Plan method: a prepared frame whose emitted counts and tokens come from
-    the int64 completion records [capacity, 16 + T] (emitted count at
-    `emitted_field`).  Without ID inputs (both None) `out` holds 2 + 2K words
-    per position, else 258."""
-    if self.packed_rows is not None:
-        raise ValueError("completion records take a rectangular plan")
-    dev = self.device
-    rows = self.capacity * self.T
-    words = ROW_WORDS if id_counts is not None else 2 + 2 * self.K
-    _check(logits, "logits", self.torch_dtype, rows * self.V_pad, dev)
-    _check(records, "records", torch.int64, self.capacity * (16 + self.T), dev)
-    _check(requested, "requested", torch.int32, self.capacity, dev)
-    if id_counts is not None or ids is not None:
-        _check(id_counts, "id_counts", torch.int32, self.capacity, dev)
-        _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
-    _check(out, "out", torch.int32, rows * words, dev)
-    _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
-    args = (ctypes.byref(self.raw), _ptr(logits), dtype_code(self.torch_dtype), rows, self.V,
-            self.V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids), _ptr(records),
-            emitted_field, self.K, _ptr(out), words, _ptr(workspace))
-    return BoundCall("flare_logprobs_run_records", args,
-                     (self, logits, records, requested, out, workspace, id_counts, ids))
-
-
-def _plan_run_records(self, logits, records, requested, out, workspace, emitted_field: int,
-                      id_counts=None, ids=None, stream=None) -> torch.Tensor:
-    """Plan method: bind_records, then launch on `stream`."""
-    self.bind_records(logits, records, requested, out, workspace, emitted_field, id_counts,
-                      ids)(stream)
-    return out
-
-
-Plan.bind_records = _plan_bind_records
-Plan.run_records = _plan_run_records
 
 
 class BoundCall:
