@@ -631,8 +631,11 @@ __device__ __forceinline__ int count_above(const char* rowp, int lo, int hi, flo
 // the target's, x_t, and kept the smallest of them, x_n.  r(x) = fl32(x - L)
 // is monotone, so no lane at or below x_t can report more than r(x_t), and a
 // lane above x_t reports at least r(x_n) >= r(x_t); the raw count is exact
-// unless r(x_n) == r(x_t) (the subtraction tied them), and such a part is
-// counted again lane by lane with reported values.
+// unless r(x_n) == r(x_t) (the subtraction tied them).  FP32 parts also carry
+// the number of lanes at x_n and the next larger value x_m: when r(x_m) >
+// r(x_t) exactly those lanes tie and are taken off; otherwise (and for bf16,
+// whose spacing makes such ties rare) the part is counted again lane by lane
+// with reported values.
 template <int DT, bool VEC, bool SCORE>
 __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   using E = Elem<DT>;
@@ -689,8 +692,8 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // parts (rows of many parts) staged in LDS, and each part's guard words
   float pm = kNegInf, ps = 0.0f;
   uint64_t c_key = 0ull;
-  int p_above = 0;
-  float p_next = __builtin_huge_valf();
+  int p_above = 0, p_count = 0;
+  float p_next = __builtin_huge_valf(), p_next2 = __builtin_huge_valf();
   if (lane < np) {
     pm = rec[u0].m;
     ps = rec[u0].s;
@@ -698,17 +701,26 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
     if (SCORE) {
       p_above = rec[u0].above;
       p_next = rec[u0].next_above;
+      if (DT == 0) {
+        const uint64_t ex = rec[u0].keys[kKeep - 1];
+        p_count = (int)(uint32_t)ex;
+        p_next2 = __uint_as_float((uint32_t)(ex >> 32));
+      }
     }
   }
-  const uint64_t raw0 = (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
-  const uint64_t raw1 = 2 + (lane >> 5) < np ? rec[part_u0[2 + (lane >> 5)]].keys[lane & 31] : 0ull;
+  // FP32 scoring records use key slot 31 for the rank (read above), not a key.
+  const bool extra_slot = SCORE && DT == 0 && (lane & 31) == kKeep - 1;
+  const uint64_t raw0 =
+      !extra_slot && (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
+  const uint64_t raw1 =
+      !extra_slot && 2 + (lane >> 5) < np ? rec[part_u0[2 + (lane >> 5)]].keys[lane & 31] : 0ull;
   if (natural && np > 4) {
     // All loads in flight at once: a row of many parts pays one round trip.
     uint64_t pre[kLdsPairs];
 #pragma unroll
     for (int i = 0; i < kLdsPairs; ++i) {
       const int part = 4 + 2 * i + (lane >> 5);
-      pre[i] = part < np ? rec[part_u0[part]].keys[lane & 31] : 0ull;
+      pre[i] = !extra_slot && part < np ? rec[part_u0[part]].keys[lane & 31] : 0ull;
     }
 #pragma unroll
     for (int i = 0; i < kLdsPairs; ++i) pair_keys[wv][i][lane] = pre[i];
@@ -739,7 +751,14 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   }
   if (SCORE) {
     const float rt = reported(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x_tok), 0)), L);
-    uint64_t ties = __ballot(lane < np && p_next < __builtin_huge_valf() && reported(p_next, L) == rt);
+    bool tie = lane < np && p_next < __builtin_huge_valf() && reported(p_next, L) == rt;
+    if (DT == 0 && tie && !(p_next2 < __builtin_huge_valf() && reported(p_next2, L) == rt)) {
+      // Only the lanes at x_n tie with the target: the next larger value
+      // already reports more, so the overcount is their number.
+      p_above -= p_count;
+      tie = false;
+    }
+    uint64_t ties = __ballot(tie);
     while (ties != 0ull) {
       const int part = __builtin_ctzll(ties);
       ties &= ties - 1ull;
@@ -773,7 +792,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
     const int part = pb + (lane >> 5);
     uint64_t raw = 0ull;
     if (pb < 4 + 2 * kLdsPairs) raw = pair_keys[wv][(pb - 4) >> 1][lane];
-    else if (part < np) raw = rec[part_u0[part]].keys[lane & 31];
+    else if (!extra_slot && part < np) raw = rec[part_u0[part]].keys[lane & 31];
     top = merge_top32(top, sort_halves_desc(raw != 0ull ? final_key(raw, L) : 0ull, lane), lane);
   }
   // ---- guard, one lane per part
@@ -793,7 +812,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
     for (int pb = 0; pb < np; pb += 2) {
       const int part = pb + (lane >> 5);
       uint64_t f = 0ull;
-      if (part < np && !((unsafe >> part) & 1ull)) {
+      if (!extra_slot && part < np && !((unsafe >> part) & 1ull)) {
         const uint64_t raw = rec[part_u0[part]].keys[lane & 31];
         if (raw != 0ull) f = final_key(raw, L);
       }
@@ -848,7 +867,9 @@ struct ReduceSmem {
   float wm[2][kWaves];                   // a part's per-wave max and scaled sum
   float ws[2][kWaves];
   int wabove[2][kWaves];                 // scoring: a part's per-wave count above the target
-  float wnext[2][kWaves];                // and smallest logit above it
+  float wnext[2][kWaves];                // and smallest logit above it,
+  int wcount[2][kWaves];                 // the lanes holding it (FP32)
+  float wnext2[2][kWaves];               // and the next larger logit (FP32)
   int arrive[2];                         // waves that flushed the part of this parity
   int merged;                            // parts of the range merged into records
   int n_staged;                          // records staged in `staged`
@@ -1043,7 +1064,8 @@ struct PassOut {
 // unit, which only delays that unit's refills.  `ht`, `stage` and `o.tau`
 // return the threshold and its test.
 // With SCORE, a chunk whose maximum exceeds xa (the target's logit) also
-// adds its lanes above xa to `above` and their minimum to `next_above`.
+// adds its lanes above xa to `above` and their minimum to `next_above`
+// (FP32: with the count of lanes at that minimum and the next larger value).
 template <int DT, bool VEC, bool SCORE>
 __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[kChunks],
                                              float m_l, bool tail, int wave_base,
@@ -1051,7 +1073,7 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
                                              const char* next_rowp, int next_base, bool has_next,
                                              int V, int lane, bool& stage, HotTest& ht, Stage& st,
                                              bool first, int kq, float xa, int& above,
-                                             float& next_above) {
+                                             float& next_above, int& next_count, float& next2) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   PassOut o;
@@ -1103,7 +1125,16 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
         const float xv = E::get(raw[c], j);
         const bool gt = xv > xa;
         above += gt ? 1 : 0;
-        next_above = gt ? fminf(next_above, xv) : next_above;
+        if (DT == 0) {
+          // FP32 also keeps how many lanes hold that smallest value and the
+          // next larger value (see the merge's rank).
+          const bool lt = gt && xv < next_above, eq = gt && xv == next_above;
+          next2 = lt ? next_above : ((gt && !eq && xv < next2) ? xv : next2);
+          next_count = lt ? 1 : (eq ? next_count + 1 : next_count);
+          next_above = lt ? xv : next_above;
+        } else {
+          next_above = gt ? fminf(next_above, xv) : next_above;
+        }
       }
     }
     if (stage) stage_chunk(st, raw[c], mc > ht.above, c, lane);
@@ -1259,6 +1290,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   }
   int above = 0;
   float next_above = __builtin_huge_valf();
+  int next_count = 0;
+  float next2 = __builtin_huge_valf();
 
   // Per lane: running max m_l and the sum, relative to m_l, of exp over the
   // lane's values except one occurrence of m_l (whose term is exactly 1 and
@@ -1345,7 +1378,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     const PassOut po = unit_pass<DT, VEC, SCORE>(
         raw, cm, m_l, tail, wave_base, row_rsrc(nxt.rowp, has_next ? row_bytes : 0), nxt.rowp,
         next_base, has_next, V, lane, stage, ht, st, natural && part_starts, kfirst, xa, above,
-        next_above);
+        next_above, next_count, next2);
     const float lm = po.lm;
 
     // ---- fold the unit into the lane's running (max, sum)
@@ -1437,9 +1470,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
           nx = fminf(nx, xlanef<4>(nx, lane));
           nx = fminf(nx, xlanef<2>(nx, lane));
           nx = fminf(nx, xlanef<1>(nx, lane));
+          int nc = 0;
+          float n2 = __builtin_huge_valf();
+          if (DT == 0) {
+            // lanes at the wave's minimum add their counts; the others offer
+            // their minimum as a candidate for the next larger value
+            nc = wave_sum_i32(next_above == nx ? next_count : 0, lane);
+            n2 = next_above == nx ? next2 : next_above;
+            n2 = fminf(n2, xlanef<32>(n2, lane));
+            n2 = fminf(n2, xlanef<16>(n2, lane));
+            n2 = fminf(n2, xlanef<8>(n2, lane));
+            n2 = fminf(n2, xlanef<4>(n2, lane));
+            n2 = fminf(n2, xlanef<2>(n2, lane));
+            n2 = fminf(n2, xlanef<1>(n2, lane));
+          }
           if (lane == 0) {
             sh.wabove[b][w] = na;
             sh.wnext[b][w] = nx;
+            sh.wcount[b][w] = nc;
+            sh.wnext2[b][w] = n2;
           }
         }
       }
@@ -1476,13 +1525,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
               if (sh.wm[b][i] != kNegInf)
                 S += sh.ws[b][i] * __builtin_amdgcn_exp2f((sh.wm[b][i] - M) * kLog2e);
           for (int i = 0; i < kWaves; ++i) pcut = sh.flush_cut[b][i] > pcut ? sh.flush_cut[b][i] : pcut;
-          int na = 0;
-          float nx = __builtin_huge_valf();
-          if (SCORE)
+          int na = 0, nc = 0;
+          float nx = __builtin_huge_valf(), n2 = __builtin_huge_valf();
+          if (SCORE) {
             for (int i = 0; i < kWaves; ++i) {
               na += sh.wabove[b][i];
               nx = fminf(nx, sh.wnext[b][i]);
             }
+            for (int i = 0; i < kWaves; ++i) {
+              nc += sh.wnext[b][i] == nx ? sh.wcount[b][i] : 0;
+              n2 = fminf(n2, sh.wnext[b][i] == nx ? sh.wnext2[b][i] : sh.wnext[b][i]);
+            }
+            // FP32 scoring: key slot 31 (beyond the K = 20 the merge uses)
+            // carries the next larger value and the count at the minimum.
+            if (DT == 0) rec->keys[kKeep - 1] = ((uint64_t)__float_as_uint(n2) << 32) | (uint32_t)nc;
+          }
           rec->m = M;
           rec->s = S;
           rec->above = na;
@@ -1521,6 +1578,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         cut = 0ull;
         above = 0;
         next_above = __builtin_huge_valf();
+        next_count = 0;
+        next2 = __builtin_huge_valf();
         part_u0 = nxt.u;
         natural = p.K > 0 && (prefix[nxt.s] & kSelBit) == 0;
       }

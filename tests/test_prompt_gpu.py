@@ -261,3 +261,27 @@ def test_prompt_repeatable_and_split_launches(oracle_handle):
     plan.run(logits, targets, out, ws, phase="merge")
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), a)
+
+
+def test_prompt_rank_fp32_value_tie_counts(oracle_handle):
+    """FP32 rows where the logits just above the target tie with it after the
+    subtraction: one value held by several lanes (taken off by its count, no
+    recount), and two distinct tying values (recounted)."""
+    V = 3 * 16384 + 5
+    rng = np.random.default_rng(12)
+    rows = rng.uniform(-30.0, -20.0, size=(3, V)).astype(np.float32)
+    up = np.nextafter(np.float32(1.0), np.float32(2.0))
+    for i in range(3):
+        rows[i, 5] = 200.0            # L = 200: 1.0 and its neighbours report -199
+        rows[i, 1000] = 1.0           # the target
+        rows[i, 30000] = 1.5          # reports more than the target
+    rows[0, [20000, 40000]] = up      # one tying value on two lanes, in one part or two
+    rows[1, [1001, 1002, 1003]] = up  # three lanes beside the target
+    rows[2, 20000] = up               # two distinct tying values
+    rows[2, 40000] = np.nextafter(up, np.float32(2.0))
+    w = _chunk_from_rows(rows, [1000, 1000, 1000], synth.FP32)
+    announce("prompt fp32 value-tie counts")
+    got, lse = run_prompt(w)
+    ref, ref_lse = oracle_prompt(oracle_handle, w)
+    assert ref[:, 2].tolist() == [3, 3, 3]
+    compare_prompt(w, got, lse, ref, ref_lse, where="fp32 value ties")
