@@ -55,6 +55,10 @@ class Oracle:
         self.lib.oracle_row.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
                                         c.c_int32, c.c_void_p, c.c_int32,
                                         c.c_void_p, c.c_void_p]
+        self.lib.oracle_row_at_lse.restype = c.c_int
+        self.lib.oracle_row_at_lse.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
+                                               c.c_int32, c.c_void_p, c.c_int32, c.c_float,
+                                               c.c_void_p]
         self.lib.oracle_frame.restype = c.c_int64
         self.lib.oracle_frame.argtypes = [c.c_void_p, c.c_int, c.c_int32, c.c_int32,
                                           c.c_int32, c.c_int32, c.c_void_p,
@@ -109,6 +113,25 @@ class Oracle:
         if rc < 0:
             raise ValueError("oracle_row rejected its arguments")
         return words[:rc].copy(), float(L.value)
+
+    def row_at(self, row: np.ndarray, token: int, K: int, L: float, sel=None,
+               V: int | None = None) -> np.ndarray:
+        """The listing of one emitted position for a given FP32 normalization
+        L (words[2 + 2W] as int32): what the row reports if its L is L."""
+        row = np.ascontiguousarray(row)
+        V = row.shape[-1] if V is None else V
+        words = np.zeros(ROW_WORDS, dtype=np.int32)
+        if sel is None or len(sel) == 0:
+            sel_arr, n = None, 0
+        else:
+            sel_arr = np.ascontiguousarray(sel, dtype=np.int32)
+            n = len(sel_arr)
+        rc = self.lib.oracle_row_at_lse(row.ctypes.data, self._dtype_of(row), V, int(token), n,
+                                        None if sel_arr is None else sel_arr.ctypes.data, K,
+                                        float(np.float32(L)), words.ctypes.data)
+        if rc < 0:
+            raise ValueError("oracle_row_at_lse rejected its arguments")
+        return words[:rc].copy()
 
     def frame(self, logits: np.ndarray, capacity: int, T: int, V: int, V_pad: int,
               requested, id_counts, ids, emitted, tokens, K: int, out: np.ndarray):

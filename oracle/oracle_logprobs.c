@@ -142,22 +142,21 @@ static void oracle_pair(const void* row, int dtype, int32_t V, int32_t id,
 }
 
 /*
- * One emitted position.  Writes words [0, 2 + 2W) of `words`, where W = n
- * (selected mode, n > 0) or K (natural mode), and returns that word count,
- * or -1 when the arguments are unusable.  `L_out` (may be NULL) gets the
- * row's normalization.
+ * The listing of one emitted position for a given normalization L: the
+ * chosen pair, then the selected pairs or the K natural alternatives, all
+ * reported as fl32(x - L) (GLP definition and tiled-reduction paragraphs).
+ * It is the second half of oracle_row, callable with any L so that a test can
+ * ask which listing a slightly different FP32 L would give.  Same return
+ * values as oracle_row.
  */
-int oracle_row(const void* row, int dtype, int32_t V, int32_t token,
-               int32_t n_sel, const int32_t* sel, int32_t K, int32_t* words,
-               float* L_out) {
+int oracle_row_at_lse(const void* row, int dtype, int32_t V, int32_t token,
+                      int32_t n_sel, const int32_t* sel, int32_t K, float L,
+                      int32_t* words) {
   if (!row || !words || V < 1 || K < 0 || K > ORACLE_MAX_K) return -1;
   if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16) return -1;
   if (n_sel < 0) n_sel = 0;
   if (n_sel > ORACLE_MAX_IDS) n_sel = ORACLE_MAX_IDS;
   if (n_sel > 0 && !sel) return -1;
-
-  float L = oracle_row_lse(row, dtype, V);
-  if (L_out) *L_out = L;
 
   oracle_pair(row, dtype, V, token, L, words);
   if (n_sel > 0) {
@@ -186,6 +185,22 @@ int oracle_row(const void* row, int dtype, int32_t V, int32_t token,
   }
   free(all);
   return 2 + 2 * K;
+}
+
+/*
+ * One emitted position.  Writes words [0, 2 + 2W) of `words`, where W = n
+ * (selected mode, n > 0) or K (natural mode), and returns that word count,
+ * or -1 when the arguments are unusable.  `L_out` (may be NULL) gets the
+ * row's normalization.
+ */
+int oracle_row(const void* row, int dtype, int32_t V, int32_t token,
+               int32_t n_sel, const int32_t* sel, int32_t K, int32_t* words,
+               float* L_out) {
+  if (!row || !words || V < 1 || K < 0 || K > ORACLE_MAX_K) return -1;
+  if (dtype != ORACLE_DTYPE_FP32 && dtype != ORACLE_DTYPE_BF16) return -1;
+  float L = oracle_row_lse(row, dtype, V);
+  if (L_out) *L_out = L;
+  return oracle_row_at_lse(row, dtype, V, token, n_sel, sel, K, L, words);
 }
 
 /*

@@ -70,6 +70,29 @@ FIXTURES = [
          row=[1.875 if i in (0, 2, 3) else 2.0 if i in (5, 17, 40) else (i % 8) / 8.0 - 1.0
               for i in range(48)],
          token=17, K=6, sel=[]),
+    dict(name="last_bit_of_L_a_v64_fp32",
+         cite="Generation-logprobs design page, tiled-reduction paragraph (keys rank the "
+              "reported FP32 values, one subtraction of the row's normalization)",
+         note="x0 = 1 - 2^-18 - 2^-24, x1 = 1 - 2^-18, x2 = 100, others -inf.  L = 100 "
+              "exactly.  x1 - L = -(99 + 2^-18) is halfway between -99 and -(99 + 2^-17) "
+              "and rounds to the even -99; x0 - L lies past the halfway point and rounds "
+              "to -(99 + 2^-17).  Order 2, 1, 0: the larger logit first.",
+         dtype="fp32",
+         row=[float(np.float32(1 - 2.0**-18 - 2.0**-24)), float(np.float32(1 - 2.0**-18)),
+              100.0] + [-np.inf] * 61,
+         token=0, K=4, sel=[]),
+    dict(name="last_bit_of_L_b_v64_fp32",
+         cite="Generation-logprobs design page, tiled-reduction paragraph (keys rank the "
+              "reported FP32 values, one subtraction of the row's normalization)",
+         note="The previous row with x2 = 100 + 2^-17, the next FP32 value: L = 100 + "
+              "2^-17 exactly, one unit in the last place above the previous L.  Now x1 - L "
+              "= -(99 + 3 * 2^-18) is halfway between -(99 + 2^-17) and -(99 + 2^-16) and "
+              "rounds to the even -(99 + 2^-16), and x0 - L rounds there too: the two tie "
+              "and the smaller ID leads.  Order 2, 0, 1.",
+         dtype="fp32",
+         row=[float(np.float32(1 - 2.0**-18 - 2.0**-24)), float(np.float32(1 - 2.0**-18)),
+              float(np.float32(100 + 2.0**-17))] + [-np.inf] * 61,
+         token=0, K=4, sel=[]),
 ]
 
 

@@ -65,3 +65,23 @@ def test_hand_claims():
     assert fx["words"][9] == fx["words"][11]
     fx = load("grid_ties_v48_bf16")
     assert fx["words"][2::2] == [5, 17, 40, 0, 2, 3]
+    a, b = load("last_bit_of_L_a_v64_fp32"), load("last_bit_of_L_b_v64_fp32")
+    assert a["L_bits"] == 0x42C80000 and b["L_bits"] == 0x42C80001  # 100 and the next float
+    assert a["words"][2::2][:3] == [2, 1, 0] and b["words"][2::2][:3] == [2, 0, 1]
+    # -99 is 0xC2C60000; each step of 2^-17 near 99 is one unit in the last place
+    assert [u32(x) for x in a["words"][3:9:2]] == [0, 0xC2C60000, 0xC2C60001]
+    assert [u32(x) for x in b["words"][3:9:2]] == [0, 0xC2C60002, 0xC2C60002]
+
+
+def test_listing_depends_on_the_last_bit_of_L(oracle_handle):
+    """The two rows differ only in the dominant logit, so the listing of row
+    a at row b's L is row b's listing of lanes 0 and 1: which of two logits
+    one ulp apart ranks first depends on the last bit of L.  A GPU whose L is
+    off by one unit would list them the other way."""
+    a, b = load("last_bit_of_L_a_v64_fp32"), load("last_bit_of_L_b_v64_fp32")
+    L_b = np.array([b["L_bits"]], np.uint32).view(np.float32)[0]
+    at_b = oracle_handle.row_at(fixture_row(a), token=0, K=4, L=L_b)
+    assert at_b[2::2].tolist()[:3] == [2, 0, 1]
+    assert [u32(int(x)) for x in at_b[5:9:2]] == [0xC2C60002, 0xC2C60002]
+    L_a = np.array([a["L_bits"]], np.uint32).view(np.float32)[0]
+    assert oracle_handle.row_at(fixture_row(a), token=0, K=4, L=L_a).tolist() == a["words"]
