@@ -30,7 +30,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libflare_logprobs.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 MAX_K = 20
 MAX_IDS = 128
 ROW_WORDS = 258
@@ -58,7 +58,7 @@ class PlanStruct(ctypes.Structure):
                 ("ranges", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
                 ("lse_offset", ctypes.c_uint64), ("slots_offset", ctypes.c_uint64),
-                ("reserved_offset", ctypes.c_uint64), ("packed_rows", ctypes.c_int32),
+                ("guard_offset", ctypes.c_uint64), ("packed_rows", ctypes.c_int32),
                 ("reserved", ctypes.c_uint32 * 5)]
 
 
@@ -302,6 +302,12 @@ class Plan:
         off = int(self.raw.lse_offset)
         return workspace[off:off + 4 * n].view(torch.float32)
 
+    def guard(self, workspace: torch.Tensor) -> torch.Tensor:
+        """Diagnostic view: per reduced row, the parts the merge's guard streamed again."""
+        n = self.capacity * self.T
+        off = int(self.raw.guard_offset)
+        return workspace[off:off + 4 * n].view(torch.int32)
+
     def new_out(self, fill: int = 0) -> torch.Tensor:
         return torch.full((self.capacity, self.T, ROW_WORDS), fill, dtype=torch.int32,
                           device=self.device)
@@ -469,6 +475,11 @@ class PromptPlan:
         """Diagnostic view: the normalization L of every scored row (valid rows only)."""
         off = int(self.raw.lse_offset)
         return workspace[off:off + 4 * self.rows].view(torch.float32)
+
+    def guard(self, workspace: torch.Tensor) -> torch.Tensor:
+        """Diagnostic view: per valid row, the parts whose lanes were counted again."""
+        off = int(self.raw.guard_offset)
+        return workspace[off:off + 4 * self.rows].view(torch.int32)
 
     def new_out(self, fill: int = 0) -> torch.Tensor:
         return torch.full((self.rows, PROMPT_ROW_WORDS), fill, dtype=torch.int32,

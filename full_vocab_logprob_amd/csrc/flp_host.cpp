@@ -110,7 +110,8 @@ static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, i
   off = align_up(off + (uint64_t)rows * sizeof(float), kAlign);
   plan->slots_offset = off;
   off = align_up(off + ((uint64_t)capacity + 1) * sizeof(int32_t), kAlign);
-  plan->reserved_offset = 0;
+  plan->guard_offset = off;
+  off = align_up(off + (uint64_t)rows * sizeof(int32_t), kAlign);
   plan->workspace_bytes = off;
   return FLARE_OK;
 }
@@ -191,6 +192,7 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
   p.out = out;
   p.records = (flp::PartRecord*)(ws + plan->record_offset);
   p.lse = (float*)(ws + plan->lse_offset);
+  p.guard = (int32_t*)(ws + plan->guard_offset);
   p.slot_rows = (int32_t*)(ws + plan->slots_offset);
   p.V_pad = V_pad;
   p.capacity = plan->capacity;
@@ -243,6 +245,7 @@ static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, 
   p.out = out;
   p.records = (flp::PartRecord*)(ws + plan->record_offset);
   p.lse = (float*)(ws + plan->lse_offset);
+  p.guard = (int32_t*)(ws + plan->guard_offset);
   p.slot_rows = (int32_t*)(ws + plan->slots_offset);
   p.V_pad = V_pad;
   p.capacity = plan->capacity;

@@ -51,6 +51,7 @@ struct Params {
   int32_t* out;
   PartRecord* records;
   float* lse;
+  int32_t* guard;       // [rows]: parts the merge read again (diagnostic)
   int32_t* slot_rows;   // [capacity + 1]: active rows before each slot, then their total
   const int64_t* crecords;     // completion records [capacity, 16 + T] (or null): emitted
                                // count at field emitted_field, tokens at fields 16 + t

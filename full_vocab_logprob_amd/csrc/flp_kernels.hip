@@ -558,14 +558,31 @@ __device__ __forceinline__ bool is_range_start(int x, int n, int grid) {
 
 // Every lane [lo, hi) of a row whose final key reaches thr, merged into the
 // sorted best 32 in `top`; thr rises to the K-th kept key as it fills.  One
-// 16-byte chunk per lane per step, eight steps' chunks loaded at once.
+// 16-byte chunk per lane per step, eight steps' chunks loaded at once.  Keys
+// that reach thr are appended to the wave's LDS buffer `buf` (`cap` keys, a
+// multiple of 64) and sorted into `top` only when it is full and at the end,
+// so a step whose lanes hold candidates costs a ballot and one LDS store.
 template <int DT, bool VEC>
 __device__ __forceinline__ void rescan_lanes(uint64_t& top, uint64_t& thr, const char* rowp, int lo,
-                                             int hi, float L, int Keff, int lane) {
+                                             int hi, float L, int Keff, int lane, uint64_t* buf,
+                                             int cap) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   constexpr int kStep = 64 * kPer;
   constexpr int kBatch = 8;  // chunks per lane in flight at once
+  int n = 0;                 // buffered keys (wave-uniform)
+  auto flush = [&]() {
+    wave_sync();
+    for (int base = 0; base < n; base += 64) {
+      const uint64_t v = base + lane < n ? buf[base + lane] : 0ull;
+      top = merge_top32(top, sort64_desc(v, lane), lane);
+    }
+    n = 0;
+    // The list only improves: its K-th key is a floor for the rest.
+    const uint64_t kth = readlane64(top, Keff - 1);
+    thr = kth > thr ? kth : thr;
+    wave_sync();
+  };
   for (int b = lo; b < hi; b += kBatch * kStep) {
     u32x4 cur[kBatch];
 #pragma unroll
@@ -579,22 +596,24 @@ __device__ __forceinline__ void rescan_lanes(uint64_t& top, uint64_t& thr, const
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int i = b + c * kStep + lane * kPer + j;
-        uint64_t f = 0ull;
-        if (i < hi) {
-          f = make_key(reported(E::get(cur[0], j), L), (uint32_t)i);
-          if (f < thr) f = 0ull;
-        }
-        if (__ballot(f != 0ull) != 0ull) {
-          top = merge_top32(top, sort64_desc(f, lane), lane);
-          // The list only improves: its K-th key is a floor for the rest.
-          const uint64_t kth = readlane64(top, Keff - 1);
-          thr = kth > thr ? kth : thr;
+        uint64_t f = i < hi ? make_key(reported(E::get(cur[0], j), L), (uint32_t)i) : 0ull;
+        if (f < thr) f = 0ull;
+        uint64_t m = __ballot(f != 0ull);
+        if (m != 0ull) {
+          if (n + __popcll(m) > cap) {
+            flush();
+            if (f < thr) f = 0ull;
+            m = __ballot(f != 0ull);
+          }
+          if (f != 0ull) buf[n + lanes_below(m)] = f;
+          n += __popcll(m);
         }
       }
 #pragma unroll
       for (int c2 = 0; c2 + 1 < kBatch; ++c2) cur[c2] = cur[c2 + 1];
     }
   }
+  flush();
 }
 
 // Lanes [lo, hi) of a row whose reported value exceeds rt, summed over the
@@ -759,6 +778,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       tie = false;
     }
     uint64_t ties = __ballot(tie);
+    if (lane == 0) p.guard[row] = __popcll(ties);
     while (ties != 0ull) {
       const int part = __builtin_ctzll(ties);
       ties &= ties - 1ull;
@@ -780,7 +800,10 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       *(int2*)(out + 2 + 2 * j) = make_int2(sel_id[h], (int32_t)bits);
     }
   }
-  if (!natural) return;
+  if (!natural) {
+    if (!SCORE && lane == 0) p.guard[row] = 0;
+    return;
+  }
 
   // ---- kept candidates re-keyed by F, two parts (64 keys) per step
   const int K = p.K;
@@ -805,6 +828,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
     bad = !ok;
   }
   const uint64_t unsafe = __ballot(bad);
+  if (!SCORE && lane == 0) p.guard[row] = __popcll(unsafe);
   if (unsafe != 0ull) {
     // Rebuild from the safe parts' candidates plus every lane of each unsafe
     // part whose final key reaches FK.
@@ -824,7 +848,8 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       const int lo = part_u0[part] * kUnitElems;
       int hi = part_u0[part + 1] * kUnitElems;
       hi = hi < V ? hi : V;
-      rescan_lanes<DT, VEC>(top, thr, rowp, lo, hi, L, Keff, lane);
+      rescan_lanes<DT, VEC>(top, thr, rowp, lo, hi, L, Keff, lane, &pair_keys[wv][0][0],
+                            kLdsPairs * 64);
     }
   }
   if (lane < K) {
@@ -1265,6 +1290,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   const int x0 = (int)((int64_t)blockIdx.x * N / ranges);
   const int x1 = (int)(((int64_t)blockIdx.x + 1) * N / ranges);
   if (x0 >= x1) return;
+  const bool short_ranges = N < 2 * (int64_t)p.workers;
 
   UnitPos cur = locate<DT>(p, prefix, x0);
   int part_u0 = cur.u;
@@ -1365,10 +1391,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     // part's first unit finds its threshold in the pass itself.
     bool stage = natural && ad.by_key && !ht.every_lane;
     // Keys each wave admits in a part's first unit: ceil(K / waves holding
-    // vocabulary), so that the part keeps at least K.
+    // vocabulary), so that the part keeps at least K; K per wave when the
+    // ranges are one or two units long, since then no later unit of the part
+    // can refine the wave's threshold and a wave holding several of the
+    // row's best lanes would leave a cut above the row's K-th value.
     const int ubase = cur.u * kUnitElems;
     const int nw = V - ubase >= kUnitElems ? kWaves : (V - ubase + kWaveElems - 1) / kWaveElems;
-    const int kfirst = nw == kWaves ? kq : (nw == 3 ? (K + 2) / 3 : (nw == 2 ? (K + 1) >> 1 : K));
+    const int kfirst = short_ranges ? K
+                       : (nw == kWaves ? kq : (nw == 3 ? (K + 2) / 3 : (nw == 2 ? (K + 1) >> 1 : K)));
 
     st.n = 0;
     float cm[kChunks];
@@ -1493,7 +1523,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         }
       }
       if (natural && lane < kKeep) sh.flush_keys[b][w][lane] = best.top;
-      if (lane == 0) sh.flush_cut[b][w] = natural ? cut : 0ull;
+      // Every key this wave kept is at or above its first-unit threshold, so
+      // once it holds K of them the lanes below the threshold rank below its
+      // K-th key, which the part's K-th kept key bounds: no cut of its own.
+      if (lane == 0) sh.flush_cut[b][w] = natural && best.n < K ? cut : 0ull;
       // The last wave to arrive merges the four shares into the record.
       int old = 0;
       if (lane == 0)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FLARE_LOGPROBS_ABI_VERSION 5u
+#define FLARE_LOGPROBS_ABI_VERSION 6u
 #define FLARE_LOGPROBS_MAX_K 20
 #define FLARE_LOGPROBS_MAX_IDS 128
 #define FLARE_LOGPROBS_ROW_WORDS 258 /* 2 + 2 * 128 */
@@ -100,7 +100,8 @@ typedef struct flare_logprobs_plan {
   uint64_t record_offset;   /* per-(row, unit) part records */
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
   uint64_t slots_offset;    /* int32[capacity + 1]: active rows before each slot, then all */
-  uint64_t reserved_offset; /* 0 */
+  uint64_t guard_offset;    /* int32[capacity * T]: parts of each reduced row that the
+                               merge read again (diagnostic, see flare_logprobs_run) */
   int32_t packed_rows;      /* P of flare_logprobs_plan_packed; 0 for the rectangular layout */
   uint32_t reserved[5];
 } flare_logprobs_plan_t;
@@ -135,6 +136,10 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
  *                   same call)
  * Two kernels run in order on the stream: the reduction, then the per-row
  * merge.  Host-checkable errors return before anything is launched.
+ * Diagnostics left in the workspace for each active position (other entries
+ * hold stale values): its L at lse_offset, and at guard_offset the number of
+ * its parts that the merge's exactness guard streamed again because their
+ * kept candidates could not settle the top K.
  */
 int flare_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,
                        int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
@@ -264,7 +269,10 @@ int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits,
  * Ownership, errors, streams and graph capture are as for flare_logprobs_run;
  * a plan of one mode is rejected by the other mode's entry points.  _reduce
  * and _merge are the two launches of _run, with the same contract as
- * flare_logprobs_reduce and flare_logprobs_merge.
+ * flare_logprobs_reduce and flare_logprobs_merge.  The diagnostics are
+ * those of flare_logprobs_run for valid rows; a row's guard_offset entry
+ * counts the parts whose lanes were counted again because the subtraction
+ * tied a larger logit with the target.
  */
 int flare_prompt_logprobs_plan(flare_logprobs_plan_t* plan, int32_t rows, int32_t V,
                                int32_t V_pad, int32_t dtype, int32_t device);

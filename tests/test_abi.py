@@ -72,8 +72,8 @@ def test_plan_host_only_geometry(flp):
     assert p.ranges == 1024 and p.mode == flp.MODE_GENERATION
     rows = 128 * 8
     assert p.lse_offset >= rows * 16 * 280 and p.slots_offset >= p.lse_offset + 4 * rows
-    assert p.slots_offset % 16 == 0 and p.reserved_offset == 0
-    assert p.workspace_bytes >= p.slots_offset + 4 * (128 + 1)
+    assert p.slots_offset % 16 == 0 and p.guard_offset >= p.slots_offset + 4 * (128 + 1)
+    assert p.guard_offset % 16 == 0 and p.workspace_bytes >= p.guard_offset + 4 * rows
     rc, p = host_plan(flp, capacity=1024, T=4, V=262144, V_pad=262144, dtype=0)
     assert rc == 0 and p.units == 32 and p.unit_elems == 8192
     rc, p = host_plan(flp, V=37, V_pad=41)
