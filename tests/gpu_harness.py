@@ -29,8 +29,10 @@ def make_plan(spec: synth.Spec, K: int | None = None):
                     K=spec.K if K is None else K, device=torch.cuda.current_device())
 
 
-def run_gpu(w: synth.Workload, dev_inputs=None, plan=None, ws=None, logits=None):
-    """Run the HIP path once; returns (out [cap, T, 258] int32, lse [cap*T])."""
+def run_gpu(w: synth.Workload, dev_inputs=None, plan=None, ws=None, logits=None,
+            guard=False):
+    """Run the HIP path once; returns (out [cap, T, 258] int32, lse [cap*T]),
+    plus the per-row guard rescan counts [cap*T] when `guard`."""
     d = dev_inputs if dev_inputs is not None else to_device(w)
     plan = plan or make_plan(w.spec)
     ws = ws if ws is not None else plan.workspace()
@@ -38,7 +40,60 @@ def run_gpu(w: synth.Workload, dev_inputs=None, plan=None, ws=None, logits=None)
     plan.run(d["logits"] if logits is None else logits, d["tokens"], d["emitted"],
              d["requested"], d["id_counts"], d["ids"], out, ws)
     torch.cuda.synchronize()
-    return out.cpu().numpy(), plan.lse(ws).cpu().numpy().copy()
+    res = (out.cpu().numpy(), plan.lse(ws).cpu().numpy().copy())
+    if guard:
+        res = res + (plan.guard(ws).cpu().numpy().copy(),)
+    return res
+
+
+def oracle_rows(o, w: synth.Workload, rows, threads: int = 16):
+    """The oracle's (words, L) for each logit row in `rows`, one row per task
+    on a thread pool (the oracle call releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    s = w.spec
+
+    def one(r):
+        sl = int(r) // s.T
+        n = int(np.clip(w.id_counts[sl], 0, 128))
+        sel = w.ids[sl * 128: sl * 128 + n] if n > 0 else None
+        return o.row(w.logits[int(r)], token=int(w.tokens[int(r)]), K=s.K, sel=sel, V=s.V)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return dict(zip((int(r) for r in rows), ex.map(one, rows)))
+
+
+def compare_rows_with_oracle(o, w: synth.Workload, got: np.ndarray, lse: np.ndarray, rows,
+                             where: str):
+    """Every given active row against the oracle, element by element: IDs and
+    layout bit-exact, values and L within TOL.  Returns (max |d logprob|,
+    max |d L|, rows whose FP32 L differs from the oracle's in any bit).
+    When IDs differ, the message says whether the oracle's listing at the
+    kernel's own L (differing by a few units in the last place) would have
+    matched, which names the cause; the test fails either way."""
+    s = w.spec
+    ref = oracle_rows(o, w, rows)
+    worst = worst_L = 0.0
+    L_bits_differ = 0
+    for r in rows:
+        r = int(r)
+        sl, t = divmod(r, s.T)
+        words, L = ref[r]
+        g = got[sl, t, :len(words)]
+        Lg = np.float32(lse[r])
+        if np.float32(L).view(np.int32) != Lg.view(np.int32):
+            L_bits_differ += 1
+        if not np.array_equal(g[0::2], words[0::2]):
+            n = int(np.clip(w.id_counts[sl], 0, 128))
+            sel = w.ids[sl * 128: sl * 128 + n] if n > 0 else None
+            at_own = o.row_at(w.logits[r], int(w.tokens[r]), s.K, Lg, sel=sel, V=s.V)
+            raise AssertionError(
+                f"{where} row {r}: IDs differ (GPU L {float(Lg)!r}, oracle L {L!r}); the "
+                f"oracle listing at the GPU's L {'matches' if np.array_equal(at_own, g) else 'does not match'}")
+        compare_words(g, words, f"{where} row {r}")
+        assert abs(float(Lg) - L) <= TOL, (where, r, float(Lg), L)
+        worst = max(worst, max_value_delta(g, words))
+        worst_L = max(worst_L, abs(float(Lg) - L))
+    return worst, worst_L, L_bits_differ
 
 
 def oracle_frame(o, w: synth.Workload):

@@ -50,10 +50,12 @@ def full_compare(o, spec, **kw):
 # ------------------------------------------------------------ named workloads
 def test_c1_decode_full(oracle_handle):
     full_compare(oracle_handle, synth.CONFIGS["C1"])
+    full_size_all_rows(oracle_handle, synth.CONFIGS["C1"])
 
 
 def test_c2_padded_half_requesting_full(oracle_handle):
     full_compare(oracle_handle, synth.CONFIGS["C2"])
+    full_size_all_rows(oracle_handle, synth.CONFIGS["C2"])
 
 
 @pytest.mark.parametrize("cap,T", [(8, 8), (3, 5)])
@@ -93,37 +95,47 @@ def test_many_ranges_per_row(oracle_handle, dtype):
     full_compare(oracle_handle, spec)
 
 
-def sampled_full_size(o, spec, nsample=24):
-    announce(f"full size {spec.name} cap={spec.capacity} T={spec.T} V={spec.V} (sampled rows)")
+def full_size_all_rows(o, spec):
+    """The configuration at its full size, in the launch configuration the
+    bench times, every active row compared with the oracle."""
+    announce(f"full size {spec.name} cap={spec.capacity} T={spec.T} V={spec.V} K={spec.K} "
+             f"(every active row)")
     w = synth.make(spec)
-    got, lse = H.run_gpu(w)
+    got, lse, guard = H.run_gpu(w, guard=True)
     act = np.nonzero(w.active_mask().reshape(-1))[0]
-    rng = np.random.default_rng(spec.seed + 100)
-    pick = sorted(set(rng.choice(act, size=min(nsample, act.size), replace=False).tolist()
-                      + [int(act[0]), int(act[-1])]))
-    worst = 0.0
-    for r in pick:
-        sl, t = divmod(r, spec.T)
-        n = int(np.clip(w.id_counts[sl], 0, 128))
-        sel = w.ids[sl * 128: sl * 128 + n] if n > 0 else None
-        words, L = o.row(w.logits[r], token=int(w.tokens[r]), K=spec.K, sel=sel, V=spec.V)
-        H.compare_words(got[sl, t, :len(words)], words, f"{spec.name} row {r}")
-        assert abs(float(lse[r]) - L) <= H.TOL, (r, lse[r], L)
-        worst = max(worst, H.max_value_delta(got[sl, t, :len(words)], words))
+    worst, worst_L, L_differ = H.compare_rows_with_oracle(o, w, got, lse, act, spec.name)
     H.check_properties(w, got, lse)
-    announce(f"{spec.name}: {len(pick)} sampled rows exact, max |d logprob| = {worst:.3g}")
+    announce(f"{spec.name}: {act.size} rows exact; max |d logprob| = {worst:.3g}, "
+             f"max |d L| = {worst_L:.3g}, L bits differ on {L_differ} rows, guard rescans "
+             f"{int(guard[act].sum())} parts")
 
 
-def test_c3_full_size_sampled(oracle_handle):
-    sampled_full_size(oracle_handle, synth.CONFIGS["C3"])
+def test_c3_full_size_all_rows(oracle_handle):
+    full_size_all_rows(oracle_handle, synth.CONFIGS["C3"])
 
 
-def test_c4_full_size_sampled(oracle_handle):
-    sampled_full_size(oracle_handle, synth.CONFIGS["C4"])
+def test_c4_full_size_all_rows(oracle_handle):
+    full_size_all_rows(oracle_handle, synth.CONFIGS["C4"])
 
 
-def test_c5_full_size_sampled(oracle_handle):
-    sampled_full_size(oracle_handle, synth.CONFIGS["C5"], nsample=12)
+def test_c5_full_size_all_rows(oracle_handle):
+    full_size_all_rows(oracle_handle, synth.CONFIGS["C5"])
+
+
+def test_listing_at_the_last_bit_of_L(oracle_handle):
+    """Two rows whose listing depends on the last bit of L (the golden
+    fixtures last_bit_of_L_a/b): L is exact on both sides here (one lane
+    dominates by e^99), so the GPU must give both listings bit for bit."""
+    rows = []
+    for name in ("last_bit_of_L_a_v64_fp32", "last_bit_of_L_b_v64_fp32"):
+        fx = json.load(open(os.path.join(HERE, "golden", name + ".json")))
+        rows.append(np.asarray(fx["row_bits"], np.uint32).view(np.float32))
+    announce("last bit of L rows fp32")
+    w = _frame_from_rows(np.stack(rows), synth.FP32, K=4)
+    got, lse = H.run_gpu(w)
+    assert lse[0] == np.float32(100.0) and lse[1] == np.float32(100 + 2.0**-17)
+    H.compare_words(got, H.oracle_frame(oracle_handle, w), "last bit of L")
+    assert got[0, 0, 2:8:2].tolist() == [2, 1, 0] and got[1, 0, 2:8:2].tolist() == [2, 0, 1]
 
 
 # ----------------------------------------------------------------- edge cases
@@ -216,10 +228,11 @@ def test_guard_trips_on_subtraction_ties(oracle_handle, dtype, background):
         row[50] = 10.0
     announce(f"guard trip row dtype={dtype} background={background}")
     w = _frame_from_rows(row[None, :], dtype)
-    got, lse = H.run_gpu(w)
+    got, lse, guard = H.run_gpu(w, guard=True)
     ref = H.oracle_frame(oracle_handle, w)
     assert ref[0, 0, 2:8:2].tolist() == [50, 0, 1]
     H.compare_words(got, ref, "guard")
+    assert guard[0] >= 1  # the diagnostic counts the rescanned part
 
 
 def test_golden_fixtures_on_gpu(oracle_handle):
