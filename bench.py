@@ -9,12 +9,13 @@ never read), K=20 natural alternatives.  Inputs are seeded synthetic logits
 copies of the logits keep the 256 MB Infinity Cache from serving repeats.
 
 Prints one JSON line: rows/s over the whole timed region (each call made
-through a prepared binding, Plan.bind, so that one call is one C call), the roofline of the
-reduction launch (algorithmic bytes / its mean duration, from HIP events around
-that launch on the launch stream), and the CPU oracle timed on a bounded sample
-of the same rows.  The HBM traffic of the reduction launch comes from the
-rocprofv3 counter summary under profiles/, and only while the kernel source is
-the one those counters were taken on.
+through a prepared binding, Plan.bind, so that one call is one C call), the
+roofline of the reduction launch (algorithmic bytes / its mean duration, from a
+second region of the same number of reduction launches back to back, HIP events
+only at its ends, on the launch stream), and the CPU oracle timed on a bounded
+sample of the same rows.  The HBM traffic of the reduction launch and its
+rocprofv3 trace average come from the summary under profiles/, and only while
+the kernel source is the one that summary was taken on.
 
 `--prompt P1` (or P2) measures prompt scoring instead: one step scores one
 prefill chunk (P1: 128 rows x V=248,320 bf16, each row's target logprob, rank
@@ -48,10 +49,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(config: str):
-    """HBM bytes per reduction launch from the committed counter summary, or
-    None when the summary is missing, covers another workload, or was taken
-    on a different kernel source."""
+def profile_field(config: str, name: str):
+    """A number from the committed rocprofv3 summary of this workload (HBM
+    bytes per reduction launch, the trace's average launch duration), or None
+    when the summary is missing, covers another workload, or was taken on a
+    different kernel source."""
     if config not in TRAFFIC_SUMMARIES:
         return None
     path = os.path.join(ROOT, TRAFFIC_SUMMARIES[config])
@@ -64,9 +66,70 @@ def measured_traffic(config: str):
     if fields.get("workload") != config:
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields[name])
     except (KeyError, ValueError):
         return None
+
+
+def host_cpu() -> str:
+    """The host CPU model and its logical core count (lscpu's model name)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical cores"
+
+
+def timed_regions(step, K: int, warmup: int, stream, graph=None):
+    """The timed part of a bench, after `warmup` untimed whole calls:
+    region 1, K whole calls back to back (the throughput); region 2, the
+    same K calls' reduction launches alone, back to back (the reduction's
+    mean duration: the roofline); region 3, their merge launches alone;
+    then `graph()`, if given, for the graph-replay rate.  Every region is
+    bracketed by a synchronization and HIP events at its two ends only, on
+    the launch stream, so no event sits between two launches."""
+    import torch
+
+    for i in range(warmup):
+        step(i)
+
+    def region(phase):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            step(warmup + i, phase)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K, time.perf_counter() - w0
+
+    ms_per_step, wall = region("all")
+    reduce_ms, _ = region("reduce")
+    merge_ms, _ = region("merge")
+    g = graph() if graph is not None else None
+    if reduce_ms > ms_per_step:
+        print(f"[bench] warning: reduction launches took {reduce_ms * 1e3:.1f} us each, more "
+              f"than a whole call ({ms_per_step * 1e3:.1f} us): clock drift between regions",
+              file=sys.stderr, flush=True)
+    return ms_per_step, wall, reduce_ms, merge_ms, g
+
+
+def roofline(config: str, kernel: str, algo_bytes: float, reduce_ms: float, packed=False):
+    achieved = algo_bytes / (reduce_ms / 1e3) / 1e9
+    trace_ns = None if packed else profile_field(config, "reduce_trace_average_ns")
+    return {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": None if packed else profile_field(config, "traffic_bytes_per_launch"),
+            "profile_trace_average_us": None if trace_ns is None else trace_ns / 1e3,
+            "profile_frac": None if trace_ns is None
+            else algo_bytes / (trace_ns / 1e9) / 1e9 / PEAK_HBM_GBPS}
 
 
 def parse():
@@ -146,8 +209,36 @@ def bench_prompt(args):
     def step(i, phase="all"):
         bound[(i % len(copies), phase)](sh)
 
-    # Correctness gate first (one call against the oracle), then the warm-up
-    # straight into the timed regions, so the GPU does not idle in between.
+    def graph():
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(gr, stream=side):
+                for c in range(len(copies)):
+                    plan.run(copies[c], targets, out, ws)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // len(copies))
+        for _ in range(2):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        per_call = g0.elapsed_time(g1) / (reps * len(copies))
+        del gr
+        return {"ms_per_call": per_call, "rows_per_s": w.rows / (per_call / 1e3),
+                "calls": reps * len(copies)}
+
+    # Warm-up straight into the timed regions; the oracle check of the
+    # output comes after them, so the GPU does not idle before timing.
+    K = args.steps
+    ms_per_step, wall, mean_reduce_ms, mean_merge_ms, graph_res = timed_regions(
+        step, K, args.warmup, stream, graph if args.graph else None)
     step(0)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
@@ -165,60 +256,6 @@ def bench_prompt(args):
             rv = np.concatenate([words[1:2], words[4::2]]).view(np.float32).astype(np.float64)
             assert np.all(np.abs(gv - rv) <= 2e-5), f"values differ on row {r}"
             checked += 1
-    for i in range(args.warmup):
-        step(i)
-
-    K = args.steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(K):
-        step(args.warmup + i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = t0.elapsed_time(t1) / K
-
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(args.warmup + i, "reduce")
-        ev[i][1].record(stream)
-        step(args.warmup + i, "merge")
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    reduce_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    merge_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    mean_reduce_ms = sum(reduce_ms) / K
-
-    graph = None
-    if args.graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(gr, stream=side):
-                for c in range(len(copies)):
-                    plan.run(copies[c], targets, out, ws)
-        torch.cuda.synchronize()
-        reps = max(1, K // len(copies))
-        for _ in range(2):
-            gr.replay()
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(reps):
-            gr.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        per_call = g0.elapsed_time(g1) / (reps * len(copies))
-        graph = {"ms_per_call": per_call, "rows_per_s": w.rows / (per_call / 1e3),
-                 "calls": reps * len(copies)}
-        del gr
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -232,11 +269,10 @@ def bench_prompt(args):
         dt = time.perf_counter() - c0
         cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
                "sample": f"first {n} rows of {spec.name} (of {w.rows}, {valid} valid), "
-                         f"single-threaded oracle, {dt:.1f} s"}
+                         f"single-threaded oracle, {dt:.1f} s", "cpu": host_cpu()}
     if args.copy_mib > 0:
         copy_kernel(dev, args.copy_mib)
 
-    achieved = algo_bytes / (mean_reduce_ms / 1e3) / 1e9
     res = {
         "metric": f"scored prompt rows/s and achieved HBM GB/s (% of peak) at V={spec.V}, "
                   f"{w.rows}-row chunk",
@@ -256,13 +292,10 @@ def bench_prompt(args):
                                f"{'bf16' if bf16 else 'fp32'}, prompt scoring",
                    "rows": w.rows, "valid_rows": valid, "V": spec.V, "copies": len(copies),
                    "oracle_rows_checked": checked},
-        "roofline": {"bound": "hbm", "kernel": "reduce_kernel (scoring)", "achieved": achieved,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic(spec.name)},
-        "reduce_ms": {"mean": mean_reduce_ms, "median": reduce_ms[K // 2],
-                      "p10": reduce_ms[K // 10], "p90": reduce_ms[(9 * K) // 10]},
-        "merge_ms": {"mean": sum(merge_ms) / K, "median": merge_ms[K // 2]},
-        "graph_replay": graph,
+        "roofline": roofline(spec.name, "reduce_kernel (scoring)", algo_bytes, mean_reduce_ms),
+        "reduce_ms": mean_reduce_ms,
+        "merge_ms": mean_merge_ms,
+        "graph_replay": graph_res,
         "algorithmic_bytes_per_launch": algo_bytes,
         "wall_s": wall,
         "cpu_baseline": cpu,
@@ -354,8 +387,41 @@ def main():
     def step(i, phase="all"):
         bound[(i % len(copies), phase)](sh)
 
-    # Correctness gate first (one call against the oracle), then the warm-up
-    # straight into the timed regions, so the GPU does not idle in between.
+    def graph():
+        # The same calls replayed from one HIP graph (one call per logits copy
+        # captured, replayed until about K calls have run).
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(gr, stream=side):
+                for c in range(len(copies)):
+                    plan.run(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
+                             row_offsets=offsets)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // len(copies))
+        for _ in range(2):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        per_call = g0.elapsed_time(g1) / (reps * len(copies))
+        del gr
+        return {"ms_per_call": per_call, "rows_per_s": active / (per_call / 1e3),
+                "calls": reps * len(copies)}
+
+    # Warm-up straight into the timed regions; the oracle check of the
+    # output comes after them, so the GPU does not idle before timing.
+    K = args.steps
+    ms_per_step, wall, mean_reduce_ms, mean_merge_ms, graph_res = timed_regions(
+        step, K, args.warmup, stream, graph if args.graph else None)
+    rows_per_s = active / (ms_per_step / 1e3)
+
     step(0)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
@@ -375,73 +441,6 @@ def main():
                        - words[1::2].view(np.float32).astype(np.float64))
             assert np.all((d <= 2e-5) | (g_[1::2] == words[1::2])), f"values differ on row {r}"
             checked += 1
-    for i in range(args.warmup):
-        step(i)
-
-    # Timed region 1: K whole calls back to back between synchronizations,
-    # events only at its ends: the throughput.
-    K = args.steps
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(K):
-        step(args.warmup + i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
-    ms_per_step = total_ms / K
-    rows_per_s = active * K / (total_ms / 1e3)
-
-    # Timed region 2: the same K calls made as their two launches, with an
-    # event pair around each launch on the launch stream: the reduction
-    # kernel's mean duration (the roofline) and the merge's.
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        ev[i][0].record(stream)
-        step(args.warmup + i, "reduce")
-        ev[i][1].record(stream)
-        step(args.warmup + i, "merge")
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    reduce_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    merge_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
-    mean_reduce_ms = sum(reduce_ms) / K
-    mean_merge_ms = sum(merge_ms) / K
-
-    # Timed region 3: the same calls replayed from one HIP graph (one call per
-    # logits copy captured, replayed until about K calls have run).
-    graph = None
-    if args.graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(gr, stream=side):
-                for c in range(len(copies)):
-                    plan.run(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
-                             row_offsets=offsets)
-        torch.cuda.synchronize()
-        reps = max(1, K // len(copies))
-        for _ in range(2):
-            gr.replay()
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(reps):
-            gr.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        per_call = g0.elapsed_time(g1) / (reps * len(copies))
-        graph = {"ms_per_call": per_call, "rows_per_s": active / (per_call / 1e3),
-                 "calls": reps * len(copies)}
-        del gr
-    achieved_gbps = algo_bytes / (mean_reduce_ms / 1e3) / 1e9
-    traffic = None if packed_rows else measured_traffic(spec.name)
 
     cpu = cpu_threads = None
     if args.cpu_seconds > 0:
@@ -458,7 +457,7 @@ def main():
         dt = time.perf_counter() - c0
         cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
                "sample": f"first {n} active rows of {spec.name} (of {active}), "
-                         f"single-threaded oracle, {dt:.1f} s"}
+                         f"single-threaded oracle, {dt:.1f} s", "cpu": host_cpu()}
         # The same per-row oracle over every active row, rows split across
         # host threads (ctypes releases the GIL during each row).
         from concurrent.futures import ThreadPoolExecutor
@@ -501,13 +500,11 @@ def main():
                                   if args.records else ""),
                    "active_rows": active, "capacity": spec.capacity, "T": spec.T, "V": spec.V,
                    "K": spec.K, "copies": len(copies), "oracle_rows_checked": checked},
-        "roofline": {"bound": "hbm", "kernel": "reduce_kernel", "achieved": achieved_gbps,
-                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved_gbps / PEAK_HBM_GBPS,
-                     "traffic": traffic},
-        "reduce_ms": {"mean": mean_reduce_ms, "median": reduce_ms[K // 2],
-                      "p10": reduce_ms[K // 10], "p90": reduce_ms[(9 * K) // 10]},
-        "merge_ms": {"mean": mean_merge_ms, "median": merge_ms[K // 2]},
-        "graph_replay": graph,
+        "roofline": roofline(spec.name if args.K is None and not args.records else "",
+                             "reduce_kernel", algo_bytes, mean_reduce_ms, packed=bool(packed_rows)),
+        "reduce_ms": mean_reduce_ms,
+        "merge_ms": mean_merge_ms,
+        "graph_replay": graph_res,
         "algorithmic_bytes_per_launch": algo_bytes,
         "wall_s": wall,
         "cpu_baseline": cpu,
