@@ -159,6 +159,9 @@ def parse():
     ap.add_argument("--packed", type=int, default=0,
                     help="1: the frame's committed rows packed into P physical rows "
                          "(shuffled slot order) and read through row offsets")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="N > 0: the vocabulary split into N shards on this GPU (N shard "
+                         "passes, then the cross-shard merge)")
     return ap.parse_args()
 
 
@@ -362,7 +365,7 @@ def main():
     id_counts, ids = g(w.id_counts), g(w.ids)
     plan = flp.Plan(spec.capacity, spec.T, spec.V, spec.V_pad,
                     dtype=torch.bfloat16 if bf16 else torch.float32, K=spec.K, device=0,
-                    packed_rows=packed_rows)
+                    packed_rows=packed_rows, shards=args.shards or None)
     ws = plan.workspace()
     out = plan.new_out(int(synth.POISON))
     stream = torch.cuda.current_stream()
@@ -370,9 +373,21 @@ def main():
     # Each call validated and marshalled once (Plan.bind): a timed step is one
     # C call per launch, so the host keeps ahead of the GPU.
     sh = stream.cuda_stream
-    bound = {(c, ph): plan.bind(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
-                                phase=ph, row_offsets=offsets)
-             for c in range(len(copies)) for ph in ("all", "reduce", "merge")}
+    if args.shards:
+        # "reduce" is every shard pass (what the ranks run side by side), "merge"
+        # the cross-shard merge.
+        def bind(c, ph):
+            if ph == "reduce":
+                return [plan.bind(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
+                                  phase=f"shard:{r}") for r in range(args.shards)]
+            return plan.bind(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
+                             phase=ph)
+        bound = {(c, ph): bind(c, ph) for c in range(len(copies))
+                 for ph in ("all", "reduce", "merge")}
+    else:
+        bound = {(c, ph): plan.bind(copies[c], tokens, emitted, requested, id_counts, ids, out,
+                                    ws, phase=ph, row_offsets=offsets)
+                 for c in range(len(copies)) for ph in ("all", "reduce", "merge")}
     if args.records:
         # Timed calls read the counts and tokens from completion records
         # (emitted count in field 3); the split launches keep the int32 inputs.
@@ -385,7 +400,9 @@ def main():
                                                   id_counts=id_counts, ids=ids)
 
     def step(i, phase="all"):
-        bound[(i % len(copies), phase)](sh)
+        b = bound[(i % len(copies), phase)]
+        for call in (b if isinstance(b, list) else [b]):
+            call(sh)
 
     def graph():
         # The same calls replayed from one HIP graph (one call per logits copy
@@ -497,11 +514,14 @@ def main():
                                f"{'bf16' if bf16 else 'fp32'}, emitted 1..{spec.T}, K={spec.K}"
                                + (f", packed into {packed_rows} rows" if packed_rows else "")
                                + (", counts and tokens from completion records"
-                                  if args.records else ""),
+                                  if args.records else "")
+                               + (f", vocabulary in {args.shards} shards" if args.shards else ""),
                    "active_rows": active, "capacity": spec.capacity, "T": spec.T, "V": spec.V,
                    "K": spec.K, "copies": len(copies), "oracle_rows_checked": checked},
-        "roofline": roofline(spec.name if args.K is None and not args.records else "",
-                             "reduce_kernel", algo_bytes, mean_reduce_ms, packed=bool(packed_rows)),
+        "roofline": roofline(spec.name if args.K is None and not args.records and not args.shards
+                             else "", "reduce_kernel" if not args.shards
+                             else f"reduce_kernel + shard_finalize_kernel, {args.shards} shard passes",
+                             algo_bytes, mean_reduce_ms, packed=bool(packed_rows or args.shards)),
         "reduce_ms": mean_reduce_ms,
         "merge_ms": mean_merge_ms,
         "graph_replay": graph_res,

@@ -16,9 +16,10 @@ alternatives) has its own plan:
     pplan.run(logits, targets, out, pplan.workspace())
 
 The functions ``flare_logprobs_plan``, ``flare_logprobs_run`` (and its two
-launches ``flare_logprobs_reduce`` and ``flare_logprobs_merge``), their
-``flare_prompt_logprobs_*`` counterparts, ``flare_status_string`` and
-``flare_logprobs_abi_version`` mirror the C entry points one to one.
+launches ``flare_logprobs_reduce`` and ``flare_logprobs_merge``), the packed,
+records and vocabulary-sharded variants, the ``flare_prompt_logprobs_*``
+counterparts, ``flare_status_string`` and ``flare_logprobs_abi_version``
+mirror the C entry points one to one.
 """
 from __future__ import annotations
 
@@ -59,7 +60,8 @@ class PlanStruct(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64), ("record_offset", ctypes.c_uint64),
                 ("lse_offset", ctypes.c_uint64), ("slots_offset", ctypes.c_uint64),
                 ("guard_offset", ctypes.c_uint64), ("packed_rows", ctypes.c_int32),
-                ("reserved", ctypes.c_uint32 * 5)]
+                ("shards", ctypes.c_int32), ("exchange_offset", ctypes.c_uint64),
+                ("reserved", ctypes.c_uint32 * 2)]
 
 
 class FlareError(RuntimeError):
@@ -113,6 +115,20 @@ def lib() -> ctypes.CDLL:
             f.restype = c.c_int
             f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
                           c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
+        L.flare_logprobs_plan_sharded.restype = c.c_int
+        L.flare_logprobs_plan_sharded.argtypes = [c.POINTER(PlanStruct)] + [c.c_int32] * 8
+        for name in ("flare_logprobs_run_sharded", "flare_logprobs_shard_merge"):
+            f = getattr(L, name)
+            f.restype = c.c_int
+            f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
+                          c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                          c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p]
+        L.flare_logprobs_shard_pass.restype = c.c_int
+        L.flare_logprobs_shard_pass.argtypes = [c.POINTER(PlanStruct), c.c_int32, c.c_void_p,
+                                                c.c_int32, c.c_int64, c.c_int32, c.c_int32,
+                                                c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                                c.c_void_p, c.c_int32, c.c_void_p, c.c_void_p,
+                                                c.c_void_p]
         L.flare_status_string.restype = c.c_char_p
         L.flare_status_string.argtypes = [c.c_int]
         L.flare_logprobs_abi_version.restype = c.c_uint32
@@ -145,6 +161,23 @@ def flare_logprobs_plan(capacity: int, T: int, V: int, V_pad: int, dtype, K: int
     if rc != 0:
         raise FlareError(rc, "flare_logprobs_plan")
     return plan
+
+
+def flare_logprobs_plan_sharded(capacity: int, T: int, V: int, V_pad: int, dtype, K: int,
+                                shards: int, device: int) -> PlanStruct:
+    plan = PlanStruct()
+    rc = lib().flare_logprobs_plan_sharded(ctypes.byref(plan), capacity, T, V, V_pad,
+                                           dtype_code(dtype), K, shards, device)
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_plan_sharded")
+    return plan
+
+
+def shard_bounds(V: int, shards: int) -> list[int]:
+    """Vocabulary lanes of each shard: shard r owns [b[r], b[r + 1]) (the C
+    library's rule: floor(r V / shards) rounded up to a multiple of 8)."""
+    b = [min(V, -(-(r * V // shards) // 8) * 8) for r in range(shards)]
+    return b + [V]
 
 
 def flare_logprobs_plan_packed(capacity: int, T: int, packed_rows: int, V: int, V_pad: int,
@@ -241,6 +274,35 @@ def flare_logprobs_run_records(plan: PlanStruct, logits, dtype, rows: int, V: in
         raise FlareError(rc, "flare_logprobs_run_records")
 
 
+def flare_logprobs_run_sharded(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                               requested, id_counts, ids, emitted_counts, tokens, K: int, out,
+                               workspace, stream=None) -> None:
+    """Every shard pass of a sharded plan, then the cross-shard merge."""
+    _call("flare_logprobs_run_sharded", plan, logits, dtype, rows, V, V_pad, requested,
+          id_counts, ids, emitted_counts, tokens, K, out, workspace, stream)
+
+
+def flare_logprobs_shard_merge(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                               requested, id_counts, ids, emitted_counts, tokens, K: int, out,
+                               workspace, stream=None) -> None:
+    """The cross-shard merge over the gathered shard records."""
+    _call("flare_logprobs_shard_merge", plan, logits, dtype, rows, V, V_pad, requested,
+          id_counts, ids, emitted_counts, tokens, K, out, workspace, stream)
+
+
+def flare_logprobs_shard_pass(plan: PlanStruct, shard: int, logits, dtype, rows: int, V: int,
+                              V_pad: int, requested, id_counts, ids, emitted_counts, tokens,
+                              K: int, out, workspace, stream=None) -> None:
+    """Shard `shard`'s pass: the reduction of its columns and its exchange records."""
+    rc = lib().flare_logprobs_shard_pass(ctypes.byref(plan), shard, _ptr(logits),
+                                         dtype_code(dtype), rows, V, V_pad, _ptr(requested),
+                                         _ptr(id_counts), _ptr(ids), _ptr(emitted_counts),
+                                         _ptr(tokens), K, _ptr(out), _ptr(workspace),
+                                         _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_shard_pass")
+
+
 def flare_logprobs_reduce(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
                           requested, id_counts, ids, emitted_counts, tokens, K: int, out,
                           workspace, stream=None) -> None:
@@ -270,19 +332,27 @@ class Plan:
 
     def __init__(self, capacity: int, T: int, V: int, V_pad: int | None = None,
                  dtype=torch.bfloat16, K: int = 20, device: int | None = None,
-                 packed_rows: int | None = None):
+                 packed_rows: int | None = None, shards: int | None = None):
         """`packed_rows` = P selects packed target rows (logits [P, V_pad], slot s's
-        row t at row_offsets[s] + t); None keeps the rectangular [capacity*T, V_pad]."""
+        row t at row_offsets[s] + t); None keeps the rectangular [capacity*T, V_pad].
+        `shards` = N splits the vocabulary into N shards (a shard pass per shard,
+        then the cross-shard merge)."""
         if device is None:
             device = torch.cuda.current_device()
         self.torch_dtype = torch.bfloat16 if dtype_code(dtype) == DTYPE_BF16 else torch.float32
         self.V_pad = V if V_pad is None else V_pad
-        if packed_rows is None:
+        if packed_rows is not None and shards is not None:
+            raise ValueError("a plan is either packed or sharded")
+        if shards is not None:
+            self.raw = flare_logprobs_plan_sharded(capacity, T, V, self.V_pad, dtype, K, shards,
+                                                   device)
+        elif packed_rows is None:
             self.raw = flare_logprobs_plan(capacity, T, V, self.V_pad, dtype, K, device)
         else:
             self.raw = flare_logprobs_plan_packed(capacity, T, packed_rows, V, self.V_pad, dtype,
                                                   K, device)
         self.packed_rows = packed_rows
+        self.shards = shards
         self.capacity, self.T, self.V, self.K, self.device_index = capacity, T, V, K, device
 
     @property
@@ -302,8 +372,15 @@ class Plan:
         off = int(self.raw.lse_offset)
         return workspace[off:off + 4 * n].view(torch.float32)
 
+    def exchange(self, workspace: torch.Tensor) -> torch.Tensor:
+        """Sharded plans: the gathered shard records, as int32 [capacity*T, shards, 138]."""
+        n = self.capacity * self.T
+        off = int(self.raw.exchange_offset)
+        return workspace[off:off + n * self.shards * 552].view(torch.int32).view(n, self.shards, 138)
+
     def guard(self, workspace: torch.Tensor) -> torch.Tensor:
-        """Diagnostic view: per reduced row, the parts the merge's guard streamed again."""
+        """Diagnostic view: per reduced row, the parts (shards, for a sharded plan)
+        that the merge's guard streamed again."""
         n = self.capacity * self.T
         off = int(self.raw.guard_offset)
         return workspace[off:off + 4 * n].view(torch.int32)
@@ -336,16 +413,28 @@ class Plan:
         _check(ids, "ids", torch.int32, self.capacity * MAX_IDS, dev)
         _check(out, "out", torch.int32, rows * ROW_WORDS, dev)
         _check(workspace, "workspace", torch.uint8, self.workspace_bytes, dev)
-        name = {"all": "flare_logprobs_run", "reduce": "flare_logprobs_reduce",
-                "merge": "flare_logprobs_merge"}[phase] + ("_packed" if packed else "")
         head = (ctypes.byref(self.raw), _ptr(logits), DTYPE_BF16 if self.torch_dtype ==
                 torch.bfloat16 else DTYPE_FP32, self.packed_rows if packed else rows, self.V,
                 self.V_pad, _ptr(requested), _ptr(id_counts), _ptr(ids), _ptr(emitted_counts),
                 _ptr(tokens))
-        args = head + ((_ptr(row_offsets),) if packed else ()) + (self.K, _ptr(out),
-                                                                  _ptr(workspace))
         keep = (self, logits, tokens, emitted_counts, requested, id_counts, ids, out, workspace,
                 row_offsets)
+        if self.shards is not None:
+            # "all": every shard pass, then the merge; "shard:r": rank r's pass;
+            # "merge": the cross-shard merge of the gathered records.
+            tail = (self.K, _ptr(out), _ptr(workspace))
+            if phase == "all":
+                return BoundCall("flare_logprobs_run_sharded", head + tail, keep)
+            if phase == "merge":
+                return BoundCall("flare_logprobs_shard_merge", head + tail, keep)
+            if phase.startswith("shard:"):
+                r = int(phase.split(":", 1)[1])
+                return BoundCall("flare_logprobs_shard_pass", (head[0], r) + head[1:] + tail, keep)
+            raise ValueError(f"sharded plans take phase 'all', 'shard:r' or 'merge', not {phase!r}")
+        name = {"all": "flare_logprobs_run", "reduce": "flare_logprobs_reduce",
+                "merge": "flare_logprobs_merge"}[phase] + ("_packed" if packed else "")
+        args = head + ((_ptr(row_offsets),) if packed else ()) + (self.K, _ptr(out),
+                                                                  _ptr(workspace))
         return BoundCall(name, args, keep)
 
     def bind_records(self, logits, records, requested, out, workspace, emitted_field: int,

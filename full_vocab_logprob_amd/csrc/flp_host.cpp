@@ -118,6 +118,35 @@ static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, i
 
 extern "C" {
 
+int flare_logprobs_plan_sharded(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T,
+                                int32_t V, int32_t V_pad, int32_t dtype, int32_t K,
+                                int32_t shards, int32_t device) {
+  if (!plan) return FLARE_ERR_INVALID_ARGUMENT;
+  memset(plan, 0, sizeof *plan);
+  if (shards < 1 || shards > flp::kMaxShards || V < 1) return FLARE_ERR_INVALID_ARGUMENT;
+  for (int r = 0; r < shards; ++r)
+    if (flp::shard_lo(r + 1, V, shards) <= flp::shard_lo(r, V, shards)) return FLARE_ERR_INVALID_ARGUMENT;
+  const int rc = make_plan(plan, capacity, T, V, V_pad, dtype, K, device, FLARE_MODE_GENERATION, 0);
+  if (rc != FLARE_OK) return rc;
+  // Part records sized for the widest shard (the shard passes reuse them in
+  // turn); then the gathered exchange records [rows, shards].
+  const int unit = flp::unit_elems(dtype);
+  int32_t units = 0;
+  for (int r = 0; r < shards; ++r) {
+    const int w = flp::shard_lo(r + 1, V, shards) - flp::shard_lo(r, V, shards);
+    const int32_t u = (w + unit - 1) / unit;
+    units = u > units ? u : units;
+  }
+  const uint64_t rows = (uint64_t)capacity * T;
+  plan->units = units;
+  plan->shards = shards;
+  uint64_t off = plan->workspace_bytes;
+  plan->exchange_offset = off;
+  off = align_up(off + rows * shards * sizeof(flp::ShardRecord), kAlign);
+  plan->workspace_bytes = off;
+  return FLARE_OK;
+}
+
 int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, int32_t V,
                         int32_t V_pad, int32_t dtype, int32_t K, int32_t device) {
   return make_plan(plan, capacity, T, V, V_pad, dtype, K, device, FLARE_MODE_GENERATION, 0);
@@ -142,6 +171,12 @@ int flare_prompt_logprobs_plan(flare_logprobs_plan_t* plan, int32_t rows, int32_
 
 }  // extern "C"
 
+// The `shard` argument of run_phases: an unsharded call, every shard pass then
+// the cross-shard merge, the merge alone, or (>= 0) one shard's pass.
+constexpr int32_t kNoShard = -1;
+constexpr int32_t kAllShards = -2;
+constexpr int32_t kShardMerge = -3;
+
 // Validate one call's arguments against its plan and launch `phases`.
 static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int32_t dtype,
                       int64_t rows, int32_t V, int32_t V_pad, const int32_t* requested,
@@ -149,7 +184,8 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
                       const int32_t* emitted_counts, const int32_t* tokens,
                       const int32_t* row_offsets, int32_t K, int32_t* out, void* workspace,
                       void* hip_stream, int phases, const int64_t* records = nullptr,
-                      int32_t emitted_field = 0, int32_t row_words = FLARE_LOGPROBS_ROW_WORDS) {
+                      int32_t emitted_field = 0, int32_t row_words = FLARE_LOGPROBS_ROW_WORDS,
+                      int32_t shard = kNoShard) {
   // Completion records replace emitted_counts and tokens; a frame without ID
   // inputs (both null) is natural-only with rows of 2 + 2K words.
   const bool rec = records != nullptr;
@@ -165,6 +201,7 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
   if ((plan->packed_rows > 0) != (row_offsets != nullptr)) return FLARE_ERR_PLAN_MISMATCH;
   if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
   if (plan->mode != FLARE_MODE_GENERATION) return FLARE_ERR_PLAN_MISMATCH;
+  if ((plan->shards > 0) != (shard != kNoShard)) return FLARE_ERR_PLAN_MISMATCH;
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
   if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad || K != plan->K)
     return FLARE_ERR_PLAN_MISMATCH;
@@ -202,8 +239,42 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
   p.units = plan->units;
   p.workers = plan->ranges;
 
+  p.shards = 0;
+  p.shard = 0;
+  p.shard_base = 0;
+  p.full_V = V;
+  p.xrec = nullptr;
+
   const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
-  const int e = flp::launch(p, dtype, vec, false, phases, hip_stream);
+  if (shard == kNoShard) {
+    const int e = flp::launch(p, dtype, vec, false, phases, hip_stream);
+    return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
+  }
+  // Vocabulary shards: a shard pass (the reduction on the shard's columns,
+  // then its exchange records), or the cross-shard merge.
+  p.shards = plan->shards;
+  p.xrec = (flp::ShardRecord*)(ws + plan->exchange_offset);
+  auto pass = [&](int r) -> int {
+    flp::Params q = p;
+    const int lo = flp::shard_lo(r, V, plan->shards), hi = flp::shard_lo(r + 1, V, plan->shards);
+    q.shard = r;
+    q.shard_base = lo;
+    q.logits = (const char*)logits + (int64_t)lo * flp::elem_bytes(dtype);
+    q.V = hi - lo;
+    q.units = (q.V + flp::unit_elems(dtype) - 1) / flp::unit_elems(dtype);
+    const bool qvec = plan->vector_rows && (((uintptr_t)q.logits & 15u) == 0);
+    int e = flp::launch(q, dtype, qvec, false, flp::kPhaseReduce, hip_stream);
+    if (e == 0) e = flp::launch_shard_finalize(q, dtype, hip_stream);
+    return e;
+  };
+  int e = 0;
+  if (shard >= 0) {
+    e = pass(shard);
+  } else {
+    if (shard == kAllShards)
+      for (int r = 0; r < plan->shards && e == 0; ++r) e = pass(r);
+    if (e == 0) e = flp::launch_shard_merge(p, dtype, vec, hip_stream);
+  }
   return e == 0 ? FLARE_OK : FLARE_ERR_LAUNCH;
 }
 
@@ -213,7 +284,7 @@ static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, 
                          int32_t* out, void* workspace, void* hip_stream, int phases) {
   if (!plan || !logits || !targets || !out || !workspace) return FLARE_ERR_INVALID_ARGUMENT;
   if (plan->abi_version != FLARE_LOGPROBS_ABI_VERSION) return FLARE_ERR_PLAN_MISMATCH;
-  if (plan->mode != FLARE_MODE_PROMPT) return FLARE_ERR_PLAN_MISMATCH;
+  if (plan->mode != FLARE_MODE_PROMPT || plan->shards != 0) return FLARE_ERR_PLAN_MISMATCH;
   if (dtype != FLARE_DTYPE_FP32 && dtype != FLARE_DTYPE_BF16) return FLARE_ERR_UNSUPPORTED_DTYPE;
   if (dtype != plan->dtype || V != plan->V || V_pad != plan->V_pad) return FLARE_ERR_PLAN_MISMATCH;
   if (rows != (int64_t)plan->capacity || plan->T != 1 || plan->K != FLARE_PROMPT_ALTERNATIVES ||
@@ -254,6 +325,11 @@ static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, 
   p.K = FLARE_PROMPT_ALTERNATIVES;
   p.units = plan->units;
   p.workers = plan->ranges;
+  p.shards = 0;
+  p.shard = 0;
+  p.shard_base = 0;
+  p.full_V = V;
+  p.xrec = nullptr;
 
   const bool vec = plan->vector_rows && (((uintptr_t)logits & 15u) == 0);
   const int e = flp::launch(p, dtype, vec, true, phases, hip_stream);
@@ -337,6 +413,41 @@ int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits, 
                          int32_t* out, void* workspace, void* hip_stream) {
   return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
                     emitted_counts, tokens, nullptr, K, out, workspace, hip_stream, flp::kPhaseMerge);
+}
+
+int flare_logprobs_run_sharded(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int32_t* emitted_counts,
+                               const int32_t* tokens, int32_t K, int32_t* out, void* workspace,
+                               void* hip_stream) {
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, nullptr, K, out, workspace, hip_stream,
+                    flp::kPhaseReduce | flp::kPhaseMerge, nullptr, 0, FLARE_LOGPROBS_ROW_WORDS,
+                    kAllShards);
+}
+
+int flare_logprobs_shard_pass(const flare_logprobs_plan_t* plan, int32_t shard,
+                              const void* logits, int32_t dtype, int64_t rows, int32_t V,
+                              int32_t V_pad, const int32_t* requested, const int32_t* id_counts,
+                              const int32_t* ids, const int32_t* emitted_counts,
+                              const int32_t* tokens, int32_t K, int32_t* out, void* workspace,
+                              void* hip_stream) {
+  if (!plan || shard < 0 || shard >= plan->shards) return FLARE_ERR_INVALID_ARGUMENT;
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, nullptr, K, out, workspace, hip_stream,
+                    flp::kPhaseReduce, nullptr, 0, FLARE_LOGPROBS_ROW_WORDS, shard);
+}
+
+int flare_logprobs_shard_merge(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int32_t* emitted_counts,
+                               const int32_t* tokens, int32_t K, int32_t* out, void* workspace,
+                               void* hip_stream) {
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, nullptr, K, out, workspace, hip_stream,
+                    flp::kPhaseMerge, nullptr, 0, FLARE_LOGPROBS_ROW_WORDS, kShardMerge);
 }
 
 int flare_prompt_logprobs_run(const flare_logprobs_plan_t* plan, const void* logits,

@@ -41,6 +41,37 @@ struct PartRecord {
 };
 static_assert(sizeof(PartRecord) == 280, "record layout");
 
+// Vocabulary sharding (one GPU standing in for tensor-parallel ranks): shard
+// r of `shards` owns vocabulary lanes [shard_lo(r), shard_lo(r + 1)), its
+// boundaries rounded up to multiples of 8 lanes so that every shard's first
+// lane is 16-byte aligned in bf16 and FP32 rows.
+constexpr int kShardAlign = 8;
+constexpr int kMaxShards = 32;
+inline __host__ __device__ int shard_lo(int r, int V, int shards) {
+  if (r >= shards) return V;
+  const int64_t b = ((int64_t)r * V / shards + kShardAlign - 1) / kShardAlign * kShardAlign;
+  return b < V ? (int)b : V;
+}
+
+// The record one shard would exchange per reduced position: its max and its
+// exponential sum relative to it, the chosen token's raw logit when it owns
+// the token, and either its best 32 raw keys (global token IDs) with a cut
+// bounding every key it dropped, or the raw logits of the selected IDs it
+// owns.  552 bytes.
+struct ShardRecord {
+  float m;
+  float s;
+  float chosen;      // raw logit of the chosen token (flags bit 0)
+  int32_t flags;     // bit 0: this shard owns the chosen token
+  uint64_t cut;      // every lane the shard dropped has a raw key <= cut (0: none)
+  union {
+    uint64_t keys[kKeep];  // natural: best raw keys, sorted descending
+    float sel[128];        // selected: raw logit of ids[j] when owned
+  };
+  uint32_t owned[4];       // selected: bit j set iff this shard owns ids[j]
+};
+static_assert(sizeof(ShardRecord) == 552, "shard record layout");
+
 struct Params {
   const void* logits;
   const int32_t* requested;
@@ -66,6 +97,15 @@ struct Params {
   int32_t K;
   int32_t units;    // units per row
   int32_t workers;  // workgroups of the persistent launch (one unit range each)
+  // Vocabulary sharding: 0 shards for an unsharded call.  A shard pass runs
+  // the reduction on shard `shard` (logits, V and units of that slice; token
+  // IDs local to it) and the finalize writes xrec[row * shards + shard]; the
+  // cross-shard merge takes the whole rows and the gathered records.
+  int32_t shards;
+  int32_t shard;
+  int32_t shard_base;   // first vocabulary lane of `shard`
+  int32_t full_V;       // the unsharded vocabulary
+  ShardRecord* xrec;
 };
 
 // Launches of one call; `phases` is a mask of kPhaseReduce and kPhaseMerge.
@@ -75,6 +115,9 @@ constexpr int kPhaseMerge = 2;
 // `score` selects prompt scoring: one row per slot (T = 1), a row is active
 // when its target (tokens[s]) is a vocabulary ID, K = 20, kPromptWords per row.
 int launch(const Params& p, int dtype, bool vector_rows, bool score, int phases, void* stream);
+// Shard pass tail and cross-shard merge (flp_kernels.hip); hipError_t as int.
+int launch_shard_finalize(const Params& p, int dtype, void* stream);
+int launch_shard_merge(const Params& p, int dtype, bool vector_rows, void* stream);
 // Resident reduction workgroups per CU (0 on error).
 int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity, bool packed);
 // Dynamic LDS of the reduction: the slot table, and each slot's packed row offset.

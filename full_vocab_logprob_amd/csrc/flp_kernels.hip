@@ -1621,6 +1621,253 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   }
 }
 
+// =========================================================== vocabulary shards
+// The pages' vocabulary-sharded variant keeps each tensor-parallel rank's
+// logits as a vocabulary shard and exchanges, per position, each shard's max
+// and exponential mass, the chosen token's raw logit from its owner, and each
+// shard's best 32 sort keys or the selected IDs' raw logits; a final launch
+// merges them into the same packed output (design page, vocabulary-sharded
+// paragraph).  Here one GPU stands in for the ranks: a shard pass is the
+// reduction on the shard's column slice followed by shard_finalize_kernel,
+// which writes the record the rank would exchange; shard_merge_kernel reads
+// the gathered records.  Keys rank raw logits (as in the unsharded path), so
+// one exchange carries everything; only a shard that fails the exactness
+// guard needs its lanes again (on one GPU the merge reads them directly).
+
+// One wave per reduced position: the shard's parts combined into its record.
+template <int DT>
+__global__ __launch_bounds__(kMergeBlock) void shard_finalize_kernel(Params p) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = (int)blockIdx.x * kMergeWaves + wv;
+  if (row >= p.capacity * p.T) return;
+  const int s = row / p.T, t = row - s * p.T;
+  const int req = p.requested[s], emi = emitted_of(p, s);
+  const int cnt = p.id_counts ? p.id_counts[s] : 0;
+  const int before = p.slot_rows[s], total = p.slot_rows[p.capacity];
+  const int tok = token_of(p, s, t);
+  const int rows_s = req == 0 ? 0 : (emi < 0 ? 0 : (emi > p.T ? p.T : emi));
+  if (t >= rows_s) return;
+  const int n_sel = cnt < 0 ? 0 : (cnt > 128 ? 128 : cnt);
+  const bool natural = p.K > 0 && n_sel == 0;
+  const int U = p.units, lo = p.shard_base, hi = p.shard_base + p.V;
+  const PartRecord* rec = p.records + (int64_t)row * U;
+  const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * Elem<DT>::kBytes;
+  ShardRecord* xr = p.xrec + (int64_t)row * p.shards + p.shard;
+
+  // The row's parts in this shard's launch, as the merge finds them.
+  const int a = before + t;
+  const int ranges = range_count((int64_t)total * U, p.workers);
+  const bool start = lane < U && (lane == 0 || is_range_start(a * U + lane, total * U, ranges));
+  const uint64_t starts = __ballot(start);
+  const int np = __popcll(starts);
+  const int u0 = start ? lane : 0;  // lane i < np: first unit of part i, after compaction below
+  int part_first = 0;
+  {
+    // compact: part i's first unit to lane i
+    const int pos = lanes_below(starts);
+    __shared__ int16_t firsts[kMergeWaves][kMaxUnits];
+    if (start) firsts[wv][pos] = (int16_t)u0;
+    wave_sync();
+    part_first = lane < np ? firsts[wv][lane] : 0;
+    wave_sync();
+  }
+  float pm = kNegInf, ps = 0.0f;
+  uint64_t c_key = 0ull;
+  if (lane < np) {
+    pm = rec[part_first].m;
+    ps = rec[part_first].s;
+    c_key = rec[part_first].cut;
+  }
+  const float M = wave_max(pm, lane);
+  float term = 0.0f;
+  if (lane < np && pm != kNegInf) term = ps * __builtin_amdgcn_exp2f((pm - M) * kLog2e);
+  const float S = wave_sum(term, lane);
+
+  // The shard's best 32 raw keys: every part's kept keys (sorted by raw key)
+  // merged two parts at a time; keys that fall out bound what was dropped.
+  uint64_t top = 0ull, cut = 0ull;
+  int kept = 0;
+  if (natural) {
+    for (int pb = 0; pb < np; pb += 2) {
+      const int part = pb + (lane >> 5);
+      const int pf = __shfl(part_first, part < 64 ? part : 0, 64);
+      const uint64_t raw = part < np ? rec[pf].keys[lane & 31] : 0ull;
+      kept += __popcll(__ballot(raw != 0ull));
+      top = merge_top32(top, sort_halves_desc(raw, lane), lane);
+    }
+    uint64_t c = c_key;
+    c = xlane64<32>(c, lane) > c ? xlane64<32>(c, lane) : c;
+    c = xlane64<16>(c, lane) > c ? xlane64<16>(c, lane) : c;
+    c = xlane64<8>(c, lane) > c ? xlane64<8>(c, lane) : c;
+    c = xlane64<4>(c, lane) > c ? xlane64<4>(c, lane) : c;
+    c = xlane64<2>(c, lane) > c ? xlane64<2>(c, lane) : c;
+    c = xlane64<1>(c, lane) > c ? xlane64<1>(c, lane) : c;
+    cut = readlane64(c, 0);
+    if (kept > kKeep) {
+      const uint64_t k32 = readlane64(top, kKeep - 1);
+      cut = k32 > cut ? k32 : cut;
+    }
+    // Global token IDs (the shard's lanes start at `lo`).
+    if (top != 0ull) top = (top & 0xFFFFFFFF00000000ull) | (uint64_t)(~(key_id(top) + (uint32_t)lo));
+    if (cut != 0ull && (uint32_t)cut != 0u)
+      cut = (cut & 0xFFFFFFFF00000000ull) | (uint64_t)(~(key_id(cut) + (uint32_t)lo));
+  }
+  // The chosen token's and the owned selected IDs' raw logits.
+  const bool own_tok = tok >= lo && tok < hi;
+  float x_tok = 0.0f;
+  if (lane == 0 && own_tok) x_tok = load_elem<DT>(rowp, tok - lo);
+  uint32_t own_mask[2] = {0u, 0u};
+  float x_sel[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    bool own = false;
+    if (j < n_sel) {
+      const int id = p.ids[(int64_t)s * 128 + j];
+      own = id >= lo && id < hi;
+      if (own) x_sel[h] = load_elem<DT>(rowp, id - lo);
+    }
+    const uint64_t b = __ballot(own);
+    own_mask[h] = 0u;
+    if (lane == 0) own_mask[h] = 0u;
+    if (lane < 2) own_mask[h] = (uint32_t)(b >> (32 * lane));
+  }
+  if (lane == 0) {
+    xr->m = M;
+    xr->s = S;
+    xr->chosen = x_tok;
+    xr->flags = own_tok ? 1 : 0;
+    xr->cut = cut;
+  }
+  if (natural) {
+    if (lane < kKeep) xr->keys[lane] = top;
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = lane + 64 * h;
+      if (j < n_sel) xr->sel[j] = x_sel[h];
+      if (lane < 2) xr->owned[2 * h + lane] = own_mask[h];
+    }
+  }
+}
+
+// One wave per reduced position: L from the gathered shard records in shard
+// order, the chosen and selected values from their owners' raw logits, and
+// the natural top K over every shard's kept keys with the exactness guard
+// per shard (an unsafe shard's lanes are streamed again).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kMergeBlock) void shard_merge_kernel(Params p) {
+  __shared__ uint64_t buf[kMergeWaves][256];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = (int)blockIdx.x * kMergeWaves + wv;
+  if (row >= p.capacity * p.T) return;
+  const int s = row / p.T, t = row - s * p.T;
+  const int req = p.requested[s], emi = emitted_of(p, s);
+  const int cnt = p.id_counts ? p.id_counts[s] : 0;
+  const int tok = token_of(p, s, t);
+  const int rows_s = req == 0 ? 0 : (emi < 0 ? 0 : (emi > p.T ? p.T : emi));
+  if (t >= rows_s) return;
+  const int n_sel = cnt < 0 ? 0 : (cnt > 128 ? 128 : cnt);
+  const bool natural = p.K > 0 && n_sel == 0;
+  const int V = p.V, N = p.shards;
+  const ShardRecord* xr = p.xrec + (int64_t)row * N;
+  int32_t* out = p.out + (int64_t)row * p.row_words;
+  const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * Elem<DT>::kBytes;
+
+  float pm = kNegInf, ps = 0.0f, pc = 0.0f;
+  int pf = 0;
+  uint64_t c_key = 0ull;
+  if (lane < N) {
+    pm = xr[lane].m;
+    ps = xr[lane].s;
+    pf = xr[lane].flags;
+    pc = xr[lane].chosen;
+    c_key = xr[lane].cut;
+  }
+  const float M = wave_max(pm, lane);
+  float term = 0.0f;
+  if (lane < N && pm != kNegInf) term = ps * __builtin_amdgcn_exp2f((pm - M) * kLog2e);
+  const float L = M + logf(wave_sum(term, lane));
+  const uint64_t owners = __ballot(lane < N && (pf & 1));
+  if (lane == 0) {
+    p.lse[row] = L;
+    out[0] = tok;
+    uint32_t bits = kNanBits;
+    if (tok >= 0 && tok < V && owners != 0ull) {
+      const float x = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(pc), __builtin_ctzll(owners)));
+      bits = __float_as_uint(reported(x, L));
+    }
+    out[1] = (int32_t)bits;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    if (j < n_sel) {
+      const int id = p.ids[(int64_t)s * 128 + j];
+      uint32_t bits = kNanBits;
+      if (id >= 0 && id < V) {
+        // the owning shard, from the boundaries
+        int r = (int)((int64_t)id * N / V);
+        while (r + 1 < N && shard_lo(r + 1, V, N) <= id) ++r;
+        while (r > 0 && shard_lo(r, V, N) > id) --r;
+        if ((xr[r].owned[j >> 5] >> (j & 31)) & 1u) bits = __float_as_uint(reported(xr[r].sel[j], L));
+      }
+      *(int2*)(out + 2 + 2 * j) = make_int2(id, (int32_t)bits);
+    }
+  }
+  if (!natural) {
+    if (lane == 0) p.guard[row] = 0;
+    return;
+  }
+  const int K = p.K;
+  const int Keff = K < V ? K : V;
+  uint64_t top = 0ull;
+  for (int pb = 0; pb < N; pb += 2) {
+    const int r = pb + (lane >> 5);
+    const uint64_t raw = r < N ? xr[r].keys[lane & 31] : 0ull;
+    top = merge_top32(top, sort_halves_desc(raw != 0ull ? final_key(raw, L) : 0ull, lane), lane);
+  }
+  const uint64_t FK = readlane64(top, Keff - 1);
+  bool bad = false;
+  if (lane < N && c_key != 0ull) {
+    const float xc = key_value(c_key);
+    bool ok = final_key(c_key, L) <= FK;
+    if (ok && xc != kNegInf) ok = ukey32(reported(Elem<DT>::pred(xc), L)) < (uint32_t)(FK >> 32);
+    bad = !ok;
+  }
+  const uint64_t unsafe = __ballot(bad);
+  if (lane == 0) p.guard[row] = __popcll(unsafe);
+  if (unsafe != 0ull) {
+    top = 0ull;
+    for (int pb = 0; pb < N; pb += 2) {
+      const int r = pb + (lane >> 5);
+      uint64_t f = 0ull;
+      if (r < N && !((unsafe >> r) & 1ull)) {
+        const uint64_t raw = xr[r].keys[lane & 31];
+        if (raw != 0ull) f = final_key(raw, L);
+      }
+      top = merge_top32(top, sort64_desc(f, lane), lane);
+    }
+    uint64_t thr = FK;
+    for (int r = 0; r < N; ++r) {
+      if (!((unsafe >> r) & 1ull)) continue;
+      rescan_lanes<DT, VEC>(top, thr, rowp, shard_lo(r, V, N), shard_lo(r + 1, V, N), L, Keff, lane,
+                            &buf[wv][0], 256);
+    }
+  }
+  if (lane < K) {
+    int32_t id = -1;
+    uint32_t bits = kNanBits;
+    if (lane < Keff) {
+      id = (int32_t)key_id(top);
+      bits = __float_as_uint(unkey32((uint32_t)(top >> 32)));
+    }
+    *(int2*)(out + 2 + 2 * lane) = make_int2(id, (int32_t)bits);
+  }
+}
+
 template <int DT, bool VEC, bool SCORE>
 hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
   if (phases & kPhaseReduce) {
@@ -1638,6 +1885,30 @@ hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
 }
 
 }  // namespace
+
+int launch_shard_finalize(const Params& p, int dtype, void* stream) {
+  const int64_t rows = (int64_t)p.capacity * p.T;
+  const dim3 grid((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves));
+  if (dtype == 1)
+    hipLaunchKernelGGL(shard_finalize_kernel<1>, grid, dim3(kMergeBlock), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(shard_finalize_kernel<0>, grid, dim3(kMergeBlock), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
+int launch_shard_merge(const Params& p, int dtype, bool vector_rows, void* stream) {
+  const int64_t rows = (int64_t)p.capacity * p.T;
+  const dim3 grid((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves));
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == 1) {
+    if (vector_rows) hipLaunchKernelGGL((shard_merge_kernel<1, true>), grid, dim3(kMergeBlock), 0, st, p);
+    else hipLaunchKernelGGL((shard_merge_kernel<1, false>), grid, dim3(kMergeBlock), 0, st, p);
+  } else {
+    if (vector_rows) hipLaunchKernelGGL((shard_merge_kernel<0, true>), grid, dim3(kMergeBlock), 0, st, p);
+    else hipLaunchKernelGGL((shard_merge_kernel<0, false>), grid, dim3(kMergeBlock), 0, st, p);
+  }
+  return (int)hipGetLastError();
+}
 
 size_t prefix_lds_bytes(int capacity, bool packed) {
   return (size_t)(capacity + 1 + (packed ? capacity : 0)) * sizeof(int);

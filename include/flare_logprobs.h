@@ -103,7 +103,9 @@ typedef struct flare_logprobs_plan {
   uint64_t guard_offset;    /* int32[capacity * T]: parts of each reduced row that the
                                merge read again (diagnostic, see flare_logprobs_run) */
   int32_t packed_rows;      /* P of flare_logprobs_plan_packed; 0 for the rectangular layout */
-  uint32_t reserved[5];
+  int32_t shards;           /* vocabulary shards of flare_logprobs_plan_sharded; 0 otherwise */
+  uint64_t exchange_offset; /* sharded plans: the gathered shard records [rows, shards] */
+  uint32_t reserved[2];
 } flare_logprobs_plan_t;
 
 /*
@@ -288,6 +290,64 @@ int flare_prompt_logprobs_merge(const flare_logprobs_plan_t* plan, const void* l
                                 int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
                                 const int32_t* targets, int32_t* out, void* workspace,
                                 void* hip_stream);
+
+/*
+ * Vocabulary-sharded reduction on one GPU (Flare generation-logprobs design
+ * page, vocabulary-sharded paragraph: each tensor-parallel rank keeps its
+ * target logits as a vocabulary shard; the ranks exchange, per position,
+ * each shard's maximum and exponential mass, the chosen token's raw logit
+ * from its owner, and each shard's best 32 sort keys or the selected IDs'
+ * raw logits; a final launch merges them into the same packed output).
+ *
+ * Here the shards are column slices of one [rows, V_pad] logits buffer:
+ * shard r owns lanes [lo(r), lo(r + 1)) with lo(r) = floor(r V / shards)
+ * rounded up to a multiple of 8 and at most V (lo(shards) = V), so that each
+ * slice starts on a 16-byte boundary.  The result is the frame flare_logprobs_run writes,
+ * with the same gating, layout and defined behaviour; only the order in which
+ * L's FP32 partial sums are combined differs (shard by shard).
+ *
+ * flare_logprobs_plan_sharded: as flare_logprobs_plan, plus 1 <= shards <= 32
+ *   with every shard non-empty (else FLARE_ERR_INVALID_ARGUMENT).  The plan
+ *   records the shard count and the exchange records in the workspace:
+ *   plan->exchange_offset, [capacity * T, shards] records of 552 bytes
+ *   (max and exponential sum as FP32, the chosen raw logit and an ownership
+ *   flag, a 64-bit cut key, then either 32 raw 64-bit keys or 128 selected raw
+ *   logits, and a 128-bit ownership mask) -- the message a rank would send.
+ * flare_logprobs_shard_pass: what rank `shard` computes on its own: the
+ *   reduction of its columns and its exchange records (two launches).  The
+ *   arguments are those of flare_logprobs_run with the whole rows in `logits`;
+ *   only the shard's columns are read.
+ * flare_logprobs_shard_merge: the final launch over the gathered records:
+ *   L from the shards' maxima and sums in shard order, chosen and selected
+ *   values from their owners' raw logits, the natural top K over all shards'
+ *   keys.  A shard whose cut could hide a lane of the top K (only when the
+ *   subtraction of L ties values at the cutoff) has its columns streamed again
+ *   here; across ranks that is a second exchange from that shard's owner.
+ * flare_logprobs_run_sharded: every shard pass, then the merge.
+ * The unsharded entry points reject a sharded plan and these reject an
+ * unsharded one (FLARE_ERR_PLAN_MISMATCH).
+ */
+int flare_logprobs_plan_sharded(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T,
+                                int32_t V, int32_t V_pad, int32_t dtype, int32_t K,
+                                int32_t shards, int32_t device);
+int flare_logprobs_run_sharded(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int32_t* emitted_counts,
+                               const int32_t* tokens, int32_t K, int32_t* out, void* workspace,
+                               void* hip_stream);
+int flare_logprobs_shard_pass(const flare_logprobs_plan_t* plan, int32_t shard,
+                              const void* logits, int32_t dtype, int64_t rows, int32_t V,
+                              int32_t V_pad, const int32_t* requested, const int32_t* id_counts,
+                              const int32_t* ids, const int32_t* emitted_counts,
+                              const int32_t* tokens, int32_t K, int32_t* out, void* workspace,
+                              void* hip_stream);
+int flare_logprobs_shard_merge(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int32_t* emitted_counts,
+                               const int32_t* tokens, int32_t K, int32_t* out, void* workspace,
+                               void* hip_stream);
 
 /* Human-readable name of a flare_status value (static storage). */
 const char* flare_status_string(int status);

@@ -37,7 +37,9 @@ def test_header_declares_the_boundary():
             "flare_logprobs_abi_version", "flare_prompt_logprobs_plan",
             "flare_prompt_logprobs_run", "flare_prompt_logprobs_reduce",
             "flare_prompt_logprobs_merge", "flare_logprobs_plan_packed",
-            "flare_logprobs_run_packed", "flare_logprobs_run_records"} <= set(names)
+            "flare_logprobs_run_packed", "flare_logprobs_run_records",
+            "flare_logprobs_plan_sharded", "flare_logprobs_run_sharded",
+            "flare_logprobs_shard_pass", "flare_logprobs_shard_merge"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol(flp):
@@ -54,8 +56,8 @@ def test_abi_version_and_status_strings(flp):
 
 
 def test_plan_struct_layout_matches_header(flp):
-    # 16 int32-sized fields, 5 uint64, packed_rows, 5 reserved uint32
-    assert ctypes.sizeof(flp.PlanStruct) == 16 * 4 + 5 * 8 + 6 * 4
+    # 16 int32-sized fields, 5 uint64, packed_rows, shards, exchange_offset, 2 reserved uint32
+    assert ctypes.sizeof(flp.PlanStruct) == 16 * 4 + 5 * 8 + 2 * 4 + 8 + 2 * 4
 
 
 def host_plan(flp, capacity=128, T=8, V=248320, V_pad=248320, dtype=1, K=20):
@@ -314,3 +316,54 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("oracle_handle", ""), f
+
+
+# ------------------------------------------------------ vocabulary shards
+def sharded_plan(flp, shards=8, capacity=128, T=8, V=248320, V_pad=248320, dtype=1, K=20):
+    plan = flp.PlanStruct()
+    rc = flp.lib().flare_logprobs_plan_sharded(ctypes.byref(plan), capacity, T, V, V_pad, dtype,
+                                               K, shards, -1)
+    return rc, plan
+
+
+def test_sharded_plan_geometry(flp):
+    rc, p = sharded_plan(flp)
+    assert rc == 0 and p.shards == 8 and p.mode == flp.MODE_GENERATION
+    b = flp.shard_bounds(248320, 8)
+    assert b == [31040 * r for r in range(9)]
+    assert p.units == 2  # each 31,040-lane shard needs two 16,384-lane units
+    rows = 128 * 8
+    assert p.exchange_offset >= p.guard_offset + 4 * rows and p.exchange_offset % 16 == 0
+    assert p.workspace_bytes >= p.exchange_offset + rows * 8 * 552
+    # boundaries: multiples of 8, nondecreasing, covering [0, V)
+    for V, n in ((1000, 7), (50001, 32), (64, 8), (248320, 3)):
+        b = flp.shard_bounds(V, n)
+        assert b[0] == 0 and b[-1] == V and all(x % 8 == 0 for x in b[:-1])
+        assert all(b[i] < b[i + 1] for i in range(n))
+    # the unsharded plan of the same geometry has no shards
+    rc, q = host_plan(flp)
+    assert q.shards == 0 and q.exchange_offset == 0
+
+
+@pytest.mark.parametrize("kw", [dict(shards=0), dict(shards=33), dict(V=40, V_pad=40, shards=8),
+                                dict(V=50, V_pad=56, shards=8), dict(K=21)])
+def test_sharded_plan_rejects(flp, kw):
+    rc, p = sharded_plan(flp, **kw)
+    assert rc == 1 and p.abi_version == 0
+
+
+def test_sharded_and_unsharded_entry_points_reject_each_other(flp):
+    rc, sp = sharded_plan(flp)
+    rc2, up = host_plan(flp)
+    assert rc == 0 and rc2 == 0
+    L = flp.lib()
+    args = (FAKE, 1, 128 * 8, 248320, 248320, FAKE, FAKE, FAKE, FAKE, FAKE, 20, FAKE, FAKE, None)
+    assert L.flare_logprobs_run(ctypes.byref(sp), *args) == 3
+    assert L.flare_logprobs_reduce(ctypes.byref(sp), *args) == 3
+    assert L.flare_logprobs_run_sharded(ctypes.byref(up), *args) == 3
+    assert L.flare_logprobs_shard_merge(ctypes.byref(up), *args) == 3
+    assert L.flare_logprobs_shard_pass(ctypes.byref(up), 0, *args) == 1  # no shard 0
+    assert L.flare_logprobs_shard_pass(ctypes.byref(sp), 8, *args) == 1
+    assert L.flare_logprobs_shard_pass(ctypes.byref(sp), -1, *args) == 1
+    assert L.flare_logprobs_run_sharded(ctypes.byref(sp), FAKE, 1, 128 * 8, 248320, 248320, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, 5, FAKE, FAKE, None) == 3
