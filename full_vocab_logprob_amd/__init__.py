@@ -45,7 +45,7 @@ DTYPE_BF16 = 1
 
 STATUS = {0: "FLARE_OK", 1: "FLARE_ERR_INVALID_ARGUMENT", 2: "FLARE_ERR_UNSUPPORTED_DTYPE",
           3: "FLARE_ERR_PLAN_MISMATCH", 4: "FLARE_ERR_DEVICE", 5: "FLARE_ERR_LAUNCH",
-          6: "FLARE_ERR_UNSUPPORTED_SIZE"}
+          6: "FLARE_ERR_UNSUPPORTED_SIZE", 7: "FLARE_ERR_SCRATCH_TOO_SMALL"}
 
 
 class PlanStruct(ctypes.Structure):
@@ -115,6 +115,11 @@ def lib() -> ctypes.CDLL:
             f.restype = c.c_int
             f.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32, c.c_int64, c.c_int32,
                           c.c_int32, c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p]
+        L.flare_logprobs_run_noalloc.restype = c.c_int
+        L.flare_logprobs_run_noalloc.argtypes = [c.POINTER(PlanStruct), c.c_void_p, c.c_int32,
+                                                 c.c_int64, c.c_int32, c.c_int32, c.c_void_p,
+                                                 c.c_void_p, c.c_void_p, c.c_void_p, c.c_void_p,
+                                                 c.c_int32, c.c_void_p, c.c_void_p]
         L.flare_logprobs_plan_sharded.restype = c.c_int
         L.flare_logprobs_plan_sharded.argtypes = [c.POINTER(PlanStruct)] + [c.c_int32] * 8
         for name in ("flare_logprobs_run_sharded", "flare_logprobs_shard_merge"):
@@ -272,6 +277,19 @@ def flare_logprobs_run_records(plan: PlanStruct, logits, dtype, rows: int, V: in
                                           out_row_words, _ptr(workspace), _stream(stream))
     if rc != 0:
         raise FlareError(rc, "flare_logprobs_run_records")
+
+
+def flare_logprobs_run_noalloc(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,
+                               requested, id_counts, ids, emitted_counts, tokens, K: int, out,
+                               stream=None) -> None:
+    """flare_logprobs_run on the library's static 16 MiB scratch (no workspace,
+    no allocation); calls that overlap on one GPU race."""
+    rc = lib().flare_logprobs_run_noalloc(ctypes.byref(plan), _ptr(logits), dtype_code(dtype),
+                                          rows, V, V_pad, _ptr(requested), _ptr(id_counts),
+                                          _ptr(ids), _ptr(emitted_counts), _ptr(tokens), K,
+                                          _ptr(out), _stream(stream))
+    if rc != 0:
+        raise FlareError(rc, "flare_logprobs_run_noalloc")
 
 
 def flare_logprobs_run_sharded(plan: PlanStruct, logits, dtype, rows: int, V: int, V_pad: int,

@@ -33,6 +33,8 @@ const char* flare_status_string(int status) {
     case FLARE_ERR_DEVICE: return "device query failed or device is not gfx950";
     case FLARE_ERR_LAUNCH: return "kernel launch failed";
     case FLARE_ERR_UNSUPPORTED_SIZE: return "vocabulary too large for the plan";
+    case FLARE_ERR_SCRATCH_TOO_SMALL:
+      return "the plan's workspace exceeds the 16 MiB static scratch of the no-allocation call";
     default: return "unknown status";
   }
 }
@@ -413,6 +415,22 @@ int flare_logprobs_merge(const flare_logprobs_plan_t* plan, const void* logits, 
                          int32_t* out, void* workspace, void* hip_stream) {
   return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
                     emitted_counts, tokens, nullptr, K, out, workspace, hip_stream, flp::kPhaseMerge);
+}
+
+int flare_logprobs_run_noalloc(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int32_t* emitted_counts,
+                               const int32_t* tokens, int32_t K, int32_t* out, void* hip_stream) {
+  if (!plan) return FLARE_ERR_INVALID_ARGUMENT;
+  if (plan->workspace_bytes > flp::kScratchBytes) return FLARE_ERR_SCRATCH_TOO_SMALL;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return FLARE_ERR_DEVICE;
+  void* ws = nullptr;
+  if (flp::scratch_address(device, &ws) != 0 || !ws) return FLARE_ERR_DEVICE;
+  return run_phases(plan, logits, dtype, rows, V, V_pad, requested, id_counts, ids,
+                    emitted_counts, tokens, nullptr, K, out, ws, hip_stream,
+                    flp::kPhaseReduce | flp::kPhaseMerge);
 }
 
 int flare_logprobs_run_sharded(const flare_logprobs_plan_t* plan, const void* logits,

@@ -115,6 +115,11 @@ constexpr int kPhaseMerge = 2;
 // `score` selects prompt scoring: one row per slot (T = 1), a row is active
 // when its target (tokens[s]) is a vocabulary ID, K = 20, kPromptWords per row.
 int launch(const Params& p, int dtype, bool vector_rows, bool score, int phases, void* stream);
+// The static device scratch of flare_logprobs_run_noalloc: its size, and its
+// address on `device` (the current device), looked up once per device.
+constexpr uint64_t kScratchBytes = 16ull << 20;
+constexpr int kMaxDevices = 64;
+int scratch_address(int device, void** ptr);
 // Shard pass tail and cross-shard merge (flp_kernels.hip); hipError_t as int.
 int launch_shard_finalize(const Params& p, int dtype, void* stream);
 int launch_shard_merge(const Params& p, int dtype, bool vector_rows, void* stream);

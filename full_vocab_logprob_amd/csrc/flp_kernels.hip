@@ -56,6 +56,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "flp_internal.h"
 
 namespace flp {
@@ -1885,6 +1887,28 @@ hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
 }
 
 }  // namespace
+
+// The workspace of flare_logprobs_run_noalloc: a file-scope device array that
+// the library never allocates or frees (each GPU holds its own copy until the
+// process ends).  Host code may not use its name as an address: the address
+// on a device comes from hipGetSymbolAddress with that device current, looked
+// up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int scratch_address(int device, void** ptr) {
+  static std::mutex lock;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices || !ptr) return (int)hipErrorInvalidValue;
+  std::lock_guard<std::mutex> hold(lock);
+  if (!addr[device]) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return 0;
+}
 
 int launch_shard_finalize(const Params& p, int dtype, void* stream) {
   const int64_t rows = (int64_t)p.capacity * p.T;

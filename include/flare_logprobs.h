@@ -70,7 +70,8 @@ enum flare_status {
   FLARE_ERR_PLAN_MISMATCH = 3,    /* run arguments differ from the plan */
   FLARE_ERR_DEVICE = 4,           /* device query failed or not gfx950 */
   FLARE_ERR_LAUNCH = 5,           /* a kernel launch reported an error */
-  FLARE_ERR_UNSUPPORTED_SIZE = 6  /* V beyond what the plan can tile */
+  FLARE_ERR_UNSUPPORTED_SIZE = 6, /* V beyond what the plan can tile */
+  FLARE_ERR_SCRATCH_TOO_SMALL = 7 /* flare_logprobs_run_noalloc: workspace_bytes > 16 MiB */
 };
 
 /*
@@ -290,6 +291,32 @@ int flare_prompt_logprobs_merge(const flare_logprobs_plan_t* plan, const void* l
                                 int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
                                 const int32_t* targets, int32_t* out, void* workspace,
                                 void* hip_stream);
+
+/*
+ * flare_logprobs_run without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It runs the same two kernels on a
+ * file-scope static device array of the library, 16 MiB per GPU, held from
+ * the library's first call on that GPU until the process ends; its address
+ * is looked up once per device (hipGetSymbolAddress) with that device
+ * current.  No allocation, free or memset happens here or in the kernels, and
+ * nothing in the scratch needs clearing: every word a call reads is written
+ * earlier in the same call.
+ *   Arguments: those of flare_logprobs_run (rectangular and unsharded plans),
+ *   minus `workspace`; the call runs on the current device.
+ *   Errors: as flare_logprobs_run, plus FLARE_ERR_SCRATCH_TOO_SMALL, before
+ *   anything is launched, when plan->workspace_bytes exceeds 16 MiB (e.g. a
+ *   1,024-slot x T=4 frame of 262,144 FP32 lanes needs 37 MB), and
+ *   FLARE_ERR_DEVICE when the scratch's address cannot be found.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ *   GPU (other streams, other threads) race and must be ordered by the
+ *   caller.  The L and guard diagnostics of such a call are not readable.
+ */
+int flare_logprobs_run_noalloc(const flare_logprobs_plan_t* plan, const void* logits,
+                               int32_t dtype, int64_t rows, int32_t V, int32_t V_pad,
+                               const int32_t* requested, const int32_t* id_counts,
+                               const int32_t* ids, const int32_t* emitted_counts,
+                               const int32_t* tokens, int32_t K, int32_t* out, void* hip_stream);
 
 /*
  * Vocabulary-sharded reduction on one GPU (Flare generation-logprobs design

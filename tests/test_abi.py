@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(flp):
 
 def test_abi_version_and_status_strings(flp):
     assert flp.flare_logprobs_abi_version() == flp.ABI_VERSION
-    for code in range(7):
+    for code in range(8):
         assert flp.flare_status_string(code) != "unknown status"
     assert flp.flare_status_string(99) == "unknown status"
 
