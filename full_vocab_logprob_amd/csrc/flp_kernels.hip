@@ -14,8 +14,10 @@
 // units (16,384 bf16 or 8,192 FP32 lanes, 32 KiB); workgroup g owns the
 // contiguous unit range [g N / R, (g + 1) N / R), R = grid once N >= 2 grid
 // (fewer units: one or two per range, see range_count), so every workgroup
-// streams the same number of bytes and a range may cross rows.  The units of
-// one row inside one range form a part.
+// streams the same number of bytes and a range may cross rows; when the
+// active rows are few enough, each range is instead one of p equal pieces
+// of a row (see range_plan).  The units of one row inside one range form a
+// part.
 //   Per unit, each thread holds 8 x 16-byte chunks (coalesced dwordx4 loads)
 //   in VGPRs and refills each chunk with the next unit as soon as it is
 //   summed.  Each wave keeps a running (max, sum of exp2) for the part.
@@ -558,6 +560,33 @@ __device__ __forceinline__ bool is_range_start(int x, int n, int grid) {
   return __builtin_floor(g * (double)n / (double)grid) == (double)x;
 }
 
+// Row-aligned ranges.  When the launch holds at least two units per
+// workgroup and cutting every active row into p = grid / rows equal pieces
+// makes no range more than one unit longer than the balanced split's
+// longest, each range is one piece of one row: one part per range, so no
+// range pays two part ends or ends on a one-unit part (the costliest unit,
+// and at the end of a range nothing overlaps it).  Workgroup b takes piece
+// b / rows of row b % rows: the pieces that hold a row's last (partial) unit
+// go to the workgroups dispatched later, which get their first data later.
+constexpr int kRowAlignSlack = 1;
+struct RangePlan {
+  int count;   // ranges of the launch
+  int pieces;  // pieces per row (0: the balanced split of all units)
+};
+__device__ __forceinline__ RangePlan range_plan(int rows, int U, int grid) {
+  const int64_t n = (int64_t)rows * U;
+  if (n < 2 * (int64_t)grid) return RangePlan{range_count(n, grid), 0};
+  const int p = grid / rows;
+  const int64_t longest = (n + grid - 1) / grid;
+  if (p >= 2 && (U + p - 1) / p <= longest + kRowAlignSlack) return RangePlan{rows * p, p};
+  return RangePlan{grid, 0};
+}
+// Whether unit x of a launch over `rows` rows of U units begins a range.
+__device__ __forceinline__ bool starts_range(int x, int rows, int U, const RangePlan& rp) {
+  if (rp.pieces) return is_range_start(x % U, U, rp.pieces);
+  return is_range_start(x, rows * U, rp.count);
+}
+
 // Every lane [lo, hi) of a row whose final key reaches thr, merged into the
 // sorted best 32 in `top`; thr rises to the K-th kept key as it fills.  One
 // 16-byte chunk per lane per step, eight steps' chunks loaded at once.  Keys
@@ -695,12 +724,12 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   int16_t* part_u0 = part_u0_all[wv];
 
   // ---- the row's parts (one lane per unit): a part starts at the row's
-  // first unit and wherever a workgroup's unit range starts, at
-  // floor(g N / R) of the N units of the active rows (the reduction's
-  // partition, recomputed exactly in double precision).
+  // first unit and wherever a workgroup's unit range starts (the
+  // reduction's partition, recomputed exactly: row pieces, or floor(g N / R)
+  // of the N units of the active rows in double precision).
   const int a = before + t;
-  const int ranges = range_count((int64_t)total * U, p.workers);
-  const bool start = lane < U && (lane == 0 || is_range_start(a * U + lane, total * U, ranges));
+  const RangePlan rplan = range_plan(total, U, p.workers);
+  const bool start = lane < U && (lane == 0 || starts_range(a * U + lane, total, U, rplan));
   const uint64_t starts = __ballot(start);
   const int np = __popcll(starts);
   if (start) part_u0[lanes_below(starts)] = (int16_t)lane;
@@ -1236,17 +1265,22 @@ __device__ __forceinline__ int opaque_lane(int lane) {
   return lane;
 }
 
-// Issue priority 3 - q for a workgroup in quarter q of its unit range.  The
-// wave arbiter of a CU favours the oldest waves, so with equal priorities
-// the workgroups dispatched first race through their ranges while the
-// youngest lag and set the end of the launch; lowering the priority as a
-// range is consumed hands issue slots to the workgroups that are behind.
-// The quarter starts are computed once per range (no division per unit).
+// Issue priority of a workgroup as it consumes its unit range.  The wave
+// arbiter of a CU favours the oldest waves, so with equal priorities the
+// workgroups dispatched first race through their ranges while the youngest
+// lag and set the end of the launch; lowering the priority as a range is
+// consumed hands issue slots to the workgroups that are behind.  A range of
+// up to kShortRange units keeps priority 3 until its last three units and
+// then steps down one level per unit (a short range's lag is a unit or two,
+// settled at its end); a longer one steps down by quarters.  The step
+// points are computed once per range (no division per unit).
+constexpr int kShortRange = 16;
 struct Quarters {
   int q1, q2, q3;
 };
 __device__ __forceinline__ Quarters range_quarters(int x0, int x1) {
   const int64_t n = x1 - x0;
+  if (n <= kShortRange) return Quarters{x1 - 3, x1 - 2, x1 - 1};
   return Quarters{x0 + (int)((n + 3) >> 2), x0 + (int)((2 * n + 3) >> 2), x0 + (int)((3 * n + 3) >> 2)};
 }
 __device__ __forceinline__ void progress_priority(int x, const Quarters& q) {
@@ -1287,10 +1321,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     for (int s = tid; s <= p.capacity; s += kBlock) p.slot_rows[s] = prefix[s] & kRowsMask;
   // This workgroup's range of the N < 2^31 units (the host checks N).
   const int64_t N = (int64_t)total * U;
-  const int ranges = range_count(N, p.workers);
-  if ((int)blockIdx.x >= ranges) return;
-  const int x0 = (int)((int64_t)blockIdx.x * N / ranges);
-  const int x1 = (int)(((int64_t)blockIdx.x + 1) * N / ranges);
+  const RangePlan rplan = range_plan(total, U, p.workers);
+  if ((int)blockIdx.x >= rplan.count) return;
+  int x0, x1;
+  if (rplan.pieces) {
+    const int row = (int)blockIdx.x % total, piece = (int)blockIdx.x / total;
+    x0 = row * U + piece * U / rplan.pieces;
+    x1 = row * U + (piece + 1) * U / rplan.pieces;
+  } else {
+    x0 = (int)((int64_t)blockIdx.x * N / rplan.count);
+    x1 = (int)(((int64_t)blockIdx.x + 1) * N / rplan.count);
+  }
   if (x0 >= x1) return;
   const bool short_ranges = N < 2 * (int64_t)p.workers;
 
@@ -1659,8 +1700,8 @@ __global__ __launch_bounds__(kMergeBlock) void shard_finalize_kernel(Params p) {
 
   // The row's parts in this shard's launch, as the merge finds them.
   const int a = before + t;
-  const int ranges = range_count((int64_t)total * U, p.workers);
-  const bool start = lane < U && (lane == 0 || is_range_start(a * U + lane, total * U, ranges));
+  const RangePlan rplan = range_plan(total, U, p.workers);
+  const bool start = lane < U && (lane == 0 || starts_range(a * U + lane, total, U, rplan));
   const uint64_t starts = __ballot(start);
   const int np = __popcll(starts);
   const int u0 = start ? lane : 0;  // lane i < np: first unit of part i, after compaction below
