@@ -37,8 +37,30 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = ("full_vocab_logprob_amd/csrc/flp_kernels.hip",
                   "full_vocab_logprob_amd/csrc/flp_internal.h")
-TRAFFIC_SUMMARIES = {"C3": "profiles/reduce_kernel_speculative_verify_bf16_K20.txt",
-                     "P1": "profiles/reduce_kernel_prompt_scoring_bf16.txt"}
+# The rocprofv3 summary of each workload (kernel trace average and HBM bytes
+# per reduction launch), keyed by the workload's tag (see workload_tag).
+TRAFFIC_SUMMARIES = {
+    "C1": "profiles/reduce_kernel_plain_decode_fp32_K20.txt",
+    "C2": "profiles/reduce_kernel_decode_batch_fp32_K20.txt",
+    "C3": "profiles/reduce_kernel_speculative_verify_bf16_K20.txt",
+    "C3-K0": "profiles/reduce_kernel_speculative_verify_bf16_K0.txt",
+    "C4": "profiles/reduce_kernel_tie_stress_bf16_selected40.txt",
+    "C5": "profiles/reduce_kernel_large_batch_fp32_K20.txt",
+    "C5-K0": "profiles/reduce_kernel_large_batch_fp32_K0.txt",
+    "C5-sel": "profiles/reduce_kernel_large_batch_fp32_selected128.txt",
+    "P1": "profiles/reduce_kernel_prompt_scoring_bf16.txt",
+    "P2": "profiles/reduce_kernel_prompt_scoring_fp32.txt",
+}
+
+
+def workload_tag(config: str, K=None, selected=None) -> str:
+    """The summary key of a generation workload: the configuration, with the
+    K or selected-ID override of a sweep."""
+    if selected == "all":
+        return f"{config}-sel"
+    if K is not None:
+        return f"{config}-K{K}"
+    return config
 
 
 def kernel_source_hash() -> str:
@@ -143,6 +165,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--K", type=int, default=None,
                     help="override the configuration's K (throughput sweeps, e.g. K=0)")
+    ap.add_argument("--selected", default=None, choices=("all",),
+                    help="every slot lists 128 caller-selected IDs (the 128-ID sweep)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--check-rows", type=int, default=4,
@@ -331,6 +355,8 @@ def main():
     spec = synth.CONFIGS[args.config]
     if args.K is not None:
         spec = spec.with_(K=args.K)
+    if args.selected:
+        spec = spec.with_(selected=args.selected)
     bf16 = spec.dtype == synth.BF16
     print(f"[bench] generating {spec.name}: {spec.description}", file=sys.stderr, flush=True)
     w = synth.make(spec)
@@ -498,7 +524,8 @@ def main():
         copy_kernel(dev, args.copy_mib)
 
     res = {
-        "metric": "logprob rows/s and achieved HBM GB/s (% of peak) at V=248,320, T=8, 128 slots",
+        "metric": f"logprob rows/s and achieved HBM GB/s (% of peak) at V={spec.V:,}, T={spec.T}, "
+                  f"{spec.capacity} slots",
         "value": rows_per_s,
         "unit": "rows/s",
         "n_gpus": 1,
@@ -509,16 +536,19 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "fp32",
-        "data": "synthetic (seeded Gumbel logits + 10 peak; garbage rows past each prefix)",
+        "data": f"synthetic, seeded ({spec.description.split(': ', 1)[1]}; rows past each "
+                f"slot's prefix hold NaN/+inf garbage)",
         "config": {"workload": f"{spec.name}: {spec.capacity} slots x T={spec.T} x V={spec.V} "
                                f"{'bf16' if bf16 else 'fp32'}, emitted 1..{spec.T}, K={spec.K}"
                                + (f", packed into {packed_rows} rows" if packed_rows else "")
                                + (", counts and tokens from completion records"
                                   if args.records else "")
-                               + (f", vocabulary in {args.shards} shards" if args.shards else ""),
+                               + (f", vocabulary in {args.shards} shards" if args.shards else "")
+                               + (", 128 selected IDs per slot" if args.selected else ""),
                    "active_rows": active, "capacity": spec.capacity, "T": spec.T, "V": spec.V,
                    "K": spec.K, "copies": len(copies), "oracle_rows_checked": checked},
-        "roofline": roofline(spec.name if args.K is None and not args.records and not args.shards
+        "roofline": roofline(workload_tag(spec.name, args.K, args.selected)
+                             if not args.records and not args.shards
                              else "", "reduce_kernel" if not args.shards
                              else f"reduce_kernel + shard_finalize_kernel, {args.shards} shard passes",
                              algo_bytes, mean_reduce_ms, packed=bool(packed_rows or args.shards)),
