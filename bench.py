@@ -35,6 +35,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+# Calls captured in the timed HIP graph.  Each replay costs a fixed few
+# microseconds of launch (about 6 us for a one-call graph of C1 or C3), so
+# the graph holds a serving loop's worth of calls, cycling the logits copies.
+GRAPH_CALLS = 16
 KERNEL_SOURCES = ("full_vocab_logprob_amd/csrc/flp_kernels.hip",
                   "full_vocab_logprob_amd/csrc/flp_internal.h")
 # The rocprofv3 summary of each workload (kernel trace average and HBM bytes
@@ -240,12 +244,13 @@ def bench_prompt(args):
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         gr = torch.cuda.CUDAGraph()
+        n = GRAPH_CALLS
         with torch.cuda.stream(side):
             with torch.cuda.graph(gr, stream=side):
-                for c in range(len(copies)):
-                    plan.run(copies[c], targets, out, ws)
+                for c in range(n):
+                    plan.run(copies[c % len(copies)], targets, out, ws)
         torch.cuda.synchronize()
-        reps = max(1, args.steps // len(copies))
+        reps = max(1, args.steps // n)
         for _ in range(2):
             gr.replay()
         torch.cuda.synchronize()
@@ -256,10 +261,10 @@ def bench_prompt(args):
             gr.replay()
         g1.record(stream)
         torch.cuda.synchronize()
-        per_call = g0.elapsed_time(g1) / (reps * len(copies))
+        per_call = g0.elapsed_time(g1) / (reps * n)
         del gr
         return {"ms_per_call": per_call, "rows_per_s": w.rows / (per_call / 1e3),
-                "calls": reps * len(copies)}
+                "calls": reps * n, "calls_per_graph": n}
 
     # Warm-up straight into the timed regions; the oracle check of the
     # output comes after them, so the GPU does not idle before timing.
@@ -431,18 +436,19 @@ def main():
             call(sh)
 
     def graph():
-        # The same calls replayed from one HIP graph (one call per logits copy
-        # captured, replayed until about K calls have run).
+        # The same calls replayed from one HIP graph (GRAPH_CALLS calls over the
+        # logits copies captured, replayed until about K calls have run).
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         gr = torch.cuda.CUDAGraph()
+        n = GRAPH_CALLS
         with torch.cuda.stream(side):
             with torch.cuda.graph(gr, stream=side):
-                for c in range(len(copies)):
-                    plan.run(copies[c], tokens, emitted, requested, id_counts, ids, out, ws,
-                             row_offsets=offsets)
+                for c in range(n):
+                    plan.run(copies[c % len(copies)], tokens, emitted, requested, id_counts, ids,
+                             out, ws, row_offsets=offsets)
         torch.cuda.synchronize()
-        reps = max(1, args.steps // len(copies))
+        reps = max(1, args.steps // n)
         for _ in range(2):
             gr.replay()
         torch.cuda.synchronize()
@@ -453,10 +459,10 @@ def main():
             gr.replay()
         g1.record(stream)
         torch.cuda.synchronize()
-        per_call = g0.elapsed_time(g1) / (reps * len(copies))
+        per_call = g0.elapsed_time(g1) / (reps * n)
         del gr
         return {"ms_per_call": per_call, "rows_per_s": active / (per_call / 1e3),
-                "calls": reps * len(copies)}
+                "calls": reps * n, "calls_per_graph": n}
 
     # Warm-up straight into the timed regions; the oracle check of the
     # output comes after them, so the GPU does not idle before timing.
