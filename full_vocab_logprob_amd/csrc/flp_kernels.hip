@@ -518,6 +518,26 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
   }
   return lo;
 }
+// The same slot for a wave-uniform a, from lane-parallel compares instead of
+// a chain of dependent reads: the counts are non-decreasing in s, so the
+// slots whose count is at most a form a prefix.  Lane l tests slot
+// l * stride (stride = ceil(cap / 64)); the last passing sample bounds the
+// slot to the stride slots after it, which a second round tests.
+__device__ __forceinline__ int slot_of_wave(const int* prefix, int cap, int a) {
+  // (the lane index is opaque, so that its addresses are formed here rather
+  // than hoisted out of the unit loop and kept in spilled registers)
+  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(lane));
+  const int stride = (cap + 63) >> 6;
+  const int sc = lane * stride;
+  const int lo = (__popcll(__ballot(sc < cap && (prefix[sc] & kRowsMask) <= a)) - 1) * stride;
+  int n = 0;
+  for (int j = 1; j < stride; j += 64) {
+    const int s = lo + j + lane;
+    n += __popcll(__ballot(j + lane < stride && s < cap && (prefix[s] & kRowsMask) <= a));
+  }
+  return __builtin_amdgcn_readfirstlane(lo + n);
+}
 
 // ==================================================================== merge
 // One wave per row, four rows per workgroup: L from the row's parts in part
@@ -574,11 +594,11 @@ struct RangePlan {
   int pieces;  // pieces per row (0: the balanced split of all units)
 };
 __device__ __forceinline__ RangePlan range_plan(int rows, int U, int grid) {
-  const int64_t n = (int64_t)rows * U;
-  if (n < 2 * (int64_t)grid) return RangePlan{range_count(n, grid), 0};
+  const uint32_t n = (uint32_t)rows * (uint32_t)U;  // below 2^31 (the host checks)
+  if (n < 2u * (uint32_t)grid) return RangePlan{range_count(n, grid), 0};
   const int p = grid / rows;
-  const int64_t longest = (n + grid - 1) / grid;
-  if (p >= 2 && (U + p - 1) / p <= longest + kRowAlignSlack) return RangePlan{rows * p, p};
+  const uint32_t longest = (n + (uint32_t)grid - 1u) / (uint32_t)grid;
+  if (p >= 2 && (uint32_t)((U + p - 1) / p) <= longest + kRowAlignSlack) return RangePlan{rows * p, p};
   return RangePlan{grid, 0};
 }
 // Whether unit x of a launch over `rows` rows of U units begins a range.
@@ -915,7 +935,7 @@ struct StagedRec {
 
 struct ReduceSmem {
   uint64_t pool[kWaves][kCandBuf];       // per-wave candidate buffers
-  uint64_t flush_keys[2][kWaves][kKeep]; // a part's sorted best 32 per wave, by part parity
+  uint64_t chain_keys[2][kKeep];         // a part's best 32 over the waves arrived so far, by parity
   u32x4 stash[kWaves][kStash];           // hot chunks of the unit being reduced
   int16_t stash_off[kWaves][kStash];     // their chunk index c * 64 + lane
   uint64_t qbar[kWaves];                 // each wave's published ceil(K/4)-th key (see pub_key)
@@ -927,6 +947,7 @@ struct ReduceSmem {
   int wcount[2][kWaves];                 // the lanes holding it (FP32)
   float wnext2[2][kWaves];               // and the next larger logit (FP32)
   int arrive[2];                         // waves that flushed the part of this parity
+  int chain[2];                          // waves whose lists are folded into chain_keys
   int merged;                            // parts of the range merged into records
   int n_staged;                          // records staged in `staged`
   StagedRec staged[kRecStage];
@@ -958,7 +979,7 @@ __device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, in
   UnitPos q;
   q.a = x / p.units;
   q.u = x - q.a * p.units;
-  q.s = __builtin_amdgcn_readfirstlane(slot_of(prefix, p.capacity, q.a));
+  q.s = slot_of_wave(prefix, p.capacity, q.a);
   const int t = q.a - (prefix[q.s] & kRowsMask);
   q.row = __builtin_amdgcn_readfirstlane(q.s * p.T + t);
   const int lrow =
@@ -1308,11 +1329,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   __shared__ ReduceSmem sh;
   extern __shared__ int prefix[];
 
+  // The set-up runs at the priority of a range's first units: workgroups
+  // dispatched later compete on equal terms with the earlier ones, which are
+  // already streaming, to issue their first loads.
+  __builtin_amdgcn_s_setprio(3);
   const int tid = threadIdx.x, lane_id = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = p.V, U = p.units;
   if (tid < kWaves) sh.qbar[tid] = 0ull;  // ordered by the barriers below
   if (tid < 2) sh.arrive[tid] = 0;
+  if (tid < 2) sh.chain[tid] = 0;
   if (tid == 0) sh.merged = 0;
   if (tid == 0) sh.n_staged = 0;
   const int total = build_prefix<kWaves, SCORE>(p, prefix, sh.scan);
@@ -1320,7 +1346,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   if (blockIdx.x == 0)
     for (int s = tid; s <= p.capacity; s += kBlock) p.slot_rows[s] = prefix[s] & kRowsMask;
   // This workgroup's range of the N < 2^31 units (the host checks N).
-  const int64_t N = (int64_t)total * U;
+  const int N = total * U;
   const RangePlan rplan = range_plan(total, U, p.workers);
   if ((int)blockIdx.x >= rplan.count) return;
   int x0, x1;
@@ -1329,11 +1355,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     x0 = row * U + piece * U / rplan.pieces;
     x1 = row * U + (piece + 1) * U / rplan.pieces;
   } else {
-    x0 = (int)((int64_t)blockIdx.x * N / rplan.count);
-    x1 = (int)(((int64_t)blockIdx.x + 1) * N / rplan.count);
+    // floor(b N / count) in double precision: b N < 2^53 is exact, and a
+    // quotient that is not an integer lies at least 1 / count from one, far
+    // beyond the division's rounding error, so the floor is exact.
+    x0 = (int)__builtin_floor((double)blockIdx.x * (double)N / (double)rplan.count);
+    x1 = (int)__builtin_floor(((double)blockIdx.x + 1.0) * (double)N / (double)rplan.count);
   }
   if (x0 >= x1) return;
-  const bool short_ranges = N < 2 * (int64_t)p.workers;
+  const bool short_ranges = N < 2 * p.workers;
 
   UnitPos cur = locate<DT>(p, prefix, x0);
   int part_u0 = cur.u;
@@ -1565,29 +1594,38 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
           }
         }
       }
-      if (natural && lane < kKeep) sh.flush_keys[b][w][lane] = best.top;
       // Every key this wave kept is at or above its first-unit threshold, so
       // once it holds K of them the lanes below the threshold rank below its
       // K-th key, which the part's K-th kept key bounds: no cut of its own.
       if (lane == 0) sh.flush_cut[b][w] = natural && best.n < K ? cut : 0ull;
-      // The last wave to arrive merges the four shares into the record.
+      // The last wave to arrive writes the record.
       int old = 0;
       if (lane == 0)
         old = __hip_atomic_fetch_add(&sh.arrive[b], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
       old = __builtin_amdgcn_readfirstlane(old);
+      // The waves fold their lists into one in the order they arrive, each
+      // merging its own into the fold of the earlier ones: the best 32 of a
+      // set of distinct keys does not depend on the order, and the last wave
+      // merges one list instead of all four.
+      uint64_t top = 0ull;
+      if (natural) {
+        top = lane < kKeep ? best.top : 0ull;
+        if (old > 0) {
+          while (__hip_atomic_load(&sh.chain[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < old)
+            __builtin_amdgcn_s_sleep(1);
+          top = merge_top32(top, lane < kKeep ? sh.chain_keys[b][lane] : 0ull, lane);
+        }
+        if (old < kWaves - 1) {
+          if (lane < kKeep) sh.chain_keys[b][lane] = top;
+          if (lane == 0)
+            __hip_atomic_store(&sh.chain[b], old + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
       if (old == kWaves - 1) {
         const int slot = __builtin_amdgcn_readfirstlane(sh.n_staged);
         StagedRec* sr = &sh.staged[slot];
         PartRecord* rec = &sr->rec;
-        uint64_t top = 0ull;
-        int held = 0;
-        if (natural) {
-          top = lane < kKeep ? sh.flush_keys[b][0][lane] : 0ull;
-#pragma unroll
-          for (int i = 1; i < kWaves; ++i)
-            top = merge_top32(top, lane < kKeep ? sh.flush_keys[b][i][lane] : 0ull, lane);
-          held = __popcll(__ballot(lane < kKeep && top != 0ull));
-        }
+        const int held = natural ? __popcll(__ballot(lane < kKeep && top != 0ull)) : 0;
         if (natural && lane < kKeep) rec->keys[lane] = top;
         // Every lane the part dropped has a key at most the part's K-th kept
         // key or one of its waves' cuts.
@@ -1625,6 +1663,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
           sr->natural = natural;
           sh.n_staged = (slot + 1 == kRecStage || !has_next) ? 0 : slot + 1;
           sh.arrive[b] = 0;
+          sh.chain[b] = 0;
           __hip_atomic_store(&sh.merged, part_seq + 1, __ATOMIC_RELEASE,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
         }
