@@ -465,6 +465,17 @@ __device__ __forceinline__ int slot_word(const Params& p, int s) {
   return rows | (n > 0 ? kSelBit : 0);
 }
 
+// Inclusive sum over lanes 0..lane of the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // prefix[s] = active rows of slots before s (with slot s's selection bit);
 // prefix[capacity] = total.  All NW waves of the workgroup take part; `scan`
 // is NW ints of LDS.
@@ -484,13 +495,11 @@ __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
     if (!SCORE && p.row_offsets) phys[s] = p.row_offsets[s];
     local += c & kRowsMask;
   }
-  // exclusive scan of `local` over the block
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  // exclusive scan of `local` over the block: within each wave an inclusive
+  // scan by DPP (shifts by 1, 2, 4, 8 inside each row of 16 lanes, zeros
+  // shifted in, then row 0's and row 1's last lanes broadcast into the rows
+  // after them), no LDS round trips
+  int incl = wave_incl_scan(local);
   if (lane == 63) scan[w] = incl;
   __syncthreads();
   int run = incl - local, total = 0;
@@ -523,11 +532,7 @@ __device__ __forceinline__ int slot_of(const int* prefix, int cap, int a) {
 // slots whose count is at most a form a prefix.  Lane l tests slot
 // l * stride (stride = ceil(cap / 64)); the last passing sample bounds the
 // slot to the stride slots after it, which a second round tests.
-__device__ __forceinline__ int slot_of_wave(const int* prefix, int cap, int a) {
-  // (the lane index is opaque, so that its addresses are formed here rather
-  // than hoisted out of the unit loop and kept in spilled registers)
-  int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  asm volatile("" : "+v"(lane));
+__device__ __forceinline__ int slot_of_wave(const int* prefix, int cap, int a, int lane) {
   const int stride = (cap + 63) >> 6;
   const int sc = lane * stride;
   const int lo = (__popcll(__ballot(sc < cap && (prefix[sc] & kRowsMask) <= a)) - 1) * stride;
@@ -975,11 +980,11 @@ struct UnitPos {
 };
 
 template <int DT>
-__device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, int x) {
+__device__ __forceinline__ UnitPos locate(const Params& p, const int* prefix, int x, int lane) {
   UnitPos q;
   q.a = x / p.units;
   q.u = x - q.a * p.units;
-  q.s = slot_of_wave(prefix, p.capacity, q.a);
+  q.s = slot_of_wave(prefix, p.capacity, q.a, lane);
   const int t = q.a - (prefix[q.s] & kRowsMask);
   q.row = __builtin_amdgcn_readfirstlane(q.s * p.T + t);
   const int lrow =
@@ -1364,7 +1369,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   if (x0 >= x1) return;
   const bool short_ranges = N < 2 * p.workers;
 
-  UnitPos cur = locate<DT>(p, prefix, x0);
+  UnitPos cur = locate<DT>(p, prefix, x0, lane_id);
   int part_u0 = cur.u;
   const int row_bytes = (int)(p.V_pad * E::kBytes);
   u32x4 raw[kChunks];
@@ -1419,7 +1424,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     UnitPos nxt = cur;
     if (has_next) {
       if (cur.u + 1 < U) nxt.u = cur.u + 1;
-      else nxt = locate<DT>(p, prefix, x + 1);
+      else nxt = locate<DT>(p, prefix, x + 1, lane);
     }
     const bool part_ends = !has_next || nxt.a != cur.a;
     const bool part_starts = cur.u == part_u0;
@@ -1625,20 +1630,37 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         const int slot = __builtin_amdgcn_readfirstlane(sh.n_staged);
         StagedRec* sr = &sh.staged[slot];
         PartRecord* rec = &sr->rec;
+        // The range's last part is written straight from registers (nothing
+        // streams after it); earlier parts are staged in LDS and written in
+        // batches, so that no store sits among the stream's loads.
+        const bool direct = !SCORE && !has_next;
         const int held = natural ? __popcll(__ballot(lane < kKeep && top != 0ull)) : 0;
-        if (natural && lane < kKeep) rec->keys[lane] = top;
+        if (natural && lane < kKeep && !direct) rec->keys[lane] = top;
+        // The waves' statistics, lane i < kWaves reading wave i's, all loads
+        // at once; S adds the waves' terms in wave order as a sum in one lane
+        // would.
+        const float wmv = lane < kWaves ? sh.wm[b][lane] : kNegInf;
+        const float wsv = lane < kWaves ? sh.ws[b][lane] : 0.0f;
+        const uint64_t wcv = lane < kWaves ? sh.flush_cut[b][lane] : 0ull;
+        float M = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wmv), 0));
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i)
+          M = fmaxf(M, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wmv), i)));
+        const float term =
+            M != kNegInf && wmv != kNegInf ? wsv * __builtin_amdgcn_exp2f((wmv - M) * kLog2e) : 0.0f;
+        float S = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i)
+          S += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(term), i));
         // Every lane the part dropped has a key at most the part's K-th kept
         // key or one of its waves' cuts.
         uint64_t pcut = held >= K ? readlane64(top, K - 1) : 0ull;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          const uint64_t c = readlane64(wcv, i);
+          pcut = c > pcut ? c : pcut;
+        }
         if (lane == 0) {
-          float M = sh.wm[b][0];
-          for (int i = 1; i < kWaves; ++i) M = fmaxf(M, sh.wm[b][i]);
-          float S = 0.0f;
-          if (M != kNegInf)
-            for (int i = 0; i < kWaves; ++i)
-              if (sh.wm[b][i] != kNegInf)
-                S += sh.ws[b][i] * __builtin_amdgcn_exp2f((sh.wm[b][i] - M) * kLog2e);
-          for (int i = 0; i < kWaves; ++i) pcut = sh.flush_cut[b][i] > pcut ? sh.flush_cut[b][i] : pcut;
           int na = 0, nc = 0;
           float nx = __builtin_huge_valf(), n2 = __builtin_huge_valf();
           if (SCORE) {
@@ -1654,13 +1676,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
             // carries the next larger value and the count at the minimum.
             if (DT == 0) rec->keys[kKeep - 1] = ((uint64_t)__float_as_uint(n2) << 32) | (uint32_t)nc;
           }
-          rec->m = M;
-          rec->s = S;
-          rec->above = na;
-          rec->next_above = nx;
-          rec->cut = pcut;
-          sr->dst = cur.row * U + part_u0;
-          sr->natural = natural;
+          if (!direct) {
+            rec->m = M;
+            rec->s = S;
+            rec->above = na;
+            rec->next_above = nx;
+            rec->cut = pcut;
+            sr->dst = cur.row * U + part_u0;
+            sr->natural = natural;
+          }
           sh.n_staged = (slot + 1 == kRecStage || !has_next) ? 0 : slot + 1;
           sh.arrive[b] = 0;
           sh.chain[b] = 0;
@@ -1671,13 +1695,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         // of the range.
         if (slot + 1 == kRecStage || !has_next) {
           wave_sync();
-          for (int r = 0; r <= slot; ++r) {
+          const int staged = direct ? slot : slot + 1;
+          for (int r = 0; r < staged; ++r) {
             const StagedRec& s = sh.staged[r];
             const int words = __builtin_amdgcn_readfirstlane(s.natural) ? 3 + kKeep : 3;
             if (lane < words)
               ((uint64_t*)(p.records + __builtin_amdgcn_readfirstlane(s.dst)))[lane] =
                   ((const uint64_t*)&s.rec)[lane];
           }
+        }
+        if (direct) {
+          // Header words (m, s), (above, next_above), cut; then the kept keys.
+          uint64_t* g = (uint64_t*)(p.records + (cur.row * U + part_u0));
+          const uint64_t hdr =
+              lane == 0 ? ((uint64_t)__float_as_uint(S) << 32) | __float_as_uint(M)
+                        : (lane == 1 ? (uint64_t)__float_as_uint(__builtin_huge_valf()) << 32 : pcut);
+          if (lane < 3) g[lane] = hdr;
+          if (natural && lane < kKeep) g[3 + lane] = top;
         }
       }
       ++part_seq;
