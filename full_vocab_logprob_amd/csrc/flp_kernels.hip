@@ -332,6 +332,22 @@ __device__ __forceinline__ uint64_t sort_halves_desc(uint64_t k, int lane) {
   return bitonic_merge_desc(lane < 32 ? k : mirrored, lane);
 }
 
+// The same for two independent lists at once (one check of both, and the
+// two networks' steps interleave).
+__device__ __forceinline__ void sort_halves_desc2(uint64_t& ka, uint64_t& kb, int lane) {
+  const uint64_t pa = wave_shr1_64(ka), pb = wave_shr1_64(kb);
+  const bool out_of_order = (lane & 31) != 0 && (pa < ka || pb < kb);
+  if (__ballot(out_of_order) != 0ull) {
+    ka = sort64_desc(ka, lane);
+    kb = sort64_desc(kb, lane);
+    return;
+  }
+  const uint64_t ma = xlane64<16>(xlane64<15>(ka, lane), lane);
+  const uint64_t mb = xlane64<16>(xlane64<15>(kb, lane), lane);
+  ka = bitonic_merge_desc(lane < 32 ? ka : ma, lane);
+  kb = bitonic_merge_desc(lane < 32 ? kb : mb, lane);
+}
+
 // Lanes 0..31 of the result hold the best 32 of {top[0..32), list[0..64)}
 // sorted descending, given `top` sorted in lanes 0..31 and `list` sorted.
 __device__ __forceinline__ uint64_t merge_top32(uint64_t top, uint64_t list, int lane) {
@@ -711,15 +727,25 @@ __device__ __forceinline__ int count_above(const char* rowp, int lo, int hi, flo
 // r(x_t) exactly those lanes tie and are taken off; otherwise (and for bf16,
 // whose spacing makes such ties rare) the part is counted again lane by lane
 // with reported values.
-template <int DT, bool VEC, bool SCORE>
+//
+// WIDE: one row per workgroup, for launches whose rows hold many parts
+// (short unit ranges).  The four waves read the row's words alike; wave w
+// re-keys, sorts and merges the part pairs w, w + 4, ... and wave 0 merges
+// the four lists and writes the row.  A row of at most four parts is merged
+// by wave 0 alone, as in the one-wave layout.
+template <int DT, bool VEC, bool SCORE, bool WIDE>
 __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   using E = Elem<DT>;
   constexpr int kUnitElems = kUnitThreads * kChunks * E::kPer;
+  constexpr int kWidePairs = (kMaxUnits / 2 + kMergeWaves - 1) / kMergeWaves;  // pairs per wave
   __shared__ int16_t part_u0_all[kMergeWaves][kMaxUnits + 1];
   __shared__ uint64_t pair_keys[kMergeWaves][kLdsPairs][64];
+  __shared__ uint64_t wide_lists[WIDE ? kMergeWaves : 1][kKeep];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int row = (int)blockIdx.x * kMergeWaves + wv;
+  const int row = WIDE ? (int)blockIdx.x : (int)blockIdx.x * kMergeWaves + wv;
+  // The wave that writes the row's words (every wave in the one-wave layout).
+  const bool lead = !WIDE || wv == 0;
   if (row >= p.capacity * p.T) return;
   const int s = row / p.T, t = row - s * p.T;
   // Every input word this row needs, loaded at once (the row counts are
@@ -733,7 +759,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   int32_t* out = p.out + (int64_t)row * (SCORE ? kPromptWords : p.row_words);
   if (SCORE && !(tok >= 0 && tok < V)) {
     // [-1, NaN, rank 0, then (-1, NaN) twenty times]
-    if (lane < kPromptWords)
+    if (lead && lane < kPromptWords)
       out[lane] = lane == 2 ? 0 : ((lane == 0 || (lane >= 3 && (lane & 1))) ? -1 : (int32_t)kNanBits);
     return;
   }
@@ -789,7 +815,15 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       !extra_slot && (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
   const uint64_t raw1 =
       !extra_slot && 2 + (lane >> 5) < np ? rec[part_u0[2 + (lane >> 5)]].keys[lane & 31] : 0ull;
-  if (natural && np > 4) {
+  // WIDE rows of more than four parts: this wave's pairs, loads all in flight.
+  const bool wide = WIDE && natural && np > 4;
+  uint64_t wraw[WIDE ? kWidePairs : 1];
+#pragma unroll
+  for (int i = 0; i < (WIDE ? kWidePairs : 1); ++i) {
+    const int part = 2 * (wv + i * kMergeWaves) + (lane >> 5);
+    wraw[i] = wide && !extra_slot && part < np ? rec[part_u0[part]].keys[lane & 31] : 0ull;
+  }
+  if (natural && np > 4 && !wide) {
     // All loads in flight at once: a row of many parts pays one round trip.
     uint64_t pre[kLdsPairs];
 #pragma unroll
@@ -819,7 +853,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   float term = 0.0f;
   if (lane < np && pm != kNegInf) term = ps * __builtin_amdgcn_exp2f((pm - M) * kLog2e);
   const float L = M + logf(wave_sum(term, lane));
-  if (lane == 0) {
+  if (lead && lane == 0) {
     p.lse[row] = L;
     out[0] = tok;
     out[1] = (int32_t)(tok >= 0 && tok < V ? __float_as_uint(reported(x_tok, L)) : kNanBits);
@@ -834,7 +868,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       tie = false;
     }
     uint64_t ties = __ballot(tie);
-    if (lane == 0) p.guard[row] = __popcll(ties);
+    if (lead && lane == 0) p.guard[row] = __popcll(ties);
     while (ties != 0ull) {
       const int part = __builtin_ctzll(ties);
       ties &= ties - 1ull;
@@ -845,34 +879,68 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       if (lane == part) p_above = exact;
     }
     const int greater = wave_sum_i32(lane < np ? p_above : 0, lane);
-    if (lane == 0) out[2] = 1 + greater;
+    if (lead && lane == 0) out[2] = 1 + greater;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int j = lane + 64 * h;
-    if (!SCORE && j < n_sel) {
+    if (!SCORE && lead && j < n_sel) {
       const uint32_t bits = sel_id[h] >= 0 && sel_id[h] < V ? __float_as_uint(reported(x_sel[h], L))
                                                             : kNanBits;
       *(int2*)(out + 2 + 2 * j) = make_int2(sel_id[h], (int32_t)bits);
     }
   }
   if (!natural) {
-    if (!SCORE && lane == 0) p.guard[row] = 0;
+    if (!SCORE && lead && lane == 0) p.guard[row] = 0;
     return;
   }
 
   // ---- kept candidates re-keyed by F, two parts (64 keys) per step
   const int K = p.K;
   const int Keff = K < V ? K : V;
-  uint64_t top = sort_halves_desc(raw0 != 0ull ? final_key(raw0, L) : 0ull, lane);
-  if (np > 2)
-    top = merge_top32(top, sort_halves_desc(raw1 != 0ull ? final_key(raw1, L) : 0ull, lane), lane);
-  for (int pb = 4; pb < np; pb += 2) {
-    const int part = pb + (lane >> 5);
-    uint64_t raw = 0ull;
-    if (pb < 4 + 2 * kLdsPairs) raw = pair_keys[wv][(pb - 4) >> 1][lane];
-    else if (!extra_slot && part < np) raw = rec[part_u0[part]].keys[lane & 31];
-    top = merge_top32(top, sort_halves_desc(raw != 0ull ? final_key(raw, L) : 0ull, lane), lane);
+  // Two independent chains (pairs 0, 2, 4, ... and 1, 3, 5, ...) merged at
+  // the end, so that a row of many parts pays half the dependent steps.
+  uint64_t top;
+  if (wide) {
+    uint64_t tw = 0ull;
+#pragma unroll
+    for (int i = 0; i < kWidePairs; ++i) {
+      if (2 * (wv + i * kMergeWaves) >= np) break;
+      const uint64_t sk = sort_halves_desc(wraw[i] != 0ull ? final_key(wraw[i], L) : 0ull, lane);
+      tw = i == 0 ? sk : merge_top32(tw, sk, lane);
+    }
+    if (lane < kKeep) wide_lists[WIDE ? wv : 0][lane] = tw;
+    __syncthreads();
+    if (wv != 0) return;
+    top = lane < kKeep ? wide_lists[0][lane] : 0ull;
+#pragma unroll
+    for (int i = 1; i < kMergeWaves; ++i)
+      top = merge_top32(top, lane < kKeep ? wide_lists[WIDE ? i : 0][lane] : 0ull, lane);
+  } else if (!lead) {
+    return;
+  } else if (np <= 2) {
+    top = sort_halves_desc(raw0 != 0ull ? final_key(raw0, L) : 0ull, lane);
+  } else {
+    uint64_t ta = raw0 != 0ull ? final_key(raw0, L) : 0ull;
+    uint64_t tb = raw1 != 0ull ? final_key(raw1, L) : 0ull;
+    sort_halves_desc2(ta, tb, lane);
+    for (int pb = 4; pb < np; pb += 4) {
+      uint64_t r[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = pb + 2 * h;
+        const int part = q + (lane >> 5);
+        r[h] = 0ull;
+        if (q < 4 + 2 * kLdsPairs) r[h] = q < np ? pair_keys[wv][(q - 4) >> 1][lane] : 0ull;
+        else if (!extra_slot && part < np) r[h] = rec[part_u0[part]].keys[lane & 31];
+      }
+      uint64_t ka = r[0] != 0ull ? final_key(r[0], L) : 0ull;
+      uint64_t kb = r[1] != 0ull ? final_key(r[1], L) : 0ull;
+      sort_halves_desc2(ka, kb, lane);
+      ta = merge_top32(ta, ka, lane);
+      tb = merge_top32(tb, kb, lane);
+    }
+    top = merge_top32(ta, tb, lane);
   }
   // ---- guard, one lane per part
   const uint64_t FK = readlane64(top, Keff - 1);
@@ -1984,6 +2052,18 @@ __global__ __launch_bounds__(kMergeBlock) void shard_merge_kernel(Params p) {
   }
 }
 
+// Whether the merge takes four waves per row: when the launch's unit ranges
+// are short enough that a row of the frame, every row active, could span
+// more than four parts (ranges of at least n units start at most
+// ceil((U - 1) / n) + 1 parts in a row of U units).  Fewer active rows only
+// shorten the ranges further; the one-wave layout merges any row, only more
+// slowly.
+bool wide_merge(const Params& p) {
+  const int64_t n = (int64_t)p.capacity * p.T * p.units;
+  const int64_t per = n < 2 * (int64_t)p.workers ? (n > p.workers ? 2 : 1) : n / p.workers;
+  return (p.units - 1 + per - 1) / per + 1 > 4;
+}
+
 template <int DT, bool VEC, bool SCORE>
 hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
   if (phases & kPhaseReduce) {
@@ -1995,8 +2075,11 @@ hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
   }
   if (!(phases & kPhaseMerge)) return hipSuccess;
   const int64_t rows = (int64_t)p.capacity * p.T;
-  hipLaunchKernelGGL((merge_kernel<DT, VEC, SCORE>), dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)),
-                     dim3(kMergeBlock), 0, st, p);
+  if (wide_merge(p))
+    hipLaunchKernelGGL((merge_kernel<DT, VEC, SCORE, true>), dim3((uint32_t)rows), dim3(kMergeBlock), 0, st, p);
+  else
+    hipLaunchKernelGGL((merge_kernel<DT, VEC, SCORE, false>),
+                       dim3((uint32_t)((rows + kMergeWaves - 1) / kMergeWaves)), dim3(kMergeBlock), 0, st, p);
   return hipGetLastError();
 }
 
