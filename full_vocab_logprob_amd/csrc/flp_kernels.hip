@@ -30,14 +30,16 @@
 //   the bar is the largest of that value, the wave's own K-th best key and
 //   the smallest of the four waves' published ceil(K / 4)-th best keys.
 //   Compaction sorts 64-key lists in registers.  At the end of a part the
-//   last wave to arrive merges the four waves' sorted best 32 into the part
-//   record (m, s, best 32 raw keys, and a cut bounding every key the part
-//   dropped), staged in LDS and written when the range ends.
+//   waves fold their sorted best 32 into one as they arrive, and the last
+//   one writes the part record (m, s, best 32 raw keys, and a cut bounding
+//   every key the part dropped), staged in LDS and written when the stage
+//   fills or the range ends.
 //
-// merge_kernel: one wave per row merges the row's part records: L from
-// the parts in part order, the chosen and selected gathers, and the natural
-// top K re-keyed by the reported value fl32(x - L), with an exactness guard
-// that rescans a part when the raw order it kept could differ from the final
+// merge_kernel: one wave per row (four per row when the launch's ranges are
+// short and rows hold many parts) merges the row's part records: L from the
+// parts in part order, the chosen and selected gathers, and the natural top
+// K re-keyed by the reported value fl32(x - L), with an exactness guard that
+// rescans a part when the raw order it kept could differ from the final
 // order.
 //
 // The pages' own scheme ranks normalized values in a second pass over the
