@@ -611,22 +611,36 @@ __device__ __forceinline__ bool is_range_start(int x, int n, int grid) {
 // and at the end of a range nothing overlaps it).  Workgroup b takes piece
 // b / rows of row b % rows: the pieces that hold a row's last (partial) unit
 // go to the workgroups dispatched later, which get their first data later.
+// When p pieces per row would leave at least a sixteenth of the grid idle
+// (grid - p rows workgroups), the last grid - p rows rows are cut into p + 1
+// pieces instead, the extra pieces going to the last workgroups: every
+// workgroup streams, and the shorter pieces go to the workgroups dispatched
+// last.  (A few idle workgroups are not worth the extra parts and merge
+// work.)
 constexpr int kRowAlignSlack = 1;
 struct RangePlan {
   int count;   // ranges of the launch
   int pieces;  // pieces per row (0: the balanced split of all units)
+  int extra;   // the last `extra` rows are cut into pieces + 1
 };
 __device__ __forceinline__ RangePlan range_plan(int rows, int U, int grid) {
   const uint32_t n = (uint32_t)rows * (uint32_t)U;  // below 2^31 (the host checks)
-  if (n < 2u * (uint32_t)grid) return RangePlan{range_count(n, grid), 0};
+  if (n < 2u * (uint32_t)grid) return RangePlan{range_count(n, grid), 0, 0};
   const int p = grid / rows;
   const uint32_t longest = (n + (uint32_t)grid - 1u) / (uint32_t)grid;
-  if (p >= 2 && (uint32_t)((U + p - 1) / p) <= longest + kRowAlignSlack) return RangePlan{rows * p, p};
-  return RangePlan{grid, 0};
+  if (p >= 2 && (uint32_t)((U + p - 1) / p) <= longest + kRowAlignSlack) {
+    const int idle = grid - rows * p;
+    const int extra = U >= p + 1 && 16 * idle >= grid ? idle : 0;
+    return RangePlan{rows * p + extra, p, extra};
+  }
+  return RangePlan{grid, 0, 0};
 }
 // Whether unit x of a launch over `rows` rows of U units begins a range.
 __device__ __forceinline__ bool starts_range(int x, int rows, int U, const RangePlan& rp) {
-  if (rp.pieces) return is_range_start(x % U, U, rp.pieces);
+  if (rp.pieces) {
+    const int a = x / U;
+    return is_range_start(x - a * U, U, rp.pieces + (a >= rows - rp.extra ? 1 : 0));
+  }
   return is_range_start(x, rows * U, rp.count);
 }
 
@@ -1426,9 +1440,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   if ((int)blockIdx.x >= rplan.count) return;
   int x0, x1;
   if (rplan.pieces) {
-    const int row = (int)blockIdx.x % total, piece = (int)blockIdx.x / total;
-    x0 = row * U + piece * U / rplan.pieces;
-    x1 = row * U + (piece + 1) * U / rplan.pieces;
+    const int b = (int)blockIdx.x;
+    int row, piece;
+    if (b < total * rplan.pieces) {
+      row = b % total;
+      piece = b / total;
+    } else {
+      row = total - rplan.extra + (b - total * rplan.pieces);
+      piece = rplan.pieces;
+    }
+    const int q = rplan.pieces + (row >= total - rplan.extra ? 1 : 0);
+    x0 = row * U + piece * U / q;
+    x1 = row * U + (piece + 1) * U / q;
   } else {
     // floor(b N / count) in double precision: b N < 2^53 is exact, and a
     // quotient that is not an integer lies at least 1 / count from one, far

@@ -95,6 +95,26 @@ def test_many_ranges_per_row(oracle_handle, dtype):
     full_compare(oracle_handle, spec)
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP32], ids=["bf16", "fp32"])
+def test_row_pieces_with_extra_pieces(oracle_handle, dtype):
+    # About 500 active rows of 8 units: two pieces per row would leave about
+    # 270 workgroups idle, so the partition cuts the last rows into three
+    # pieces (the extra pieces go to the last workgroups).  Every row is
+    # compared with the oracle.
+    per = 16384 if dtype == synth.BF16 else 8192
+    spec = synth.CONFIGS["C3"].with_(capacity=112, T=8, V=8 * per - 5, V_pad=8 * per,
+                                     dtype=dtype, seed=93)
+    w = synth.make(spec)
+    rows = int(w.active_mask().sum())
+    grid = int(H.make_plan(spec).raw.grid)
+    p = grid // rows
+    idle = grid - p * rows
+    longest = -(-rows * 8 // grid)
+    assert rows * 8 >= 2 * grid and p >= 2 and -(-8 // p) <= longest + 1, (rows, grid)
+    assert 16 * idle >= grid, (rows, grid)
+    full_compare(oracle_handle, spec)
+
+
 def full_size_all_rows(o, spec):
     """The configuration at its full size, in the launch configuration the
     bench times, every active row compared with the oracle."""
