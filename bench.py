@@ -38,7 +38,16 @@ PEAK_HBM_GBPS = 8000.0
 # Calls captured in the timed HIP graph.  Each replay costs a fixed few
 # microseconds of launch (about 6 us for a one-call graph of C1 or C3), so
 # the graph holds a serving loop's worth of calls, cycling the logits copies.
-GRAPH_CALLS = 16
+GRAPH_CALLS = 32
+# Calls in each diagnostic region (the reduction launches alone, the merge
+# launches alone, the graph replay): at least this many, so that their
+# averages describe a warm GPU whatever --steps is.
+DIAG_CALLS = 200
+# Whole calls the GPU has run before the diagnostic regions start: when the
+# warm-up and the timed steps were fewer, untimed calls make up the rest.
+# The first few hundred calls after an idle GPU run slower while it ramps up,
+# and the diagnostic regions describe the kernels on a warm GPU.
+DIAG_WARM_CALLS = 800
 KERNEL_SOURCES = ("full_vocab_logprob_amd/csrc/flp_kernels.hip",
                   "full_vocab_logprob_amd/csrc/flp_internal.h")
 # The rocprofv3 summary of each workload (kernel trace average and HBM bytes
@@ -113,10 +122,12 @@ def host_cpu() -> str:
 
 def timed_regions(step, K: int, warmup: int, stream, graph=None):
     """The timed part of a bench, after `warmup` untimed whole calls:
-    region 1, K whole calls back to back (the throughput); region 2, the
-    same K calls' reduction launches alone, back to back (the reduction's
-    mean duration: the roofline); region 3, their merge launches alone;
-    then `graph()`, if given, for the graph-replay rate.  Every region is
+    region 1, K whole calls back to back (the throughput); then, once the GPU
+    has run DIAG_WARM_CALLS whole calls in all, region 2, the same calls'
+    reduction launches alone, back to back, max(K, DIAG_CALLS) of them (the
+    reduction's mean duration: the roofline); region 3, as many merge
+    launches alone; then `graph()`, if given, for the graph-replay rate.
+    Every region is
     bracketed by a synchronization and HIP events at its two ends only, on
     the launch stream, so no event sits between two launches."""
     import torch
@@ -124,21 +135,23 @@ def timed_regions(step, K: int, warmup: int, stream, graph=None):
     for i in range(warmup):
         step(i)
 
-    def region(phase):
+    def region(phase, n):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         e0.record(stream)
-        for i in range(K):
+        for i in range(n):
             step(warmup + i, phase)
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / K, time.perf_counter() - w0
+        return e0.elapsed_time(e1) / n, time.perf_counter() - w0
 
-    ms_per_step, wall = region("all")
-    reduce_ms, _ = region("reduce")
-    merge_ms, _ = region("merge")
+    ms_per_step, wall = region("all", K)
+    for i in range(max(0, DIAG_WARM_CALLS - warmup - K)):
+        step(i)
+    reduce_ms, _ = region("reduce", max(K, DIAG_CALLS))
+    merge_ms, _ = region("merge", max(K, DIAG_CALLS))
     g = graph() if graph is not None else None
     if reduce_ms > ms_per_step:
         print(f"[bench] warning: reduction launches took {reduce_ms * 1e3:.1f} us each, more "
@@ -250,7 +263,7 @@ def bench_prompt(args):
                 for c in range(n):
                     plan.run(copies[c % len(copies)], targets, out, ws)
         torch.cuda.synchronize()
-        reps = max(1, args.steps // n)
+        reps = max(1, max(args.steps, DIAG_CALLS) // n)
         for _ in range(2):
             gr.replay()
         torch.cuda.synchronize()
@@ -326,6 +339,8 @@ def bench_prompt(args):
                    "oracle_rows_checked": checked},
         "roofline": roofline(spec.name, "reduce_kernel (scoring)", algo_bytes, mean_reduce_ms),
         "reduce_ms": mean_reduce_ms,
+        "diagnostic_calls": max(K, DIAG_CALLS),
+        "diagnostic_after_calls": max(DIAG_WARM_CALLS, args.warmup + K),
         "merge_ms": mean_merge_ms,
         "graph_replay": graph_res,
         "algorithmic_bytes_per_launch": algo_bytes,
@@ -448,7 +463,7 @@ def main():
                     plan.run(copies[c % len(copies)], tokens, emitted, requested, id_counts, ids,
                              out, ws, row_offsets=offsets)
         torch.cuda.synchronize()
-        reps = max(1, args.steps // n)
+        reps = max(1, max(args.steps, DIAG_CALLS) // n)
         for _ in range(2):
             gr.replay()
         torch.cuda.synchronize()
@@ -559,6 +574,8 @@ def main():
                              else f"reduce_kernel + shard_finalize_kernel, {args.shards} shard passes",
                              algo_bytes, mean_reduce_ms, packed=bool(packed_rows or args.shards)),
         "reduce_ms": mean_reduce_ms,
+        "diagnostic_calls": max(K, DIAG_CALLS),
+        "diagnostic_after_calls": max(DIAG_WARM_CALLS, args.warmup + K),
         "merge_ms": mean_merge_ms,
         "graph_replay": graph_res,
         "algorithmic_bytes_per_launch": algo_bytes,
