@@ -125,7 +125,8 @@ int launch_shard_finalize(const Params& p, int dtype, void* stream);
 int launch_shard_merge(const Params& p, int dtype, bool vector_rows, void* stream);
 // Resident reduction workgroups per CU (0 on error).
 int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity, bool packed);
-// Dynamic LDS of the reduction: the slot table, and each slot's packed row offset.
+// Dynamic LDS of the reduction: the slot table, and each slot's packed row offset (packed
+// launches) or scored target (scoring: callers pass packed = true).
 size_t prefix_lds_bytes(int capacity, bool packed);
 
 }  // namespace flp

@@ -469,13 +469,8 @@ __device__ __forceinline__ int token_of(const Params& p, int s, int t) {
   return v < -0x80000000ll || v > 0x7FFFFFFF ? -1 : (int)v;
 }
 
-// A scored prompt row (one per slot) is active when its target is an ID.
-template <bool SCORE>
+// A generation slot's active rows and whether it selects IDs.
 __device__ __forceinline__ int slot_word(const Params& p, int s) {
-  if (SCORE) {
-    const int tk = p.tokens[s];
-    return (tk >= 0 && tk < p.V) ? 1 : 0;
-  }
   // The words are loaded together (one round trip).
   const int r = p.requested[s], e = emitted_of(p, s), n = p.id_counts ? p.id_counts[s] : 0;
   int rows = r == 0 ? 0 : (e < 0 ? 0 : (e > p.T ? p.T : e));
@@ -506,11 +501,20 @@ __device__ int build_prefix(const Params& p, int* prefix, int* scan) {
   const int s0 = tid * per;
   const int s1 = s0 + per < cap ? s0 + per : cap;
   int local = 0;
-  int* phys = prefix + cap + 1;  // packed row offsets (packed launches only)
+  // Packed row offsets (packed launches), or the scored rows' targets (scoring).
+  int* phys = prefix + cap + 1;
   for (int s = s0; s < s1; ++s) {
-    const int c = slot_word<SCORE>(p, s);
+    int c;
+    if (SCORE) {
+      // A scored prompt row (one per slot) is active when its target is an ID.
+      const int tk = p.tokens[s];
+      c = (tk >= 0 && tk < p.V) ? 1 : 0;
+      phys[s] = tk;
+    } else {
+      c = slot_word(p, s);
+      if (p.row_offsets) phys[s] = p.row_offsets[s];
+    }
     prefix[s] = c;
-    if (!SCORE && p.row_offsets) phys[s] = p.row_offsets[s];
     local += c & kRowsMask;
   }
   // exclusive scan of `local` over the block: within each wave an inclusive
@@ -1474,14 +1478,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
 
   // Scoring: lane i holds the target logit of the range's i-th row (the
   // host keeps a range within kMaxRangeRows rows); each lane counts its
-  // part's lanes above it.
+  // part's lanes above it.  The targets come from the slot table, so each
+  // target logit's load follows the first unit's at once instead of after a
+  // round trip for the target queued behind the whole unit.
   const int a_first = x0 / U;
   float xa_lane = 0.0f;
   if (SCORE) {
     const int a = a_first + lane_id;
     if (lane_id < kMaxRangeRows && (int64_t)a * U < x1) {
       const int s = slot_of(prefix, p.capacity, a);
-      xa_lane = load_elem<DT>((const char*)p.logits + (int64_t)s * p.V_pad * E::kBytes, p.tokens[s]);
+      xa_lane = load_elem<DT>((const char*)p.logits + (int64_t)s * p.V_pad * E::kBytes,
+                              prefix[p.capacity + 1 + s]);
     }
   }
   int above = 0;
@@ -2092,7 +2099,7 @@ bool wide_merge(const Params& p) {
 template <int DT, bool VEC, bool SCORE>
 hipError_t launch_typed(const Params& p, int phases, hipStream_t st) {
   if (phases & kPhaseReduce) {
-    const size_t lds = prefix_lds_bytes(p.capacity, p.row_offsets != nullptr);
+    const size_t lds = prefix_lds_bytes(p.capacity, SCORE || p.row_offsets != nullptr);
     hipLaunchKernelGGL((reduce_kernel<DT, VEC, SCORE>), dim3((uint32_t)p.workers), dim3(kBlock), lds,
                        st, p);
     const hipError_t e = hipGetLastError();
@@ -2169,7 +2176,7 @@ int occupancy_typed(size_t lds) {
 }
 
 int reduce_occupancy(int dtype, bool vector_rows, bool score, int capacity, bool packed) {
-  const size_t lds = prefix_lds_bytes(capacity, packed);
+  const size_t lds = prefix_lds_bytes(capacity, packed || score);
   if (dtype == 1) {
     if (score) return vector_rows ? occupancy_typed<1, true, true>(lds) : occupancy_typed<1, false, true>(lds);
     return vector_rows ? occupancy_typed<1, true, false>(lds) : occupancy_typed<1, false, false>(lds);
