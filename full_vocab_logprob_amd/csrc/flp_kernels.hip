@@ -800,13 +800,22 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // of the N units of the active rows in double precision).
   const int a = before + t;
   const RangePlan rplan = range_plan(total, U, p.workers);
-  const bool start = lane < U && (lane == 0 || starts_range(a * U + lane, total, U, rplan));
-  const uint64_t starts = __ballot(start);
-  const int np = __popcll(starts);
-  if (start) part_u0[lanes_below(starts)] = (int16_t)lane;
-  if (lane == 0) part_u0[np] = (int16_t)U;
+  int np, u0;
+  if (rplan.pieces) {
+    // Row pieces: part i of q starts at unit floor(i U / q).
+    np = rplan.pieces + (a >= total - rplan.extra ? 1 : 0);
+    u0 = lane <= np ? lane * U / np : 0;
+    if (lane <= np) part_u0[lane] = (int16_t)u0;
+  } else {
+    const bool start = lane < U && (lane == 0 || starts_range(a * U + lane, total, U, rplan));
+    const uint64_t starts = __ballot(start);
+    np = __popcll(starts);
+    if (start) part_u0[lanes_below(starts)] = (int16_t)lane;
+    if (lane == 0) part_u0[np] = (int16_t)U;
+    wave_sync();
+    u0 = lane < np ? part_u0[lane] : 0;
+  }
   wave_sync();
-  const int u0 = lane < np ? part_u0[lane] : 0;
 
   // ---- record and logit loads, issued together: the part statistics, the
   // first four parts' kept keys in registers, those of the next 2 kLdsPairs
