@@ -115,6 +115,36 @@ def test_row_pieces_with_extra_pieces(oracle_handle, dtype):
     full_compare(oracle_handle, spec)
 
 
+@pytest.mark.parametrize("case", ["fp32_64_units", "bf16_33_units_selected"])
+def test_four_wave_merge_many_parts(oracle_handle, case):
+    # One-unit ranges, so every unit of a row is its own part: 64 parts per
+    # row (eight pairs per merge wave, the most the layout holds) or 33 with
+    # rows that select IDs among them.  Every row against the oracle.
+    if case == "fp32_64_units":
+        spec = synth.CONFIGS["C1"].with_(capacity=8, V=64 * 8192 - 3, V_pad=64 * 8192,
+                                         emitted="one", seed=95)
+    else:
+        spec = synth.CONFIGS["C4"].with_(capacity=6, T=4, V=33 * 16384 - 9, V_pad=33 * 16384,
+                                         emitted="uniform", selected="frac40", seed=96)
+    full_compare(oracle_handle, spec)
+
+
+def test_row_pieces_three_and_four(oracle_handle):
+    # About 400 active rows of 12 units: three pieces per row leave about 80
+    # workgroups idle, so the last rows get four pieces.
+    spec = synth.CONFIGS["C3"].with_(capacity=400, T=1, emitted="one", V=12 * 16384 - 5,
+                                     V_pad=12 * 16384, seed=97)
+    w = synth.make(spec)
+    rows = int(w.active_mask().sum())
+    grid = int(H.make_plan(spec).raw.grid)
+    p = grid // rows
+    idle = grid - p * rows
+    longest = -(-rows * 12 // grid)
+    if not (rows * 12 >= 2 * grid and p == 3 and -(-12 // p) <= longest + 1 and 16 * idle >= grid):
+        pytest.skip(f"{rows} rows on a grid of {grid} do not take three and four pieces")
+    full_compare(oracle_handle, spec)
+
+
 def full_size_all_rows(o, spec):
     """The configuration at its full size, in the launch configuration the
     bench times, every active row compared with the oracle."""
