@@ -1042,6 +1042,7 @@ struct ReduceSmem {
   int16_t stash_off[kWaves][kStash];     // their chunk index c * 64 + lane
   uint64_t qbar[kWaves];                 // each wave's published ceil(K/4)-th key (see pub_key)
   uint64_t flush_cut[2][kWaves];         // a part's per-wave cut, by part parity
+  float first_tau[2][kWaves];            // short ranges: the waves' first-unit thresholds, by parity
   float wm[2][kWaves];                   // a part's per-wave max and scaled sum
   float ws[2][kWaves];
   int wabove[2][kWaves];                 // scoring: a part's per-wave count above the target
@@ -1252,7 +1253,8 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
                                              const char* next_rowp, int next_base, bool has_next,
                                              int V, int lane, bool& stage, HotTest& ht, Stage& st,
                                              bool first, int kq, float xa, int& above,
-                                             float& next_above, int& next_count, float& next2) {
+                                             float& next_above, int& next_count, float& next2,
+                                             float* tau_base, int tau_off) {
   using E = Elem<DT>;
   constexpr int kPer = E::kPer;
   PassOut o;
@@ -1271,6 +1273,21 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
     const bool voter = wave_base + lane * kPer < V;
     const int nv = __popcll(__ballot(voter));
     o.tau = nv >= kq ? key_floor16(wave_kth_largest16(ukey32(lm) >> 16, voter, kq)) : kNegInf;
+    if (!SCORE && tau_off >= 0) {
+      // One- and two-unit ranges: every wave admits down to the smallest of
+      // the waves' thresholds (waves without vocabulary left out).  Each
+      // wave holding vocabulary has kq lanes at or above its own, so the part
+      // keeps at least K lanes at or above that smallest one, and its cut
+      // cannot sit above the row's K-th value, while the waves admit far
+      // fewer lanes than K each.
+      const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+      if (lane == 0) tau_base[tau_off + wv] = nv > 0 ? o.tau : __builtin_huge_valf();
+      __syncthreads();
+      float t = tau_base[tau_off];
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) t = fminf(t, tau_base[tau_off + i]);
+      o.tau = t;
+    }
     ht = hot_test(o.tau, false, ht.vlim);
     stage = !ht.every_lane;
   }
@@ -1577,13 +1594,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     // part's first unit finds its threshold in the pass itself.
     bool stage = natural && ad.by_key && !ht.every_lane;
     // Keys each wave admits in a part's first unit: ceil(K / waves holding
-    // vocabulary), so that the part keeps at least K; K per wave when the
-    // ranges are one or two units long, since then no later unit of the part
-    // can refine the wave's threshold and a wave holding several of the
-    // row's best lanes would leave a cut above the row's K-th value.
+    // vocabulary), so that the part keeps at least K.  When the ranges are
+    // one or two units long no later unit of the part can refine a wave's
+    // threshold, and a wave holding several of the row's best lanes would
+    // leave a cut above the row's K-th value: there the waves share the
+    // smallest of their thresholds (unit_pass), or, in the scoring kernels
+    // (whose registers are fuller), each wave admits K lanes.
     const int ubase = cur.u * kUnitElems;
     const int nw = V - ubase >= kUnitElems ? kWaves : (V - ubase + kWaveElems - 1) / kWaveElems;
-    const int kfirst = short_ranges ? K
+    const int kfirst = SCORE && short_ranges ? K
                        : (nw == kWaves ? kq : (nw == 3 ? (K + 2) / 3 : (nw == 2 ? (K + 1) >> 1 : K)));
 
     st.n = 0;
@@ -1594,7 +1613,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     const PassOut po = unit_pass<DT, VEC, SCORE>(
         raw, cm, m_l, tail, wave_base, row_rsrc(nxt.rowp, has_next ? row_bytes : 0), nxt.rowp,
         next_base, has_next, V, lane, stage, ht, st, natural && part_starts, kfirst, xa, above,
-        next_above, next_count, next2);
+        next_above, next_count, next2, &sh.first_tau[0][0],
+        short_ranges ? (part_seq & 1) * kWaves : -1);
     const float lm = po.lm;
 
     // ---- fold the unit into the lane's running (max, sum)
