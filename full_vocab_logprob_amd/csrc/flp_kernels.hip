@@ -387,11 +387,16 @@ struct Best32 {
 };
 
 
-// Insert the wave-uniform key k if it ranks among the best 32.
+// Insert the wave-uniform key k if it ranks among the best 32: lanes past
+// its position p take their lower neighbour's key (the shift's bound control
+// feeds lane 0 a zero, which it never keeps) and lane p takes k.
 __device__ __forceinline__ void best_insert(Best32& b, uint64_t k, int lane) {
   const int p = __popc((uint32_t)__ballot(b.top > k));  // better keys in lanes 0..31
   if (p >= kKeep) return;
-  const uint64_t shifted = wave_shr1_64(b.top);
+  const uint32_t lo = (uint32_t)b.top, hi = (uint32_t)(b.top >> 32);
+  const uint32_t slo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, 0x138, 0xf, 0xf, true);
+  const uint32_t shi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, 0x138, 0xf, 0xf, true);
+  const uint64_t shifted = ((uint64_t)shi << 32) | slo;
   b.top = lane < p ? b.top : (lane == p ? k : shifted);
   b.n = b.n < kKeep ? b.n + 1 : kKeep;
 }
@@ -1231,6 +1236,22 @@ __device__ __forceinline__ void refill_chunk(u32x4& r, __amdgpu_buffer_rsrc_t rs
 // unit as soon as they have been used, so a unit's loads are always in
 // flight behind the current unit's arithmetic; with `stage` a chunk whose
 // maximum passes the test is stashed first.
+// Maximum of the eight chunk maxima in four instructions.  The maxima come
+// out of v_max3 chains (never signalling NaNs), so the canonicalising moves
+// the compiler would put before each fmaxf of a value it cannot trace (nine
+// per unit) are not needed.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max8(const float (&cm)[kChunks]) {
+  static_assert(kChunks == 8, "eight chunks per lane");
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(cm[6]), "v"(cm[7]));
+  return vmax3(vmax3(cm[0], cm[1], cm[2]), vmax3(cm[3], cm[4], cm[5]), r);
+}
+
 struct PassOut {
   float acc, lm, mref, nb;
   float tau;  // a first unit's threshold
@@ -1268,8 +1289,7 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
       for (int j = 1; j < kPer; ++j) mc = fmaxf(mc, E::get(raw[c], j));
       cm[c] = mc;
     }
-    const float lm = fmaxf(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])),
-                           fmaxf(fmaxf(cm[4], cm[5]), fmaxf(cm[6], cm[7])));
+    const float lm = max8(cm);
     const bool voter = wave_base + lane * kPer < V;
     const int nv = __popcll(__ballot(voter));
     o.tau = nv >= kq ? key_floor16(wave_kth_largest16(ukey32(lm) >> 16, voter, kq)) : kNegInf;
@@ -1298,6 +1318,10 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
   o.mref = fmaxf(m_l, c0);
   o.nb = -o.mref * kLog2e;
   o.acc = 0.0f;
+  // Byte offsets of this lane's chunks 0 and 4 in the next unit's row (each
+  // chunk of the wave is 64 lanes x 16 bytes further on).
+  uint32_t vo_lo = (uint32_t)((next_base + lane * kPer) * E::kBytes);
+  uint32_t vo_hi = vo_lo + 4u * 1024u;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     // Empty asm statements only add data dependencies: chunk c is not
@@ -1334,15 +1358,21 @@ __device__ __forceinline__ PassOut unit_pass(u32x4 (&raw)[kChunks], float (&cm)[
       }
     }
     if (stage) stage_chunk(st, raw[c], mc > ht.above, c, lane);
-    {
+    if (VEC) {
+      // The empty asm takes the offset register as rewritten after the
+      // chunk's last use, so the refill cannot move above it; chunks 0-3
+      // and 4-7 share one offset each (the rest is the immediate field).
+      uint32_t& vo = c < 4 ? vo_lo : vo_hi;
+      asm volatile("" : "+v"(vo) : "v"(o.acc), "v"(mc), "v"(raw[c]));
+      raw[c] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(next_rsrc, vo + (uint32_t)(c & 3) * 1024u, 0, kSlc));
+    } else {
       int lane_dep = lane;
       asm volatile("" : "+v"(lane_dep) : "v"(o.acc), "v"(mc), "v"(raw[c]));
       refill_chunk<DT, VEC>(raw[c], next_rsrc, next_rowp, next_base, c, lane_dep, V, has_next);
     }
   }
-  // The lane maximum from the chunk maxima (max3 chains, no per-chunk update).
-  o.lm = fmaxf(fmaxf(fmaxf(cm[0], cm[1]), fmaxf(cm[2], cm[3])),
-               fmaxf(fmaxf(cm[4], cm[5]), fmaxf(cm[6], cm[7])));
+  o.lm = max8(cm);
   return o;
 }
 
