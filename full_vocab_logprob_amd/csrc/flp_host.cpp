@@ -11,6 +11,11 @@ namespace {
 constexpr uint64_t kAlign = 256;
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+// The chosen (or scored target) raw logits a reduction captures for its
+// merge: float[capacity * T] after the guard counts.
+uint64_t chosen_offset(const flare_logprobs_plan_t* plan) {
+  return plan->guard_offset + align_up((uint64_t)plan->capacity * plan->T * sizeof(int32_t), kAlign);
+}
 
 bool geometry_ok(int32_t capacity, int32_t T, int32_t V, int32_t V_pad, int32_t K) {
   if (capacity < 1 || T < 1 || V < 1 || V_pad < V) return false;
@@ -114,6 +119,7 @@ static int make_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T, i
   off = align_up(off + ((uint64_t)capacity + 1) * sizeof(int32_t), kAlign);
   plan->guard_offset = off;
   off = align_up(off + (uint64_t)rows * sizeof(int32_t), kAlign);
+  off = align_up(off + (uint64_t)rows * sizeof(float), kAlign);  // chosen raw logits
   plan->workspace_bytes = off;
   return FLARE_OK;
 }
@@ -232,6 +238,7 @@ static int run_phases(const flare_logprobs_plan_t* plan, const void* logits, int
   p.records = (flp::PartRecord*)(ws + plan->record_offset);
   p.lse = (float*)(ws + plan->lse_offset);
   p.guard = (int32_t*)(ws + plan->guard_offset);
+  p.xtok = (float*)(ws + chosen_offset(plan));
   p.slot_rows = (int32_t*)(ws + plan->slots_offset);
   p.V_pad = V_pad;
   p.capacity = plan->capacity;
@@ -319,6 +326,7 @@ static int prompt_phases(const flare_logprobs_plan_t* plan, const void* logits, 
   p.records = (flp::PartRecord*)(ws + plan->record_offset);
   p.lse = (float*)(ws + plan->lse_offset);
   p.guard = (int32_t*)(ws + plan->guard_offset);
+  p.xtok = (float*)(ws + chosen_offset(plan));
   p.slot_rows = (int32_t*)(ws + plan->slots_offset);
   p.V_pad = V_pad;
   p.capacity = plan->capacity;

@@ -30,7 +30,7 @@ constexpr int elem_bytes(int dtype) { return dtype == 1 ? 2 : 4; }
 // not keep has a raw key <= cut (0: the part kept every lane).  When a
 // prompt row is scored, `above` counts the part's lanes whose raw logit
 // exceeds the target's and `next_above` is the smallest such logit (+inf
-// if none).  Stored at records[row * units + first unit of part].
+// if none).  Stored at records[row * units + i] for the row's i-th part.
 struct PartRecord {
   float m;
   float s;
@@ -84,6 +84,7 @@ struct Params {
   float* lse;
   int32_t* guard;       // [rows]: parts the merge read again (diagnostic)
   int32_t* slot_rows;   // [capacity + 1]: active rows before each slot, then their total
+  float* xtok;          // [rows]: chosen raw logits captured by the reduction
   const int64_t* crecords;     // completion records [capacity, 16 + T] (or null): emitted
                                // count at field emitted_field, tokens at fields 16 + t
   int32_t emitted_field;

@@ -589,6 +589,13 @@ __device__ __forceinline__ int slot_of_wave(const int* prefix, int cap, int a, i
 // either test is rescanned lane by lane with final keys; F_K over a subset
 // never exceeds the true K-th key, so the test stays sound.
 constexpr int kMergeWaves = kMergeBlock / 64;
+// A part record's statistics words, loaded one lane per part.
+struct PartRecord0 {
+  float m, s;
+  int32_t above;
+  float next_above;
+  uint64_t cut;
+};
 constexpr int kLdsPairs = 14;  // part pairs after the first two staged in LDS (rows up to 32 parts)
 
 // Whether unit x begins one of the `grid` ranges [floor(g n / grid),
@@ -651,6 +658,13 @@ __device__ __forceinline__ bool starts_range(int x, int rows, int U, const Range
     return is_range_start(x - a * U, U, rp.pieces + (a >= rows - rp.extra ? 1 : 0));
   }
   return is_range_start(x, rows * U, rp.count);
+}
+
+// Whether the reduction's idle workgroups capture every active position's
+// chosen (or scored target) raw logit, one thread per position, for the
+// merge of an unsharded call.
+__device__ __forceinline__ bool chosen_captured(const Params& p, const RangePlan& rp) {
+  return p.shards == 0 && (int64_t)(p.workers - rp.count) * kBlock >= (int64_t)p.capacity * p.T;
 }
 
 // Every lane [lo, hi) of a row whose final key reaches thr, merged into the
@@ -781,6 +795,26 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int before = p.slot_rows[s], total = p.slot_rows[p.capacity];
   const int tok = SCORE ? p.tokens[row] : token_of(p, s, t);
   const int V = p.V, U = p.units;
+  // Loaded with the row's words, before anything depends on them (records
+  // are stored by part index, so their addresses need nothing the row's
+  // words give): each part's statistics (lane i: part i), the first four
+  // parts' kept keys, the chosen raw logit captured by the reduction, and
+  // the slot's selected IDs.
+  const PartRecord* rec = p.records + (int64_t)row * U;
+  PartRecord0 hdr{kNegInf, 0.0f, 0, __builtin_huge_valf(), 0ull};
+  if (lane < U) hdr = PartRecord0{rec[lane].m, rec[lane].s, rec[lane].above, rec[lane].next_above, rec[lane].cut};
+  uint64_t ex31 = 0ull;
+  if (SCORE && DT == 0 && lane < U) ex31 = rec[lane].keys[kKeep - 1];
+  const uint64_t spec0 = (lane >> 5) < U ? rec[lane >> 5].keys[lane & 31] : 0ull;
+  const uint64_t spec1 = 2 + (lane >> 5) < U ? rec[2 + (lane >> 5)].keys[lane & 31] : 0ull;
+  const float xt_spec = p.shards == 0 ? p.xtok[row] : 0.0f;
+  int ids_spec[2] = {0, 0};
+  if (!SCORE && p.ids) {
+    ids_spec[0] = p.ids[(int64_t)s * 128 + lane];
+    ids_spec[1] = p.ids[(int64_t)s * 128 + 64 + lane];
+  }
+  asm volatile("" ::"v"(hdr.m), "v"(hdr.s), "v"(hdr.above), "v"(hdr.next_above), "v"(hdr.cut),
+               "v"(ex31), "v"(spec0), "v"(spec1), "v"(xt_spec), "v"(ids_spec[0]), "v"(ids_spec[1]));
   int32_t* out = p.out + (int64_t)row * (SCORE ? kPromptWords : p.row_words);
   if (SCORE && !(tok >= 0 && tok < V)) {
     // [-1, NaN, rank 0, then (-1, NaN) twenty times]
@@ -794,7 +828,6 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   if (t >= rows_s) return;
   const int n_sel = cnt < 0 ? 0 : (cnt > 128 ? 128 : cnt);
   const bool natural = p.K > 0 && n_sel == 0;
-  const PartRecord* rec = p.records + (int64_t)row * U;
   const int lrow = !SCORE && p.row_offsets ? off + t : row;
   const char* rowp = (const char*)p.logits + (int64_t)lrow * p.V_pad * E::kBytes;
   int16_t* part_u0 = part_u0_all[wv];
@@ -805,20 +838,17 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   // of the N units of the active rows in double precision).
   const int a = before + t;
   const RangePlan rplan = range_plan(total, U, p.workers);
-  int np, u0;
+  int np;
   if (rplan.pieces) {
     // Row pieces: part i of q starts at unit floor(i U / q).
     np = rplan.pieces + (a >= total - rplan.extra ? 1 : 0);
-    u0 = lane <= np ? lane * U / np : 0;
-    if (lane <= np) part_u0[lane] = (int16_t)u0;
+    if (lane <= np) part_u0[lane] = (int16_t)(lane * U / np);
   } else {
     const bool start = lane < U && (lane == 0 || starts_range(a * U + lane, total, U, rplan));
     const uint64_t starts = __ballot(start);
     np = __popcll(starts);
     if (start) part_u0[lanes_below(starts)] = (int16_t)lane;
     if (lane == 0) part_u0[np] = (int16_t)U;
-    wave_sync();
-    u0 = lane < np ? part_u0[lane] : 0;
   }
   wave_sync();
 
@@ -830,32 +860,29 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   int p_above = 0, p_count = 0;
   float p_next = __builtin_huge_valf(), p_next2 = __builtin_huge_valf();
   if (lane < np) {
-    pm = rec[u0].m;
-    ps = rec[u0].s;
-    c_key = rec[u0].cut;
+    pm = hdr.m;
+    ps = hdr.s;
+    c_key = hdr.cut;
     if (SCORE) {
-      p_above = rec[u0].above;
-      p_next = rec[u0].next_above;
+      p_above = hdr.above;
+      p_next = hdr.next_above;
       if (DT == 0) {
-        const uint64_t ex = rec[u0].keys[kKeep - 1];
-        p_count = (int)(uint32_t)ex;
-        p_next2 = __uint_as_float((uint32_t)(ex >> 32));
+        p_count = (int)(uint32_t)ex31;
+        p_next2 = __uint_as_float((uint32_t)(ex31 >> 32));
       }
     }
   }
   // FP32 scoring records use key slot 31 for the rank (read above), not a key.
   const bool extra_slot = SCORE && DT == 0 && (lane & 31) == kKeep - 1;
-  const uint64_t raw0 =
-      !extra_slot && (lane >> 5) < np ? rec[part_u0[lane >> 5]].keys[lane & 31] : 0ull;
-  const uint64_t raw1 =
-      !extra_slot && 2 + (lane >> 5) < np ? rec[part_u0[2 + (lane >> 5)]].keys[lane & 31] : 0ull;
+  const uint64_t raw0 = !extra_slot && (lane >> 5) < np ? spec0 : 0ull;
+  const uint64_t raw1 = !extra_slot && 2 + (lane >> 5) < np ? spec1 : 0ull;
   // WIDE rows of more than four parts: this wave's pairs, loads all in flight.
   const bool wide = WIDE && natural && np > 4;
   uint64_t wraw[WIDE ? kWidePairs : 1];
 #pragma unroll
   for (int i = 0; i < (WIDE ? kWidePairs : 1); ++i) {
     const int part = 2 * (wv + i * kMergeWaves) + (lane >> 5);
-    wraw[i] = wide && !extra_slot && part < np ? rec[part_u0[part]].keys[lane & 31] : 0ull;
+    wraw[i] = wide && !extra_slot && part < np ? rec[part].keys[lane & 31] : 0ull;
   }
   if (natural && np > 4 && !wide) {
     // All loads in flight at once: a row of many parts pays one round trip.
@@ -863,21 +890,24 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < kLdsPairs; ++i) {
       const int part = 4 + 2 * i + (lane >> 5);
-      pre[i] = !extra_slot && part < np ? rec[part_u0[part]].keys[lane & 31] : 0ull;
+      pre[i] = !extra_slot && part < np ? rec[part].keys[lane & 31] : 0ull;
     }
 #pragma unroll
     for (int i = 0; i < kLdsPairs; ++i) pair_keys[wv][i][lane] = pre[i];
     wave_sync();
   }
+  // The chosen raw logit: captured by the reduction's idle workgroups when it
+  // had some (see reduce_kernel), else read from the row.
+  const bool xt_valid = chosen_captured(p, rplan);
   float x_tok = 0.0f;
-  if (lane == 0 && tok >= 0 && tok < V) x_tok = load_elem<DT>(rowp, tok);
+  if (lane == 0 && tok >= 0 && tok < V) x_tok = xt_valid ? xt_spec : load_elem<DT>(rowp, tok);
   int sel_id[2] = {0, 0};
   float x_sel[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int j = lane + 64 * h;
     if (j < n_sel) {
-      sel_id[h] = p.ids[(int64_t)s * 128 + j];
+      sel_id[h] = ids_spec[h];
       if (sel_id[h] >= 0 && sel_id[h] < V) x_sel[h] = load_elem<DT>(rowp, sel_id[h]);
     }
   }
@@ -966,7 +996,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
         const int part = q + (lane >> 5);
         r[h] = 0ull;
         if (q < 4 + 2 * kLdsPairs) r[h] = q < np ? pair_keys[wv][(q - 4) >> 1][lane] : 0ull;
-        else if (!extra_slot && part < np) r[h] = rec[part_u0[part]].keys[lane & 31];
+        else if (!extra_slot && part < np) r[h] = rec[part].keys[lane & 31];
       }
       uint64_t ka = r[0] != 0ull ? final_key(r[0], L) : 0ull;
       uint64_t kb = r[1] != 0ull ? final_key(r[1], L) : 0ull;
@@ -995,7 +1025,7 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
       const int part = pb + (lane >> 5);
       uint64_t f = 0ull;
       if (!extra_slot && part < np && !((unsafe >> part) & 1ull)) {
-        const uint64_t raw = rec[part_u0[part]].keys[lane & 31];
+        const uint64_t raw = rec[part].keys[lane & 31];
         if (raw != 0ull) f = final_key(raw, L);
       }
       top = merge_top32(top, sort64_desc(f, lane), lane);
@@ -1497,8 +1527,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   // This workgroup's range of the N < 2^31 units (the host checks N).
   const int N = total * U;
   const RangePlan rplan = range_plan(total, U, p.workers);
-  if ((int)blockIdx.x >= rplan.count) return;
-  int x0, x1;
+  if ((int)blockIdx.x >= rplan.count) {
+    // A workgroup with no units captures chosen raw logits for the merge,
+    // one active position per thread, when the idle ones cover them all.
+    if (chosen_captured(p, rplan)) {
+      const int q = ((int)blockIdx.x - rplan.count) * kBlock + tid;
+      if (q < p.capacity * p.T) {
+        const int s = q / p.T, t = q - s * p.T;
+        if (t < (prefix[s + 1] & kRowsMask) - (prefix[s] & kRowsMask)) {
+          const int tok = token_of(p, s, t);
+          const int lrow = p.row_offsets ? prefix[p.capacity + 1 + s] + t : q;
+          if (tok >= 0 && tok < V)
+            p.xtok[q] = load_elem<DT>((const char*)p.logits + (int64_t)lrow * p.V_pad * E::kBytes, tok);
+        }
+      }
+    }
+    return;
+  }
+  // The range, and the index of its first part among its row's parts (the
+  // slot of the part's record): parts are numbered by where they start.
+  int x0, x1, part_idx;
   if (rplan.pieces) {
     const int b = (int)blockIdx.x;
     int row, piece;
@@ -1512,18 +1560,28 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
     const int q = rplan.pieces + (row >= total - rplan.extra ? 1 : 0);
     x0 = row * U + piece * U / q;
     x1 = row * U + (piece + 1) * U / q;
+    part_idx = piece;
   } else {
     // floor(b N / count) in double precision: b N < 2^53 is exact, and a
     // quotient that is not an integer lies at least 1 / count from one, far
     // beyond the division's rounding error, so the floor is exact.
-    x0 = (int)__builtin_floor((double)blockIdx.x * (double)N / (double)rplan.count);
-    x1 = (int)__builtin_floor(((double)blockIdx.x + 1.0) * (double)N / (double)rplan.count);
+    const double b = (double)blockIdx.x, n = (double)N, c = (double)rplan.count;
+    x0 = (int)__builtin_floor(b * n / c);
+    x1 = (int)__builtin_floor((b + 1.0) * n / c);
+    // Ranges start at distinct units (count <= N), so ranges 0..b are the
+    // ones starting at or before x0, and ceil((r + 1) count / N) of them
+    // start at or before unit r: the row's first unit r = (x0 / U) U starts
+    // part 0, and each range start after it one more part.
+    const double r1 = (double)((x0 / U) * U + 1);
+    part_idx = (int)blockIdx.x + 1 - (int)__builtin_ceil(r1 * c / n);
   }
   if (x0 >= x1) return;
   const bool short_ranges = N < 2 * p.workers;
 
   UnitPos cur = locate<DT>(p, prefix, x0, lane_id);
-  int part_u0 = cur.u;
+  // The current part's first unit (bits 0-7; U <= 64) and its index among
+  // its row's parts (bits 8 up).
+  int part_tag = cur.u | part_idx << 8;
   const int row_bytes = (int)(p.V_pad * E::kBytes);
   u32x4 raw[kChunks];
 #pragma unroll
@@ -1583,7 +1641,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
       else nxt = locate<DT>(p, prefix, x + 1, lane);
     }
     const bool part_ends = !has_next || nxt.a != cur.a;
-    const bool part_starts = cur.u == part_u0;
+    const bool part_starts = cur.u == (part_tag & 0xff);
     const int wave_base = cur.u * kUnitElems + w * kWaveElems;
     const int next_base = nxt.u * kUnitElems + w * kWaveElems;
     const bool tail = wave_base + kWaveElems > V;  // the slice reaches past V
@@ -1841,7 +1899,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
             rec->above = na;
             rec->next_above = nx;
             rec->cut = pcut;
-            sr->dst = cur.row * U + part_u0;
+            sr->dst = cur.row * U + (part_tag >> 8);
             sr->natural = natural;
           }
           sh.n_staged = (slot + 1 == kRecStage || !has_next) ? 0 : slot + 1;
@@ -1865,7 +1923,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         }
         if (direct) {
           // Header words (m, s), (above, next_above), cut; then the kept keys.
-          uint64_t* g = (uint64_t*)(p.records + (cur.row * U + part_u0));
+          uint64_t* g = (uint64_t*)(p.records + (cur.row * U + (part_tag >> 8)));
           const uint64_t hdr =
               lane == 0 ? ((uint64_t)__float_as_uint(S) << 32) | __float_as_uint(M)
                         : (lane == 1 ? (uint64_t)__float_as_uint(__builtin_huge_valf()) << 32 : pcut);
@@ -1888,7 +1946,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
         next_above = __builtin_huge_valf();
         next_count = 0;
         next2 = __builtin_huge_valf();
-        part_u0 = nxt.u;
+        part_tag = nxt.u;  // a range's later parts start rows: index 0
         natural = p.K > 0 && (prefix[nxt.s] & kSelBit) == 0;
       }
     }
@@ -1930,29 +1988,18 @@ __global__ __launch_bounds__(kMergeBlock) void shard_finalize_kernel(Params p) {
   const char* rowp = (const char*)p.logits + (int64_t)row * p.V_pad * Elem<DT>::kBytes;
   ShardRecord* xr = p.xrec + (int64_t)row * p.shards + p.shard;
 
-  // The row's parts in this shard's launch, as the merge finds them.
+  // The row's parts in this shard's launch, as the merge finds them; part i's
+  // record is the row's i-th.
   const int a = before + t;
   const RangePlan rplan = range_plan(total, U, p.workers);
   const bool start = lane < U && (lane == 0 || starts_range(a * U + lane, total, U, rplan));
-  const uint64_t starts = __ballot(start);
-  const int np = __popcll(starts);
-  const int u0 = start ? lane : 0;  // lane i < np: first unit of part i, after compaction below
-  int part_first = 0;
-  {
-    // compact: part i's first unit to lane i
-    const int pos = lanes_below(starts);
-    __shared__ int16_t firsts[kMergeWaves][kMaxUnits];
-    if (start) firsts[wv][pos] = (int16_t)u0;
-    wave_sync();
-    part_first = lane < np ? firsts[wv][lane] : 0;
-    wave_sync();
-  }
+  const int np = __popcll(__ballot(start));
   float pm = kNegInf, ps = 0.0f;
   uint64_t c_key = 0ull;
   if (lane < np) {
-    pm = rec[part_first].m;
-    ps = rec[part_first].s;
-    c_key = rec[part_first].cut;
+    pm = rec[lane].m;
+    ps = rec[lane].s;
+    c_key = rec[lane].cut;
   }
   const float M = wave_max(pm, lane);
   float term = 0.0f;
@@ -1966,8 +2013,7 @@ __global__ __launch_bounds__(kMergeBlock) void shard_finalize_kernel(Params p) {
   if (natural) {
     for (int pb = 0; pb < np; pb += 2) {
       const int part = pb + (lane >> 5);
-      const int pf = __shfl(part_first, part < 64 ? part : 0, 64);
-      const uint64_t raw = part < np ? rec[pf].keys[lane & 31] : 0ull;
+      const uint64_t raw = part < np ? rec[part].keys[lane & 31] : 0ull;
       kept += __popcll(__ballot(raw != 0ull));
       top = merge_top32(top, sort_halves_desc(raw, lane), lane);
     }

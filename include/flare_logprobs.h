@@ -135,8 +135,8 @@ int flare_logprobs_plan(flare_logprobs_plan_t* plan, int32_t capacity, int32_t T
  *   tokens          device int32 [capacity, T]: chosen token of each position
  *   out             device int32 [capacity, T, 258]: one output frame
  *   workspace       device, plan->workspace_bytes, 16-byte aligned; needs no
- *                   initialisation (every word read is written first in the
- *                   same call)
+ *                   initialisation (every word whose value is used is written
+ *                   first in the same call)
  * Two kernels run in order on the stream: the reduction, then the per-row
  * merge.  Host-checkable errors return before anything is launched.
  * Diagnostics left in the workspace for each active position (other entries
@@ -226,7 +226,9 @@ int flare_logprobs_run_records(const flare_logprobs_plan_t* plan, const void* lo
  * other work between them or time them apart (design page, tiled-reduction
  * paragraph: the per-tile statistics and best-key launches, then the final
  * merge launch).  flare_logprobs_reduce streams the logits once and writes
- * each part's statistics and best raw keys to the workspace;
+ * each part's statistics and best raw keys to the workspace (and, when it has
+ * a workgroup with no logits to stream for every 256 positions, the chosen
+ * tokens' raw logits);
  * flare_logprobs_merge reads them and writes `out` (and each row's L).  Both
  * take run's arguments and validate them the same way; a merge must follow
  * its reduce on the same stream with the same arguments and workspace, and
