@@ -787,19 +787,10 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const bool lead = !WIDE || wv == 0;
   if (row >= p.capacity * p.T) return;
   const int s = row / p.T, t = row - s * p.T;
-  // Every input word this row needs, loaded at once (the row counts are
-  // only meaningful for an active row).
-  const int req = SCORE ? 1 : p.requested[s], emi = SCORE ? 1 : emitted_of(p, s);
-  const int cnt = SCORE || !p.id_counts ? 0 : p.id_counts[s];
-  const int off = !SCORE && p.row_offsets ? p.row_offsets[s] : 0;
-  const int before = p.slot_rows[s], total = p.slot_rows[p.capacity];
-  const int tok = SCORE ? p.tokens[row] : token_of(p, s, t);
   const int V = p.V, U = p.units;
-  // Loaded with the row's words, before anything depends on them (records
-  // are stored by part index, so their addresses need nothing the row's
-  // words give): each part's statistics (lane i: part i), the first four
-  // parts' kept keys, the chosen raw logit captured by the reduction, and
-  // the slot's selected IDs.
+  // Issued first, before the row's words and with nothing depending on them
+  // (records are stored by part index): each part's statistics (lane i:
+  // part i), the first four parts' kept keys and the slot's selected IDs.
   const PartRecord* rec = p.records + (int64_t)row * U;
   PartRecord0 hdr{kNegInf, 0.0f, 0, __builtin_huge_valf(), 0ull};
   if (lane < U) hdr = PartRecord0{rec[lane].m, rec[lane].s, rec[lane].above, rec[lane].next_above, rec[lane].cut};
@@ -807,14 +798,59 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   if (SCORE && DT == 0 && lane < U) ex31 = rec[lane].keys[kKeep - 1];
   const uint64_t spec0 = (lane >> 5) < U ? rec[lane >> 5].keys[lane & 31] : 0ull;
   const uint64_t spec1 = 2 + (lane >> 5) < U ? rec[2 + (lane >> 5)].keys[lane & 31] : 0ull;
-  const float xt_spec = p.shards == 0 ? p.xtok[row] : 0.0f;
   int ids_spec[2] = {0, 0};
   if (!SCORE && p.ids) {
     ids_spec[0] = p.ids[(int64_t)s * 128 + lane];
     ids_spec[1] = p.ids[(int64_t)s * 128 + 64 + lane];
   }
+  // Every input word this row needs and the captured chosen logit, in one
+  // round trip: the ten scalar loads are issued back to back and waited for
+  // once.  (Scalar loads
+  // complete out of order, so compiled code waits for all of them before
+  // it tests any pointer or word, one round trip per test.)  An input not
+  // given reads a stand-in word (the slot table's first, always valid),
+  // ignored below; the row counts only mean something for an active row.
+  const int32_t* const w0 = p.slot_rows;
+  const bool crec = !SCORE && p.crecords != nullptr;
+  const int64_t* const cr = crec ? p.crecords + (int64_t)s * (kRecordMeta + p.T) : (const int64_t*)w0;
+  const int64_t* const a_ce = crec ? cr + p.emitted_field : cr;
+  const int64_t* const a_ct = crec ? cr + kRecordMeta + t : cr;
+  const int32_t* const a_req = SCORE ? w0 : p.requested + s;
+  const int32_t* const a_em = !SCORE && p.emitted ? p.emitted + s : w0;
+  const int32_t* const a_tk = SCORE ? p.tokens + row : (p.tokens ? p.tokens + (s * p.T + t) : w0);
+  const int32_t* const a_cnt = !SCORE && p.id_counts ? p.id_counts + s : w0;
+  const int32_t* const a_off = !SCORE && p.row_offsets ? p.row_offsets + s : w0;
+  const int32_t* const a_bef = p.slot_rows + s;
+  const int32_t* const a_tot = p.slot_rows + p.capacity;
+  const int32_t* const a_xt = p.shards == 0 ? (const int32_t*)p.xtok + row : w0;
+  int w_req, w_em, w_tk, w_cnt, w_off, before, total, w_xt;
+  int64_t w_ce, w_ct;
+  asm volatile(
+      "s_load_dword %0, %10, 0x0\n\t"
+      "s_load_dword %1, %11, 0x0\n\t"
+      "s_load_dword %2, %12, 0x0\n\t"
+      "s_load_dword %3, %13, 0x0\n\t"
+      "s_load_dword %4, %14, 0x0\n\t"
+      "s_load_dword %5, %15, 0x0\n\t"
+      "s_load_dword %6, %16, 0x0\n\t"
+      "s_load_dword %7, %17, 0x0\n\t"
+      "s_load_dwordx2 %8, %18, 0x0\n\t"
+      "s_load_dwordx2 %9, %19, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(w_req), "=&s"(w_em), "=&s"(w_tk), "=&s"(w_cnt), "=&s"(w_off), "=&s"(before),
+        "=&s"(total), "=&s"(w_xt), "=&s"(w_ce), "=&s"(w_ct)
+      : "s"(a_req), "s"(a_em), "s"(a_tk), "s"(a_cnt), "s"(a_off), "s"(a_bef), "s"(a_tot), "s"(a_xt),
+        "s"(a_ce), "s"(a_ct)
+      : "memory");
+  const float xt_spec = __int_as_float(w_xt);
+  const int req = SCORE ? 1 : w_req;
+  const int emi = SCORE ? 1 : (crec ? (w_ce < 0 || w_ce > 0x7FFFFFFF ? 0 : (int)w_ce) : w_em);
+  const int tok = crec ? (w_ct < -0x80000000ll || w_ct > 0x7FFFFFFF ? -1 : (int)w_ct) : w_tk;
+  const int cnt = !SCORE && p.id_counts ? w_cnt : 0;
+  const int off = !SCORE && p.row_offsets ? w_off : 0;
+  // The record loads above are not sunk past the row's tests.
   asm volatile("" ::"v"(hdr.m), "v"(hdr.s), "v"(hdr.above), "v"(hdr.next_above), "v"(hdr.cut),
-               "v"(ex31), "v"(spec0), "v"(spec1), "v"(xt_spec), "v"(ids_spec[0]), "v"(ids_spec[1]));
+               "v"(ex31), "v"(spec0), "v"(spec1), "v"(ids_spec[0]), "v"(ids_spec[1]));
   int32_t* out = p.out + (int64_t)row * (SCORE ? kPromptWords : p.row_words);
   if (SCORE && !(tok >= 0 && tok < V)) {
     // [-1, NaN, rank 0, then (-1, NaN) twenty times]
@@ -1066,7 +1102,7 @@ constexpr int kRecStage = 8;         // part records staged in LDS before they a
 // share the in-order memory counter with them and hold up the next waits.
 struct StagedRec {
   PartRecord rec;
-  int32_t dst;      // record index, row * units + the part's first unit
+  int32_t dst;      // record index, row * units + the part's index in its row
   int32_t natural;  // whether the kept keys are meaningful
 };
 
