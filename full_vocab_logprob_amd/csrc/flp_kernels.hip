@@ -785,6 +785,22 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int row = WIDE ? (int)blockIdx.x : (int)blockIdx.x * kMergeWaves + wv;
   // The wave that writes the row's words (every wave in the one-wave layout).
   const bool lead = !WIDE || wv == 0;
+  {
+    // The arguments the loads below take, all fetched before the first is
+    // needed: one wait for the argument block instead of one per use.
+    const void* a0 = p.records;
+    const void* a1 = p.requested;
+    const void* a2 = p.crecords;
+    const void* a3 = p.emitted;
+    const void* a4 = p.tokens;
+    const void* a5 = p.id_counts;
+    const void* a6 = p.row_offsets;
+    const void* a7 = p.slot_rows;
+    const void* a8 = p.xtok;
+    const void* a9 = p.ids;
+    asm volatile("" ::"s"(a0), "s"(a1), "s"(a2), "s"(a3), "s"(a4), "s"(a5), "s"(a6), "s"(a7), "s"(a8),
+                 "s"(a9), "s"(p.capacity), "s"(p.T), "s"(p.units), "s"(p.shards), "s"(p.emitted_field));
+  }
   if (row >= p.capacity * p.T) return;
   const int s = row / p.T, t = row - s * p.T;
   const int V = p.V, U = p.units;
@@ -1548,6 +1564,22 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(5))) voi
   // dispatched later compete on equal terms with the earlier ones, which are
   // already streaming, to issue their first loads.
   __builtin_amdgcn_s_setprio(3);
+  {
+    // The arguments of the set-up, all fetched before the first is needed:
+    // one wait for the argument block instead of one per use.
+    const void* a0 = p.requested;
+    const void* a1 = p.crecords;
+    const void* a2 = p.emitted;
+    const void* a3 = p.id_counts;
+    const void* a4 = p.row_offsets;
+    const void* a5 = p.tokens;
+    const void* a6 = p.logits;
+    const void* a7 = p.slot_rows;
+    const void* a8 = p.records;
+    asm volatile("" ::"s"(a0), "s"(a1), "s"(a2), "s"(a3), "s"(a4), "s"(a5), "s"(a6), "s"(a7), "s"(a8),
+                 "s"(p.capacity), "s"(p.T), "s"(p.V), "s"(p.K), "s"(p.units), "s"(p.workers),
+                 "s"(p.emitted_field), "s"(p.packed_rows), "s"(p.V_pad));
+  }
   const int tid = threadIdx.x, lane_id = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int V = p.V, U = p.units;
