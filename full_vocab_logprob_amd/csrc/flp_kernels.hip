@@ -821,11 +821,11 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   }
   // Every input word this row needs and the captured chosen logit, in one
   // round trip: the ten scalar loads are issued back to back and waited for
-  // once.  (Scalar loads
-  // complete out of order, so compiled code waits for all of them before
-  // it tests any pointer or word, one round trip per test.)  An input not
-  // given reads a stand-in word (the slot table's first, always valid),
-  // ignored below; the row counts only mean something for an active row.
+  // once.  (Scalar loads complete out of order, so compiled code waits for
+  // all of them before it tests any pointer or word: a round trip per test.)
+  // An input not given reads a stand-in word (the slot table's first, always
+  // valid), ignored below; the row counts only mean something for an active
+  // row.  The wait is in the same block as the loads.
   const int32_t* const w0 = p.slot_rows;
   const bool crec = !SCORE && p.crecords != nullptr;
   const int64_t* const cr = crec ? p.crecords + (int64_t)s * (kRecordMeta + p.T) : (const int64_t*)w0;

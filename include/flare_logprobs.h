@@ -98,7 +98,7 @@ typedef struct flare_logprobs_plan {
   int32_t ranges;        /* contiguous unit ranges of the launch (== grid) */
   int32_t mode;          /* enum flare_mode: which run entry points accept it */
   uint64_t workspace_bytes; /* bytes of device workspace the caller provides */
-  uint64_t record_offset;   /* per-(row, unit) part records */
+  uint64_t record_offset;   /* part records: units slots per row, part i in slot i */
   uint64_t lse_offset;      /* float[capacity * T]: L of each reduced row */
   uint64_t slots_offset;    /* int32[capacity + 1]: active rows before each slot, then all */
   uint64_t guard_offset;    /* int32[capacity * T]: parts of each reduced row that the
