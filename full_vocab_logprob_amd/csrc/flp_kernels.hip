@@ -806,19 +806,13 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int V = p.V, U = p.units;
   // Issued first, before the row's words and with nothing depending on them
   // (records are stored by part index): each part's statistics (lane i:
-  // part i), the first four parts' kept keys and the slot's selected IDs.
+  // part i) and the first two parts' kept keys.
   const PartRecord* rec = p.records + (int64_t)row * U;
   PartRecord0 hdr{kNegInf, 0.0f, 0, __builtin_huge_valf(), 0ull};
   if (lane < U) hdr = PartRecord0{rec[lane].m, rec[lane].s, rec[lane].above, rec[lane].next_above, rec[lane].cut};
   uint64_t ex31 = 0ull;
   if (SCORE && DT == 0 && lane < U) ex31 = rec[lane].keys[kKeep - 1];
   const uint64_t spec0 = (lane >> 5) < U ? rec[lane >> 5].keys[lane & 31] : 0ull;
-  const uint64_t spec1 = 2 + (lane >> 5) < U ? rec[2 + (lane >> 5)].keys[lane & 31] : 0ull;
-  int ids_spec[2] = {0, 0};
-  if (!SCORE && p.ids) {
-    ids_spec[0] = p.ids[(int64_t)s * 128 + lane];
-    ids_spec[1] = p.ids[(int64_t)s * 128 + 64 + lane];
-  }
   // Every input word this row needs and the captured chosen logit, in one
   // round trip: the ten scalar loads are issued back to back and waited for
   // once.  (Scalar loads complete out of order, so compiled code waits for
@@ -859,6 +853,17 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
         "s"(a_ce), "s"(a_ct)
       : "memory");
   const float xt_spec = __int_as_float(w_xt);
+  // Issued after the words and not waited for with the records above: the
+  // third and fourth parts' keys and the selected IDs, which only some rows
+  // use (and whose lines, unlike the records just written, may come from
+  // HBM).
+  // Unconditional loads (clamped part, stand-in word), so that the wait for
+  // the records can count them as issued after the records on every path.
+  const int part1 = 2 + (lane >> 5) < U ? 2 + (lane >> 5) : U - 1;
+  const uint64_t spec1_raw = rec[part1].keys[lane & 31];
+  const bool has_ids = !SCORE && p.ids != nullptr;
+  const int32_t* const idb = has_ids ? p.ids + (int64_t)s * 128 : w0;
+  const int ids_raw0 = idb[has_ids ? lane : 0], ids_raw1 = idb[has_ids ? 64 + lane : 0];
   const int req = SCORE ? 1 : w_req;
   const int emi = SCORE ? 1 : (crec ? (w_ce < 0 || w_ce > 0x7FFFFFFF ? 0 : (int)w_ce) : w_em);
   const int tok = crec ? (w_ct < -0x80000000ll || w_ct > 0x7FFFFFFF ? -1 : (int)w_ct) : w_tk;
@@ -866,7 +871,9 @@ __global__ __launch_bounds__(kMergeBlock) void merge_kernel(Params p) {
   const int off = !SCORE && p.row_offsets ? w_off : 0;
   // The record loads above are not sunk past the row's tests.
   asm volatile("" ::"v"(hdr.m), "v"(hdr.s), "v"(hdr.above), "v"(hdr.next_above), "v"(hdr.cut),
-               "v"(ex31), "v"(spec0), "v"(spec1), "v"(ids_spec[0]), "v"(ids_spec[1]));
+               "v"(ex31), "v"(spec0));
+  const uint64_t spec1 = 2 + (lane >> 5) < U ? spec1_raw : 0ull;
+  const int ids_spec[2] = {ids_raw0, ids_raw1};
   int32_t* out = p.out + (int64_t)row * (SCORE ? kPromptWords : p.row_words);
   if (SCORE && !(tok >= 0 && tok < V)) {
     // [-1, NaN, rank 0, then (-1, NaN) twenty times]
